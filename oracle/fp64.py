@@ -1,0 +1,185 @@
+"""Exact attention in float64, written as the plain definition.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark, never by the product path.
+
+What is computed (FlashAttention reading notes, section "problem setting"):
+for every batch entry b and head h, with Q, K, V each holding N rows of d
+features, the output is O = softmax(S) V where S = scale * Q K^T.  The
+caller's ``scale`` multiplies the raw dot products before the softmax (the
+problem statement on that page carries no scale; the workloads use
+1/sqrt(d), which is also what the worked mask example on the Qiita page,
+section 6, needs to print the value it prints).
+
+Causal masking: key j is visible to query i iff j <= i.  The pages name a
+causal (GPT-2) workload but do not write the convention out; this is the
+plainest lower-triangular reading with the diagonal kept, so no row is empty.
+
+Optional ``key_valid`` [B, N] (True = the key takes part) is the additive
+-inf key-padding bias described on the Qiita page, section 4 and section 6:
+a padded key gets -inf added to its score.  A row that sees no key at all
+has no defined softmax; the oracle returns NaN for it.
+
+LSE: the forward pass keeps, besides O, the softmax statistics m (row max)
+and l (row sum of exp(s - m)) for the backward pass (FlashAttention reading
+notes, section "recomputation").  They are returned folded into one number
+per row, LSE_i = m_i + ln(l_i), natural log of the scaled, masked scores.
+
+Arithmetic: inputs are converted exactly to float64 (bf16 and fp32 values
+are exact there); scores, exponentials, sums and the final division are
+float64.  The softmax is evaluated in two passes over a full row (max, then
+exp and sum) with no online rescaling, so it shares no algorithm with the
+tiled GPU kernel beyond the definition itself.
+
+Each step is a small module-level function so that the tests can replace one
+step with a plausible mistake and check that the pins catch it.
+"""
+
+import math
+
+import numpy as np
+
+
+def _scores(q, k, scale):
+    """S = scale * Q K^T for one head: q [R, d], k [N, d] -> [R, N]."""
+    return scale * (q @ k.T)
+
+
+def _visible(rows, n_keys, causal, key_valid):
+    """bool [R, N]: True where key j enters query row rows[r]'s softmax."""
+    vis = np.ones((len(rows), n_keys), dtype=bool)
+    if causal:
+        vis &= np.arange(n_keys)[None, :] <= rows[:, None]
+    if key_valid is not None:
+        vis &= key_valid[None, :]
+    return vis
+
+
+def _row_max(s):
+    """m_i = max_j s_ij (the softmax's shift; -inf for an empty row)."""
+    return s.max(axis=1)
+
+
+def _exp_shifted(s, m):
+    """exp(s_ij - m_i); a masked score (-inf) gives exactly 0."""
+    return np.exp(s - m[:, None])
+
+
+def _row_sum(e):
+    """l_i = sum_j exp(s_ij - m_i)."""
+    return e.sum(axis=1)
+
+
+def _weighted_values(e, v):
+    """sum_j exp(s_ij - m_i) * v_j, before normalisation: [R, N] x [N, d]."""
+    return e @ v
+
+
+def _normalise(o_unnormalised, l):
+    """O_i = (sum_j e_ij v_j) / l_i."""
+    return o_unnormalised / l[:, None]
+
+
+def _lse(m, l):
+    """LSE_i = m_i + ln l_i (natural log)."""
+    return m + np.log(l)
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention(q, k, v, scale, causal=False, key_valid=None, rows=None,
+              row_chunk=512):
+    """Exact attention forward, float64.
+
+    q, k, v: arrays [B, H, N, d] (any real dtype; converted exactly to f64).
+    scale:   multiplies Q K^T.
+    causal:  hide key j from query i when j > i.
+    key_valid: optional bool [B, N]; False hides that key from every query.
+    rows:    optional 1-D array of query indices, evaluated for every (b, h);
+             default all N rows.  Lets large workloads be checked on a sample.
+    Returns (o [B, H, R, d], lse [B, H, R]) in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    if k.shape != (B, H, N, d) or v.shape != (B, H, N, d):
+        raise ValueError("q, k, v must share the shape [B, H, N, d]")
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    kv = None if key_valid is None else np.asarray(key_valid, dtype=bool)
+    o = np.empty((B, H, len(rows), d), dtype=np.float64)
+    lse = np.empty((B, H, len(rows)), dtype=np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        for b in range(B):
+            for h in range(H):
+                for c0 in range(0, len(rows), row_chunk):
+                    r = rows[c0:c0 + row_chunk]
+                    s = _scores(q[b, h, r], k[b, h], scale)
+                    vis = _visible(r, N, causal, None if kv is None else kv[b])
+                    s = np.where(vis, s, -np.inf)
+                    m = _row_max(s)
+                    e = _exp_shifted(s, m)
+                    l = _row_sum(e)
+                    o[b, h, c0:c0 + len(r)] = _normalise(_weighted_values(e, v[b, h]), l)
+                    lse[b, h, c0:c0 + len(r)] = _lse(m, l)
+    return o, lse
+
+
+def attention_materialised(q, k, v, scale, causal=False, key_valid=None):
+    """Standard attention with the full score and probability tables.
+
+    This is the "standard attention" the FlashAttention reading notes contrast
+    with the method (section "problem setting": S = Q K^T and P = softmax(S)
+    both written out in full).  Used only on tiny inputs to cross-check
+    ``attention``.  Returns (o, lse, p) with p the [B, H, N, N] probabilities.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    s = scale * np.matmul(q, np.swapaxes(k, -1, -2))          # [B, H, N, N]
+    hide = np.zeros((B, 1, N, N), dtype=bool)
+    if causal:
+        hide |= np.triu(np.ones((N, N), dtype=bool), k=1)[None, None]
+    if key_valid is not None:
+        hide |= ~np.asarray(key_valid, dtype=bool)[:, None, None, :]
+    s = np.where(hide, -np.inf, s)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        top = s.max(axis=-1, keepdims=True)
+        w = np.exp(s - top)
+        z = w.sum(axis=-1, keepdims=True)
+        p = w / z
+        o = np.matmul(p, v)
+        lse = (top + np.log(z))[..., 0]
+    return o, lse, p
+
+
+def attention_fsum(q, k, v, scale, causal=False, key_valid=None):
+    """Pure-Python attention with every sum exactly rounded (math.fsum).
+
+    Products of two fp32 values are exact in float64, so each dot product is
+    the correctly rounded exact value; every later sum is correctly rounded
+    too.  The result therefore does not depend on the order of the keys,
+    which makes bit-exact permutation checks possible.  Tiny inputs only.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                keys = [j for j in range(N)
+                        if (not causal or j <= i)
+                        and (key_valid is None or key_valid[b][j])]
+                if not keys:
+                    o[b, h, i] = np.nan
+                    lse[b, h, i] = np.nan
+                    continue
+                s = {j: scale * math.fsum(q[b, h, i, t] * k[b, h, j, t] for t in range(d))
+                     for j in keys}
+                m = max(s.values())
+                e = {j: math.exp(s[j] - m) for j in keys}
+                z = math.fsum(e.values())
+                for t in range(d):
+                    o[b, h, i, t] = math.fsum(e[j] * v[b, h, j, t] for j in keys) / z
+                lse[b, h, i] = m + math.log(z)
+    return o, lse

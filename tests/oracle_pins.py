@@ -1,0 +1,319 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a fact it did not compute itself: a value printed on a page, a closed form,
+an invariant of the definition, or another library's routine.  The tests run
+every pin against the oracle as it stands, and run the "independent" pins
+again against deliberately broken copies of single oracle steps to show that
+each plausible mistake is caught.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import fp64 as O
+from workloads import WORKLOADS, make_inputs, to_f64
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, atol, what):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= atol, f"{what}: max abs error {err:.3e} > {atol:.1e}"
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_uniform_closed_form():
+    """Q = 0 makes every score 0: each row averages the values it can see.
+
+    Non-causal: O_i = mean_j V_j and LSE_i = ln N.  Causal: O_i is the mean of
+    V_0..V_i and LSE_i = ln(i + 1).  A small row chunk makes the causal mask
+    cross chunk boundaries, so it must use global query indices.
+    """
+    rng = _rng(1)
+    B, H, N, d = 2, 3, 37, 16
+    q = np.zeros((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    o, lse = O.attention(q, k, v, 0.3)
+    _close(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), 1e-12, "uniform O")
+    _close(lse, np.full((B, H, N), math.log(N)), 1e-12, "uniform LSE")
+    o, lse = O.attention(q, k, v, 0.3, causal=True, row_chunk=7)
+    counts = np.arange(1, N + 1, dtype=np.float64)
+    _close(o, np.cumsum(v, axis=2) / counts[:, None], 1e-12, "causal prefix-mean O")
+    _close(lse, np.broadcast_to(np.log(counts), (B, H, N)), 1e-12, "causal LSE = ln(i+1)")
+
+
+def _identity_probs(beta, n, causal):
+    e = math.exp(beta)
+    p = np.zeros((n, n))
+    for i in range(n):
+        seen = i + 1 if causal else n
+        z = e + seen - 1
+        for j in range(seen):
+            p[i, j] = (e if j == i else 1.0) / z
+    lse = np.array([math.log(e + (i + 1 if causal else n) - 1) for i in range(n)])
+    return p, lse
+
+
+def pin_identity_closed_form():
+    """Q = K = alpha * (first N rows of I_d), V = first N rows of I_d.
+
+    Then s_ij = beta * [i == j] with beta = scale * alpha^2, so
+    P_ij = (e^beta [i==j] + [i!=j]) / (e^beta + N - 1), O = P padded with zero
+    columns, and LSE_i = ln(e^beta + N - 1).  Causal: row i only sees
+    j <= i, so the N above becomes i + 1.  beta = 40 makes LSE ~ 40, which
+    exposes an LSE that forgets the row max.
+    """
+    n, d = 6, 8
+    for alpha, scale in ((3.0, 0.7), (8.0, 0.625)):
+        beta = scale * alpha * alpha
+        eye = np.eye(n, d)[None, None]
+        for causal in (False, True):
+            p, lse_ref = _identity_probs(beta, n, causal)
+            o, lse = O.attention(alpha * eye, alpha * eye, eye, scale, causal=causal)
+            o_ref = np.zeros((n, d))
+            o_ref[:, :n] = p
+            _close(o[0, 0], o_ref, 1e-13, f"identity O beta={beta} causal={causal}")
+            _close(lse[0, 0], lse_ref, 1e-12, f"identity LSE beta={beta} causal={causal}")
+
+
+def pin_single_peak_orientation():
+    """Only query i* and key j* (i* != j*) are non-zero, both along feature 0.
+
+    Row i* gives key j* the score beta = scale * gamma and every other key 0;
+    every other row is uniform.  Scores of K Q^T instead of Q K^T would put
+    the peak in row j*; pairing keys with the wrong values moves it too.
+    """
+    rng = _rng(2)
+    n, d, i_s, j_s, gamma, scale = 9, 4, 2, 6, 5.0, 0.5
+    beta = scale * gamma
+    q = np.zeros((1, 1, n, d))
+    k = np.zeros((1, 1, n, d))
+    q[0, 0, i_s, 0] = gamma
+    k[0, 0, j_s, 0] = 1.0
+    v = rng.standard_normal((1, 1, n, d))
+    o, lse = O.attention(q, k, v, scale)
+    vv = v[0, 0]
+    expect = np.broadcast_to(vv.mean(axis=0), (n, d)).copy()
+    expect[i_s] = (math.exp(beta) * vv[j_s] + vv.sum(axis=0) - vv[j_s]) / (math.exp(beta) + n - 1)
+    lse_ref = np.full(n, math.log(n))
+    lse_ref[i_s] = math.log(math.exp(beta) + n - 1)
+    _close(o[0, 0], expect, 1e-13, "single-peak O")
+    _close(lse[0, 0], lse_ref, 1e-13, "single-peak LSE")
+
+
+# ------------------------------------------------------------------ invariants
+
+def pin_constant_values():
+    """V = c everywhere gives O = c (rows of P sum to one).
+
+    Main oracle: within a few ulp.  fsum variant with c a power of two:
+    bit-exact, since scaling by 2^k commutes with correct rounding.
+    """
+    rng = _rng(3)
+    B, H, N, d = 1, 2, 50, 8
+    q, k = rng.standard_normal((2, B, H, N, d))
+    for c in (0.375, -2.0):
+        for causal in (False, True):
+            o, _ = O.attention(q, k, np.full((B, H, N, d), c), 0.125, causal=causal)
+            _close(o, np.full_like(o, c), 8 * abs(c) * 2.0 ** -52, f"constant V={c}")
+    qs, ks = q[:, :1, :12], k[:, :1, :12]
+    o, _ = O.attention_fsum(qs, ks, np.full((1, 1, 12, 8), 0.5), 0.125)
+    assert np.all(o == 0.5), "fsum oracle: constant V not bit-exact"
+
+
+def pin_single_key():
+    """N = 1: the only probability is exp(0) = 1, so O = V bit-exactly and
+    LSE = scale * q.k."""
+    rng = _rng(4)
+    q, k, v = rng.standard_normal((3, 2, 3, 1, 16))
+    o, lse = O.attention(q, k, v, 0.25)
+    assert np.array_equal(o, v), "N=1: O != V"
+    ref = np.array([[0.25 * math.fsum(q[b, h, 0] * k[b, h, 0]) for h in range(3)] for b in range(2)])
+    _close(lse[..., 0], ref, 1e-13, "N=1 LSE")
+
+
+def pin_causal_row_zero():
+    """Causal row 0 sees only key 0: O_0 = V_0 bit-exactly, LSE_0 = scale*q0.k0."""
+    rng = _rng(5)
+    q, k, v = rng.standard_normal((3, 1, 2, 20, 8))
+    o, lse = O.attention(q, k, v, 0.125, causal=True)
+    assert np.array_equal(o[..., 0, :], v[..., 0, :]), "causal row 0: O != V_0"
+    ref = [0.125 * math.fsum(q[0, h, 0] * k[0, h, 0]) for h in range(2)]
+    _close(lse[0, :, 0], ref, 1e-13, "causal row 0 LSE")
+
+
+def pin_key_value_permutation():
+    """Permuting keys and values together leaves O and LSE unchanged;
+    permuting queries permutes the output rows (non-causal)."""
+    rng = _rng(6)
+    B, H, N, d = 1, 2, 40, 8
+    q, k, v = rng.standard_normal((3, B, H, N, d))
+    perm = rng.permutation(N)
+    o, lse = O.attention(q, k, v, 0.4)
+    o2, lse2 = O.attention(q, k[:, :, perm], v[:, :, perm], 0.4)
+    _close(o2, o, 1e-13, "key/value permutation O")
+    _close(lse2, lse, 1e-13, "key/value permutation LSE")
+    o3, lse3 = O.attention(q[:, :, perm], k, v, 0.4)
+    _close(o3, o[:, :, perm], 1e-13, "query permutation O")
+    _close(lse3, lse[:, :, perm], 1e-13, "query permutation LSE")
+    qs, ks, vs = q[:, :1, :10], k[:, :1, :10], v[:, :1, :10]
+    p = perm[perm < 10]
+    a = O.attention_fsum(qs, ks, vs, 0.4)
+    b = O.attention_fsum(qs, ks[:, :, p], vs[:, :, p], 0.4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), "fsum: permutation not bit-exact"
+
+
+def pin_score_shift():
+    """Adding one vector w to every key adds scale*q_i.w to row i's scores:
+    O is unchanged and LSE_i grows by exactly that amount."""
+    rng = _rng(7)
+    B, H, N, d = 1, 2, 30, 8
+    q, k, v = rng.standard_normal((3, B, H, N, d))
+    w = 3.0 * rng.standard_normal(d)
+    for causal in (False, True):
+        o, lse = O.attention(q, k, v, 0.5, causal=causal)
+        o2, lse2 = O.attention(q, k + w, v, 0.5, causal=causal)
+        _close(o2, o, 1e-12, "score shift O")
+        _close(lse2 - lse, 0.5 * (q @ w), 1e-12, "score shift LSE")
+
+
+def pin_one_hot_limit():
+    """A score 900 above the rest: O_i = V_argmax and LSE_i = 900 up to
+    e^-850.  Any evaluation that exponentiates unshifted scores overflows."""
+    rng = _rng(8)
+    n, d = 8, 4
+    q = 0.1 * rng.standard_normal((1, 1, n, d))
+    k = 0.1 * rng.standard_normal((1, 1, n, d))
+    q[0, 0, 0] = [30.0, 0.0, 0.0, 0.0]
+    k[0, 0, 3] = [30.0, 0.0, 0.0, 0.0]
+    v = rng.standard_normal((1, 1, n, d))
+    o, lse = O.attention(q, k, v, 1.0)
+    _close(o[0, 0, 0], v[0, 0, 3], 1e-40, "one-hot O")
+    _close(lse[0, 0, 0], 900.0 + 0.0, 1e-12, "one-hot LSE")
+
+
+# ------------------------------------------------------ printed worked example
+
+def pin_page_mask_example():
+    """Qiita page, section 6: with q = k = v drawn by torch.manual_seed(0);
+    torch.randn(1, 2, 4, 8) and key 3 padded, the inverted boolean mask
+    matches the additive -inf reference (0.0) and the un-inverted one, which
+    attends only to key 3, differs by 3.46 at most.  Only scale 1/sqrt(8)
+    prints 3.46, so this also pins the default-scale reading."""
+    with open(os.path.join(GOLDEN, "mask_polarity_example.json")) as f:
+        g = json.load(f)
+    gen = torch.Generator().manual_seed(0)
+    x = torch.randn(1, 2, 4, 8, generator=gen).double().numpy()
+    keep = np.array([[True, True, True, False]])
+    scale = 1.0 / math.sqrt(8)
+    ref, _ = O.attention(x, x, x, scale, key_valid=keep)
+    inv, _ = O.attention(x, x, x, scale, key_valid=keep)
+    asis, _ = O.attention(x, x, x, scale, key_valid=~keep)
+    digits = g["printed_decimals"]
+    got_inv = round(float(np.max(np.abs(inv - ref))), digits)
+    got_asis = round(float(np.max(np.abs(asis - ref))), digits)
+    assert got_inv == g["cases"]["inverted_boolean_mask_attends_keys_0_1_2"], got_inv
+    assert got_asis == g["cases"]["boolean_mask_as_is_attends_only_key_3"], got_asis
+
+
+# ----------------------------------------------------------- library routines
+
+def pin_torch_sdpa_float64():
+    """torch's own float64 scaled_dot_product_attention (CPU) and
+    torch.logsumexp of the masked scores agree with the oracle."""
+    import torch.nn.functional as F
+    rng = _rng(9)
+    B, H, N, d = 2, 3, 45, 16
+    q, k, v = (torch.from_numpy(a) for a in rng.standard_normal((3, B, H, N, d)))
+    keep = rng.random((B, N)) > 0.3
+    keep[:, 0] = True
+    for causal in (False, True):
+        for kv in (None, keep):
+            o, lse = O.attention(q.numpy(), k.numpy(), v.numpy(), 0.3, causal=causal, key_valid=kv)
+            mask = torch.ones(B, 1, N, N, dtype=torch.bool)
+            if causal:
+                mask &= torch.ones(N, N, dtype=torch.bool).tril()
+            if kv is not None:
+                mask &= torch.from_numpy(kv)[:, None, None, :]
+            ref = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=0.3)
+            s = (0.3 * (q @ k.transpose(-1, -2))).masked_fill(~mask, float("-inf"))
+            _close(o, ref.numpy(), 1e-12, f"SDPA f64 causal={causal} mask={kv is not None}")
+            _close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12, "logsumexp f64")
+
+
+# ------------------------------------------------------- other implementations
+
+def pin_materialised_brute_force():
+    """The materialised (standard) attention agrees on the tiny workload and
+    on random small shapes; its rows of P sum to one."""
+    w = WORKLOADS["tiny"]
+    q, k, v = (to_f64(t) for t in make_inputs(w))
+    cases = [(q, k, v, w.scale)]
+    rng = _rng(10)
+    for n, d in ((1, 8), (5, 3), (33, 16), (64, 64), (65, 8)):
+        cases.append(tuple(rng.standard_normal((3, 2, 2, n, d))) + (0.2,))
+    for q, k, v, scale in cases:
+        for causal in (False, True):
+            o, lse = O.attention(q, k, v, scale, causal=causal, row_chunk=17)
+            ob, lb, p = O.attention_materialised(q, k, v, scale, causal=causal)
+            _close(o, ob, 1e-12, f"brute force O n={q.shape[2]} causal={causal}")
+            _close(lse, lb, 1e-12, f"brute force LSE n={q.shape[2]} causal={causal}")
+            _close(p.sum(axis=-1), np.ones(p.shape[:-1]), 1e-14 * q.shape[2], "rows of P")
+
+
+def pin_fsum_variant():
+    """The exactly rounded pure-Python variant agrees on tiny shapes."""
+    rng = _rng(11)
+    for n, d, causal in ((1, 4, False), (7, 5, True), (16, 8, False), (13, 6, True)):
+        q, k, v = rng.standard_normal((3, 1, 2, n, d))
+        o, lse = O.attention(q, k, v, 0.35, causal=causal)
+        of, lf = O.attention_fsum(q, k, v, 0.35, causal=causal)
+        _close(o, of, 1e-14, "fsum O")
+        _close(lse, lf, 1e-14, "fsum LSE")
+
+
+def pin_row_sampling():
+    """Evaluating a subset of rows gives those rows of the full result."""
+    rng = _rng(12)
+    q, k, v = rng.standard_normal((3, 1, 2, 70, 8))
+    rows = np.array([0, 5, 63, 64, 69])
+    for causal in (False, True):
+        o, lse = O.attention(q, k, v, 0.3, causal=causal)
+        os_, ls = O.attention(q, k, v, 0.3, causal=causal, rows=rows, row_chunk=2)
+        _close(os_, o[:, :, rows], 1e-14, "sampled rows O")
+        _close(ls, lse[:, :, rows], 1e-14, "sampled rows LSE")
+
+
+INDEPENDENT_PINS = [
+    pin_uniform_closed_form,
+    pin_identity_closed_form,
+    pin_single_peak_orientation,
+    pin_constant_values,
+    pin_single_key,
+    pin_causal_row_zero,
+    pin_key_value_permutation,
+    pin_score_shift,
+    pin_one_hot_limit,
+    pin_page_mask_example,
+]
+
+ALL_PINS = INDEPENDENT_PINS + [
+    pin_torch_sdpa_float64,
+    pin_materialised_brute_force,
+    pin_fsum_variant,
+    pin_row_sampling,
+]

@@ -1,0 +1,53 @@
+"""Plant one plausible mistake at a time in a step of the oracle (on the CPU)
+and check that the independent pins catch it.
+
+The pins used here exclude the materialised brute force, the fsum variant
+and torch's SDPA: closed forms, invariants and the page's printed example
+must be strong enough on their own.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import fp64 as O
+from tests.oracle_pins import INDEPENDENT_PINS
+
+MUTANTS = {
+    "scores_transposed": ("_scores", lambda q, k, scale: scale * (k @ q.T) if q.shape[0] == k.shape[0]
+                          else scale * (q @ k.T)[:, ::-1]),
+    "scale_dropped": ("_scores", lambda q, k, scale: q @ k.T),
+    "scale_squared": ("_scores", lambda q, k, scale: scale * scale * (q @ k.T)),
+    "causal_strict": ("_visible", lambda rows, n, causal, kv: (
+        (np.arange(n)[None, :] < rows[:, None]) if causal else np.ones((len(rows), n), bool))
+        & (True if kv is None else kv[None, :])),
+    "causal_local_rows": ("_visible", lambda rows, n, causal, kv: (
+        (np.arange(n)[None, :] <= (rows - rows[0])[:, None]) if causal else np.ones((len(rows), n), bool))
+        & (True if kv is None else kv[None, :])),
+    "causal_upper": ("_visible", lambda rows, n, causal, kv: (
+        (np.arange(n)[None, :] >= rows[:, None]) if causal else np.ones((len(rows), n), bool))
+        & (True if kv is None else kv[None, :])),
+    "key_mask_ignored": ("_visible", lambda rows, n, causal, kv: (
+        (np.arange(n)[None, :] <= rows[:, None]) if causal else np.ones((len(rows), n), bool))),
+    "no_max_shift": ("_row_max", lambda s: np.zeros(s.shape[0])),
+    "exp_sign_flipped": ("_exp_shifted", lambda s, m: np.exp(m[:, None] - s)),
+    "exp_base_two": ("_exp_shifted", lambda s, m: np.exp2(s - m[:, None])),
+    "sum_drops_last_key": ("_row_sum", lambda e: e[:, :-1].sum(axis=1)),
+    "values_reversed": ("_weighted_values", lambda e, v: e @ v[::-1]),
+    "not_normalised": ("_normalise", lambda ou, l: ou),
+    "lse_without_max": ("_lse", lambda m, l: np.log(l)),
+    "lse_base_two": ("_lse", lambda m, l: m + np.log2(l)),
+    "lse_of_sum_only": ("_lse", lambda m, l: m),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_independent_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in INDEPENDENT_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every independent pin"
