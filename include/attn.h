@@ -1,0 +1,97 @@
+/*
+ * attn.h - exact attention forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * Operation.  For every batch entry b < B and head h < H, with Q, K, V each
+ * holding N rows of d features, the library writes
+ *
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,
+ *     LSE_i = m_i + ln(l_i),  m_i = max_j s_ij,  l_i = sum_j exp(s_ij - m_i),
+ *
+ * where s_ij = scale * q_i . k_j, and a causal call hides key j from query i
+ * whenever j > i.  This is exact attention as defined on the page
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with
+ * IO-Awareness" (reading notes at notes.yuuk.io), section "problem setting";
+ * the kernel follows that page's section "proposed method": it walks K and
+ * V in tiles, keeps a running row max and row sum (tiling), never writes the
+ * N x N score or probability matrices to device memory (kernel fusion), and
+ * keeps the softmax statistics for a backward pass (recomputation) in the
+ * form of LSE.  The result matches the plain definition up to rounding.
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: q, k, v, o are contiguous row-major [B][H][N][d] (d fastest);
+ *     lse is contiguous [B][H][N].  All pointers are device pointers.
+ *   - Ownership: the caller owns every buffer.  q, k, v are only read;
+ *     o and lse are only written, and must not overlap q, k, v or each other.
+ *     The library keeps no pointer after the call returns, allocates no
+ *     device memory (no workspace at any size) and holds no per-call state;
+ *     calls are reentrant and may come from several host threads.
+ *   - Stream: `stream` is a hipStream_t passed as void*; NULL means the
+ *     default stream.  The call only enqueues work: it returns before the
+ *     kernel runs, and the caller synchronises.
+ *   - scale: any finite float; scale < 0 is allowed.  The usual choice is
+ *     1/sqrt(d).
+ *   - causal: 0 = every query sees all N keys; non-zero = query i sees keys
+ *     0..i (the diagonal included, so no row is empty).
+ *   - Numerics: scores, the online softmax and both products accumulate in
+ *     fp32.  Non-finite inputs are not scrubbed; they propagate as the
+ *     definition says.
+ *   - Errors are reported synchronously, before anything is enqueued; on an
+ *     error the outputs are untouched.  A fault inside the kernel surfaces at
+ *     the caller's next synchronisation (HIP convention).  No C++ exception
+ *     crosses this interface.
+ */
+#ifndef EXACT_ATTENTION_29_AMD_ATTN_H
+#define EXACT_ATTENTION_29_AMD_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    /* A null pointer; B, H or N below 1; d other than 64; a non-finite
+     * scale; or B*H*N*d at or above 2^31 elements. */
+    ATTN_E_INVALID = 1,
+    /* q, k, v or o not 16-byte aligned (the kernels move 128-bit vectors;
+     * rows of 64 features keep every row aligned), or lse not 4-byte
+     * aligned. */
+    ATTN_E_ALIGN = 2,
+    /* No HIP device is current, or the current device is not gfx950. */
+    ATTN_E_DEVICE = 3,
+    /* The kernel launch was rejected by the runtime. */
+    ATTN_E_LAUNCH = 4
+} attn_status;
+
+/*
+ * attn_fwd: bf16 input and output, the main path.
+ *   q, k, v : const bf16 [B][H][N][d]   (bf16 = 16-bit bfloat, raw bits)
+ *   o       : bf16 [B][H][N][d], rounded to nearest-even from fp32
+ *   lse     : float [B][H][N], natural-log log-sum-exp of the scaled,
+ *             masked scores of each query row
+ *   B, H, N : batch, heads, sequence length (queries = keys = N); N may be
+ *             any value >= 1, not only a multiple of the tile size
+ *   d       : head size; 64 is the only size built
+ * The probabilities multiplying V are rounded to bf16 (nearest-even) before
+ * that product; the row sum l adds up the unrounded fp32 probabilities.
+ */
+attn_status attn_fwd(const void *q, const void *k, const void *v, void *o,
+                     float *lse, int B, int H, int N, int d, float scale,
+                     int causal, void *stream);
+
+/*
+ * attn_fwd_fp32: the same operation with fp32 input, output and arithmetic
+ * throughout (no bf16 or reduced-precision products).  Same layout,
+ * ownership, stream and error rules as attn_fwd; q, k, v, o are float.
+ */
+attn_status attn_fwd_fp32(const float *q, const float *k, const float *v,
+                          float *o, float *lse, int B, int H, int N, int d,
+                          float scale, int causal, void *stream);
+
+/* Static, human-readable text for a status code; never NULL. */
+const char *attn_strerror(attn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_29_AMD_ATTN_H */

@@ -1,0 +1,99 @@
+"""The C-ABI library: it loads, exports every declared entry point, and its
+host-side validation works without a GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_29_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(ea.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ea.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_library_exports_nothing_else_c_visible():
+    # the only extern "C" symbols are the declared ones
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", ea.library_path()],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    attn = sorted(n for n in names if n.startswith("attn_"))
+    assert attn == declared_functions()
+
+
+def test_strerror_covers_every_status():
+    texts = [ea.attn_strerror(s) for s in range(5)]
+    assert texts[0] == "success"
+    assert len(set(texts)) == 5
+    assert ea.attn_strerror(99) == "unknown status"
+
+
+ALIGNED = 0x100000  # a fake, 16-byte aligned address; never dereferenced
+
+
+def call(fn, **kw):
+    args = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED,
+                B=1, H=1, N=8, d=64, scale=0.125, causal=0, stream=None)
+    args.update(kw)
+    lib = ea.load_library()
+    return getattr(lib, fn)(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                            args["B"], args["H"], args["N"], args["d"], args["scale"],
+                            args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_fp32"])
+@pytest.mark.parametrize("bad, status", [
+    (dict(q=None), ea.ATTN_E_INVALID),
+    (dict(lse=None), ea.ATTN_E_INVALID),
+    (dict(B=0), ea.ATTN_E_INVALID),
+    (dict(H=-1), ea.ATTN_E_INVALID),
+    (dict(N=0), ea.ATTN_E_INVALID),
+    (dict(d=128), ea.ATTN_E_INVALID),
+    (dict(d=32), ea.ATTN_E_INVALID),
+    (dict(scale=float("nan")), ea.ATTN_E_INVALID),
+    (dict(scale=float("inf")), ea.ATTN_E_INVALID),
+    (dict(B=1 << 12, H=1 << 12, N=2), ea.ATTN_E_INVALID),   # 2^31 elements
+    (dict(q=ALIGNED + 8), ea.ATTN_E_ALIGN),
+    (dict(v=ALIGNED + 2), ea.ATTN_E_ALIGN),
+    (dict(o=ALIGNED + 4), ea.ATTN_E_ALIGN),
+    (dict(lse=ALIGNED + 2), ea.ATTN_E_ALIGN),
+])
+def test_validation_rejects(fn, bad, status):
+    assert call(fn, **bad) == status
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_fp32"])
+def test_valid_arguments_without_a_gpu_report_no_device(fn):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call(fn) == ea.ATTN_E_DEVICE
+    assert call(fn, lse=ALIGNED + 4, causal=1, scale=-0.5, N=1) == ea.ATTN_E_DEVICE
+
+
+def test_binding_raises_without_compute_on_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.forward(q, q, q)
+    with pytest.raises(TypeError):
+        ea.forward(q.half(), q.half(), q.half())

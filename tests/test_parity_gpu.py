@@ -1,0 +1,308 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every test here runs the production entry points (attn_fwd / attn_fwd_fp32
+via the Python binding) on cuda:0 and compares element by element with the
+oracle on the same seeded inputs: in full where the oracle finishes in
+seconds, and on sampled rows (every head, both ends, the ragged tail and
+random rows) at the full 3 MP and 8 MP patch sizes.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_29_amd as ea
+from oracle import attention as oracle_attention
+from tests.parity import BF16, FP32, assert_within, errors
+from workloads import PATCH_SWEEP, WORKLOADS, Workload, make_inputs, sample_rows, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ea.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_run(q, k, v, scale, causal):
+    o, lse = ea.forward(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(w, q, k, v, o, lse, rows=None, what=""):
+    qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
+    o_ref, lse_ref = oracle_attention(qf, kf, vf, w.scale, causal=w.causal, rows=rows)
+    o_h, lse_h = to_f64(o), to_f64(lse)
+    if rows is not None:
+        o_h, lse_h = o_h[:, :, rows], lse_h[:, :, rows]
+    err = errors(o_h, lse_h, o_ref, lse_ref)
+    assert_within(err, FP32 if w.dtype == "fp32" else BF16, what or w.name)
+    return err
+
+
+def bf16_workload(n, causal, B=2, H=3, seed=100, sigma=1.0, scale=0.125):
+    return Workload(f"edge_N{n}_{'c' if causal else 'nc'}", B, H, n, 64, "bf16", sigma, scale,
+                    causal, seed + n, "edge size")
+
+
+# ------------------------------------------------------------ the workloads
+
+@pytest.mark.parametrize("name", ["tiny", "bert_large", "gpt2_small_causal"])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    print(f"[case] {name} {w.shape} {w.dtype} causal={w.causal}", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = gpu_run(q, k, v, w.scale, w.causal)
+    err = compare(w, q, k, v, o, lse)
+    print(f"[ok] {name} {err}", flush=True)
+
+
+@pytest.mark.parametrize("n", list(PATCH_SWEEP) + [11616, 38400])
+def test_patch_workload_sampled(n):
+    base = WORKLOADS["patch_8mp"] if n == 38400 else WORKLOADS["patch_3mp"]
+    w = base if n == base.N else base.with_n(n)
+    print(f"[case] {w.name} {w.shape}", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = gpu_run(q, k, v, w.scale, w.causal)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    rows = sample_rows(n, 40)
+    err = compare(w, q, k, v, o, lse, rows=rows)
+    print(f"[ok] {w.name} rows={len(rows)} {err}", flush=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_patch_3mp_causal_variant_sampled(causal):
+    """The 3 MP shape also run causal: exercises the causal skip at 182 tiles."""
+    w = Workload("patch_3mp_causal", 1, 16, 11616, 64, "bf16", 0.5, 0.125, causal, 3, "")
+    q, k, v = make_inputs(w)
+    o, lse = gpu_run(q, k, v, w.scale, w.causal)
+    compare(w, q, k, v, o, lse, rows=sample_rows(w.N, 40))
+
+
+# ------------------------------------------------------------ edge sizes
+
+EDGE_N = [1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 511, 513, 1000]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", EDGE_N)
+def test_edge_sizes_bf16(n, causal):
+    w = bf16_workload(n, causal)
+    print(f"[case] bf16 N={n} causal={causal}", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = gpu_run(q, k, v, w.scale, causal)
+    compare(w, q, k, v, o, lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 100, 128, 129, 257])
+def test_edge_sizes_fp32(n, causal):
+    w = Workload(f"fp32_N{n}", 2, 2, n, 64, "fp32", 1.0, 0.125, causal, 200 + n, "")
+    print(f"[case] fp32 N={n} causal={causal}", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = gpu_run(q, k, v, w.scale, causal)
+    compare(w, q, k, v, o, lse)
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 1.0, 0.01])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_other_scales(scale, dtype):
+    """Negative, zero, large and small scales.  With N(0,1) inputs and d=64
+    the scores are ~N(0, (8*scale)^2); an fp32 dot product of 64 terms carries
+    an absolute error proportional to the score size, which exp turns into a
+    relative error of O.  The fp32 bar therefore grows with 8*|scale| beyond
+    the 1e-5 that holds at scale 1/8."""
+    for causal in (False, True):
+        w = Workload("scale", 1, 2, 200, 64, dtype, 1.0, scale, causal, 300, "")
+        q, k, v = make_inputs(w)
+        o, lse = gpu_run(q, k, v, scale, causal)
+        if dtype == "fp32":
+            qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
+            o_ref, lse_ref = oracle_attention(qf, kf, vf, scale, causal=causal)
+            grow = max(1.0, 8.0 * abs(scale))
+            bar = dict(o_max=1e-5 * grow, o_mean=1e-5, lse_max=1e-5 * grow, rel_fro=1e-5 * grow)
+            assert_within(errors(to_f64(o), to_f64(lse), o_ref, lse_ref), bar, f"scale={scale}")
+        else:
+            compare(w, q, k, v, o, lse, what=f"scale={scale} {dtype} causal={causal}")
+
+
+# ------------------------------------------------------------ invariants
+
+def bf16_ulp(x):
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [200, 3952])
+def test_constant_values_give_constant_output(n, causal):
+    """V = c (a bf16 value): every output element is exactly c after rounding."""
+    w = bf16_workload(n, causal, B=1, H=4)
+    q, k, _ = make_inputs(w)
+    for c in (0.375, -1.25):
+        v = torch.full_like(q, c)
+        o, _ = gpu_run(q, k, v, w.scale, causal)
+        assert bool((o.float() == c).all()), f"constant V={c}: {o.float().unique()[:8]}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_single_key_gives_values(dtype):
+    w = Workload("n1", 3, 5, 1, 64, dtype, 1.0, 0.125, False, 400, "")
+    q, k, v = make_inputs(w)
+    for causal in (False, True):
+        o, lse = gpu_run(q, k, v, w.scale, causal)
+        assert torch.equal(o.cpu(), v), "N=1: O != V"
+        ref = w.scale * (to_f64(q) * to_f64(k)).sum(-1)
+        assert np.abs(to_f64(lse) - ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_causal_row_zero_is_v0(dtype):
+    w = Workload("row0", 2, 3, 777, 64, dtype, 1.0, 0.125, True, 401, "")
+    q, k, v = make_inputs(w)
+    o, _ = gpu_run(q, k, v, w.scale, True)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+
+
+def test_key_value_permutation():
+    w = bf16_workload(1000, False, B=1, H=2)
+    q, k, v = make_inputs(w)
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(w.N))
+    o1, l1 = gpu_run(q, k, v, w.scale, False)
+    o2, l2 = gpu_run(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), w.scale, False)
+    a, b = to_f64(o1), to_f64(o2)
+    # Permuting keys changes the order of the key tiles, hence the running max
+    # against which each probability is formed and rounded to bf16.  Each
+    # rounded probability is within 2^-8 (relative) of its exact value, so
+    # each result is within 2^-8 * sum_j p_j |v_j| of the exact-probability
+    # result (plus output rounding and fp32 noise), and the two results within
+    # twice that.  sum_j p_j |v_j| is the oracle's output for |V|.
+    w_abs, _ = oracle_attention(to_f64(q), to_f64(k), np.abs(to_f64(v)), w.scale)
+    tol = 2.0 ** -7 * w_abs + bf16_ulp(a) + bf16_ulp(b) + 1e-6
+    bad = np.abs(a - b) > tol
+    assert not bad.any(), f"{bad.sum()} elements differ; max {np.abs(a - b).max():.3e}"
+    assert np.abs(to_f64(l1) - to_f64(l2)).max() <= 1e-5
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [129, 11616])
+def test_uniform_attention_closed_form(n, causal):
+    """Q = 0: O_i is the mean of the visible values and LSE_i = ln(#visible).
+    A dropped or repeated key tile, or unmasked padding keys, moves LSE by more
+    than the 1e-3 bar at every N here."""
+    w = Workload("uniform", 1, 2, n, 64, "bf16", 0.5, 0.125, causal, 402, "")
+    _, k, v = make_inputs(w)
+    q = torch.zeros_like(k)
+    o, lse = gpu_run(q, k, v, w.scale, causal)
+    cnt = np.arange(1, n + 1, dtype=np.float64) if causal else np.full(n, float(n))
+    assert np.abs(to_f64(lse) - np.log(cnt)).max() <= 1e-3
+    vf = to_f64(v)
+    mean = np.cumsum(vf, axis=2) / cnt[:, None] if causal else np.broadcast_to(vf.mean(2, keepdims=True), vf.shape)
+    assert np.abs(to_f64(o) - mean).max() <= 2e-2
+
+
+def test_identity_closed_form():
+    """Q = K = alpha * I rows (N <= 64): s_ij = beta [i == j], so
+    P_ij = (e^beta [i==j] + [i!=j]) / (e^beta + seen - 1) and
+    LSE_i = ln(e^beta + seen - 1), seen = N (or i + 1 when causal).
+    beta = 3 ln 2 makes every probability exact in bf16 (1 and 1/8); beta = 2
+    makes 47 equal off-diagonal probabilities that all round the same way in
+    bf16, which the fp32 row sum must not inherit."""
+    n, alpha = 48, 4.0
+    eye = torch.zeros(1, 1, n, 64)
+    eye[0, 0, torch.arange(n), torch.arange(n)] = 1.0
+    q = (alpha * eye).to(torch.bfloat16)
+    v = eye.to(torch.bfloat16)
+    for beta in (3 * math.log(2), 2.0):
+        scale = beta / (alpha * alpha)
+        for causal in (False, True):
+            o, lse = gpu_run(q, q, v, scale, causal)
+            seen = np.arange(1, n + 1) if causal else np.full(n, n)
+            exact = np.log(math.exp(beta) + seen - 1)
+            assert np.abs(to_f64(lse)[0, 0] - exact).max() <= 1e-5, (beta, causal)
+            p_diag = math.exp(beta) / (math.exp(beta) + seen - 1)
+            assert np.abs(to_f64(o)[0, 0, np.arange(n), np.arange(n)] - p_diag).max() <= 4e-3
+
+
+def test_one_hot_limit():
+    """One score ~200 log2-units above the rest: O_i = V_argmax exactly."""
+    n = 300
+    rng = np.random.default_rng(403)
+    q = torch.zeros(1, 1, n, 64)
+    k = torch.from_numpy(0.01 * rng.standard_normal((1, 1, n, 64)).astype(np.float32))
+    q[0, 0, :, 0] = 16.0
+    k[0, 0, 137, 0] = 8.0
+    v = torch.from_numpy(rng.standard_normal((1, 1, n, 64)).astype(np.float32))
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, _ = gpu_run(q, k, v, 1.0, False)
+    assert torch.equal(o[0, 0].cpu(), v[0, 0, 137].expand(n, 64))
+
+
+def test_deterministic_repeat():
+    w = WORKLOADS["bert_large"]
+    q, k, v = (t.to(DEV) for t in make_inputs(w))
+    o1, l1 = ea.forward(q, k, v, scale=w.scale)
+    o2, l2 = ea.forward(q, k, v, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------ memory behaviour
+
+def test_no_workspace_and_no_out_of_bounds_writes():
+    """The call allocates nothing beyond O and LSE, and writes nothing outside
+    them: O and LSE sit inside guard bands filled with a canary."""
+    w = WORKLOADS["patch_3mp"].with_n(1944)
+    q, k, v = (t.to(DEV) for t in make_inputs(w))
+    B, H, N, d = w.shape
+    guard = 4096
+    o_buf = torch.full((guard + B * H * N * d + guard,), -7.0, dtype=torch.bfloat16, device=DEV)
+    l_buf = torch.full((guard + B * H * N + guard,), -7.0, dtype=torch.float32, device=DEV)
+    o = o_buf[guard:guard + B * H * N * d].view(B, H, N, d)
+    lse = l_buf[guard:guard + B * H * N].view(B, H, N)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    ea.forward(q, k, v, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() - base == 0
+    assert torch.cuda.mem_get_info()[0] == free0
+    for buf in (o_buf, l_buf):
+        assert bool((buf[:guard] == -7.0).all()) and bool((buf[-guard:] == -7.0).all())
+    assert bool(torch.isfinite(o.float()).all())
+
+
+def test_runs_on_the_callers_stream():
+    w = bf16_workload(700, True)
+    q, k, v = make_inputs(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qd, kd, vd = (t.to(DEV, non_blocking=False) for t in (q, k, v))
+        o, lse = ea.forward(qd, kd, vd, scale=w.scale, causal=True)
+    s.synchronize()
+    compare(w, q, k, v, o, lse)
+
+
+def test_errors_leave_outputs_untouched():
+    q = torch.randn(1, 2, 64, 32, device=DEV).to(torch.bfloat16)
+    with pytest.raises(ea.AttnError) as e:
+        ea.forward(q, q, q)
+    assert e.value.code == ea.ATTN_E_INVALID
+    q = torch.randn(1, 2, 64, 64, device=DEV).to(torch.bfloat16)
+    o = torch.full_like(q, 3.0)
+    lse = torch.full((1, 2, 64), 3.0, device=DEV)
+    with pytest.raises(ea.AttnError):
+        ea.attn_fwd(q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    1, 2, 64, 64, float("nan"), 0, None)
+    torch.cuda.synchronize()
+    assert bool((o == 3.0).all()) and bool((lse == 3.0).all())
