@@ -202,6 +202,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", default=None, help="write one JSON line per workload to this file")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -216,6 +218,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_mib:
+        # A plain copy kernel of known size: reads and writes copy_mib MiB once.
+        # rocprofv3's FETCH_SIZE / WRITE_SIZE for it give the counters' scale.
+        n = args.copy_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 3}))
+        return
 
     if args.sweep:
         cases = [WORKLOADS[n] for n in ("bert_large", "gpt2_small_causal")]

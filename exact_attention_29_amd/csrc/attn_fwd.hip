@@ -11,23 +11,32 @@
 // LSE, are written).  The block sizes on that page were chosen for another
 // GPU's shared memory; the tiles below are sized for gfx950 instead.
 //
-// bf16 kernel, one workgroup = 4 waves = 256 query rows of one head:
-//   * each wave owns 64 queries as two 32-query blocks; its Q^T operands stay
-//     in VGPRs for the whole kernel;
-//   * K and V tiles of 64 keys are staged through double-buffered LDS with
-//     16-byte global loads, in a row-major layout whose 16-byte chunks are
-//     XOR-swizzled per row so both read patterns below are bank-conflict free;
+// bf16 kernel.  One workgroup = 8 waves = 256 query rows of one head, one
+// workgroup per CU (two waves per SIMD):
+//   * each wave owns 32 query rows; their Q^T operands stay in VGPRs;
+//   * K and V tiles of 64 keys go through a 4-stage LDS ring, rows padded to
+//     144 B (K) and 192 B (V) so both read patterns below are bank-conflict
+//     free and every LDS address is a per-lane constant plus an immediate;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: lane l then holds 16 keys of
-//     ONE query (l % 32), so the row max / row sum is a per-lane reduction
-//     plus one exchange with lane l ^ 32;
+//     ONE query (l % 32), so row reductions stay in the lane plus one
+//     exchange with lane l ^ 32;
 //   * the S^T accumulator layout is exactly the B-operand layout of the next
 //     MFMA, so P^T feeds O^T += V^T P^T without any lane shuffle; the V^T
 //     operand is read from the row-major V tile with ds_read_b64_tr_b16;
-//   * online softmax in fp32 with exp2 and scale*log2(e) folded into one FMA;
-//     l sums the fp32 probabilities (so LSE carries fp32 error only), and
-//     P is rounded to bf16 just before the PV product;
+//   * software pipeline over half tiles (32 keys): step j issues the MFMAs of
+//     PV(j-1) and S(j+1) interleaved one by one with the vector-ALU softmax of
+//     S(j), while the LDS operands of step j+1 are read.  On gfx950 a wave's
+//     transcendental ops overlap its own MFMAs only when interleaved this
+//     way; another wave's do not;
+//   * online softmax in fp32: exp2 with scale*log2(e) folded into one FMA,
+//     l sums the fp32 probabilities, P is rounded to bf16 for the PV product.
+//     Edge tiles take the exact tile max; the steady state reuses the running
+//     reference max and needs none.  A partial row sum above 2^32 (a score
+//     far above the reference, or an overflow) flags the wave, which then
+//     recomputes its rows with the exact max on every tile (a rare path that
+//     reads K and V straight from global memory);
 //   * causal: key tiles past a wave's last query are skipped, only the
-//     diagonal and ragged tiles pay for masking.
+//     diagonal and ragged half tiles pay for masking.
 // fp32 kernel: one thread per query row, fp32 FMA on the vector ALU, K/V
 // tiles broadcast from LDS; same online softmax.  Used for fp32 I/O.
 
@@ -36,6 +45,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -52,18 +62,23 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kD = 64;                       // head size
-constexpr int kBc = 64;                      // keys per K/V tile
-constexpr int kWaves = 4;                    // waves per workgroup
-constexpr int kQBlocks = 2;                  // 32-query blocks per wave
-constexpr int kBr = kWaves * kQBlocks * 32;  // 256 queries per workgroup
+constexpr int kBc = 64;                      // keys per K/V tile (two half tiles)
+constexpr int kWaves = 8;                    // waves per workgroup (2 per SIMD)
+constexpr int kBr = kWaves * 32;             // 256 queries per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kTileBytes = kBc * kD * 2;     // 8 KiB per K or V tile
-constexpr int kStageBytes = 2 * kTileBytes;  // K tile then V tile
-constexpr int kLdsBytes = 2 * kStageBytes;   // double buffered: 32 KiB
+constexpr int kKRow = 144;                   // bytes per K row in LDS (128 + 16 pad)
+constexpr int kVRow = 192;                   // bytes per V row in LDS (128 + 64 pad)
+constexpr int kKTile = kBc * kKRow;          // 9216
+constexpr int kVTile = kBc * kVRow;          // 12288
+constexpr int kStageBytes = kKTile + kVTile; // 21504
+constexpr int kStages = 4;                   // LDS ring of K/V tiles
+constexpr int kLdsBytes = kStages * kStageBytes;  // 86016: one workgroup per CU
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kTau = 8.0f;  // reference-max slack, log2 units: p <= 256
+constexpr float kTau = 8.0f;                 // slack when the reference max is set
+constexpr float kRedo = 4294967296.0f;       // 2^32: a partial row sum above this
+                                             // means the reference max is stale
 
 struct Bf16Args {
   const uint16_t* q;
@@ -74,21 +89,9 @@ struct Bf16Args {
   int n;            // sequence length
   int q_tiles;      // ceil(n / kBr)
   int total_tiles;  // B * H * q_tiles
-  float c;          // |scale| * log2(e)
+  float c;          // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign;  // 0x80008000 when scale < 0 (Q negated), else 0
 };
-
-// 3-bit reversal: the per-row chunk swizzle is bitrev3((row >> 1) & 7).
-__device__ __forceinline__ int bitrev3(int x) {
-  return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
-}
-
-__device__ __forceinline__ int swz(int row) { return bitrev3((row >> 1) & 7); }
-
-// Byte offset of 16-byte chunk `chunk` of tile row `row` (8 chunks per row).
-__device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ swz(row)) << 4);
-}
 
 // max(x[lane], x[lane ^ 32]) in every lane, via v_permlane32_swap (which
 // exchanges the upper half of one register with the lower half of another).
@@ -113,6 +116,16 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
 }
 
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
+  return *(const bf16x8*)(base + off);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_vt(const char* p0, const char* p1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <bool kCausal>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -134,244 +147,379 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // which half of the wave
-  const int q_wave = qt * kBr + wave * (kQBlocks * 32);
+  const int q_wave = qt * kBr + wave * 32;
+  const int qi = q_wave + l32;  // this lane's query row
 
   // ---- Q^T operands (B operand of S^T = K Q^T): lane holds 8 consecutive
-  // features (16*ks + 8*hi ..) of query q_wave + 32*qb + l32.
-  bf16x8 qop[kQBlocks][4];
+  // features (16*ks + 8*hi ..) of query qi.
+  bf16x8 qop[4];
 #pragma unroll
-  for (int qb = 0; qb < kQBlocks; ++qb) {
-    const int qi = q_wave + qb * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (qi < n) w = *(const u32x4*)(qg + (size_t)qi * kD + 16 * ks + 8 * hi);
-      w ^= a.q_sign;
-      qop[qb][ks] = __builtin_bit_cast(bf16x8, w);
-    }
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (qi < n) w = *(const u32x4*)(qg + (size_t)qi * kD + 16 * ks + 8 * hi);
+    w ^= a.q_sign;
+    qop[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
-  // ---- number of key tiles this workgroup visits
+  // ---- key range
   int kv_end = n;
   if (kCausal) kv_end = min(n, qt * kBr + kBr);
-  const int n_tiles = (kv_end + kBc - 1) / kBc;
-  // last key tile with any visible key for this wave (causal skip)
-  // (a wave whose rows all lie past N has nothing to compute)
-  const int wave_last_key =
-      q_wave >= n ? -1 : (kCausal ? min(n - 1, q_wave + kQBlocks * 32 - 1) : n - 1);
+  const int n_half = (kv_end + 31) / 32;  // half tiles of 32 keys
+  const int n_tiles = (n_half + 1) / 2;
+  // last key / half tile with any visible key for this wave
+  const int wave_last_key = q_wave >= n ? -1 : (kCausal ? min(n - 1, q_wave + 31) : n - 1);
+  const int last_h = wave_last_key < 0 ? -1 : wave_last_key / 32;
 
-  // ---- global -> register staging: thread handles chunks tid and tid+256 of
-  // the 512 16-byte chunks of a tile: row = idx / 8, chunk = idx % 8.
-  u32x4 kreg[2], vreg[2];
+  // ---- global -> LDS staging: thread tid moves 16-byte chunk tid of the K
+  // tile and of the V tile (row tid / 8, chunk tid % 8).
+  constexpr int kChunks = 512 / kThreads;  // 16-byte chunks per thread per tile
+  const int st_row = tid >> 3, st_ch = tid & 7;  // chunk j adds kThreads/8 rows
+  const int st_koff = st_row * kKRow + st_ch * 16;
+  const int st_voff = kKTile + st_row * kVRow + st_ch * 16;
+  u32x4 kreg[kChunks], vreg[kChunks];
   auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int idx = tid + j * kThreads;
-      const int row = idx >> 3, ch = idx & 7;
-      const int key = kt * kBc + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[j] = z;
-      vreg[j] = z;
+    for (int jc = 0; jc < kChunks; ++jc) {
+      const int key = kt * kBc + st_row + jc * (kThreads / 8);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kreg[jc] = z;
+      vreg[jc] = z;
       if (key < n) {
-        kreg[j] = *(const u32x4*)(kg + (size_t)key * kD + ch * 8);
-        vreg[j] = *(const u32x4*)(vg + (size_t)key * kD + ch * 8);
+        kreg[jc] = *(const u32x4*)(kg + (size_t)key * kD + st_ch * 8);
+        vreg[jc] = *(const u32x4*)(vg + (size_t)key * kD + st_ch * 8);
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    char* base = lds + stage * kStageBytes;
+  auto store_regs = [&](char* base) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int idx = tid + j * kThreads;
-      const int row = idx >> 3, ch = idx & 7;
-      const int off = tile_off(row, ch);
-      *(u32x4*)(base + off) = kreg[j];
-      *(u32x4*)(base + kTileBytes + off) = vreg[j];
+    for (int jc = 0; jc < kChunks; ++jc) {
+      *(u32x4*)(base + st_koff + jc * (kThreads / 8) * kKRow) = kreg[jc];
+      *(u32x4*)(base + st_voff + jc * (kThreads / 8) * kVRow) = vreg[jc];
+    }
+  };
+  auto store_tile = [&](int stage) { store_regs(lds + stage * kStageBytes); };
+
+  // ---- per-lane LDS read offsets within a stage
+  // K operand (A of S^T), half h, step ks: row 32*h + l32, features 16*ks + 8*hi.
+  const int k_lane = l32 * kKRow + hi * 16;  // + 32*h*kKRow + 32*ks
+  // V^T operand via ds_read_b64_tr_b16 (half h, step tt, feature block db):
+  // in each 16-lane group g, lane j points at row 32*h + 16*tt + 4*hi + (j>>2)
+  // (+8 for the second half of the operand) and feature 32*db + 16*(g&1) + 4*(j&3).
+  const int g = lane >> 4, j16 = lane & 15;
+  const int v_lane = kKTile + (4 * hi + (j16 >> 2)) * kVRow + 2 * (16 * (g & 1) + 4 * (j16 & 3));
+  // + (32*h + 16*tt + 8*sec) * kVRow + 64*db
+
+  const float c = a.c;
+  f32x16 acc[2];  // O^T, feature blocks db = 0, 1
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  bool stale = false;  // set when the steady state saw a stale reference max
+  const f32x16 zero16 = {};
+
+  // ---- the three pieces of work on one half tile (32 keys).  Half tile j
+  // covers keys 32*j .. 32*j+31: tile j/2 (LDS stage (j/2) % 4), rows 32*(j%2)..
+  //
+  // S^T = K Q^T: s holds keys 32*j + 8*(r/4) + 4*hi + r%4 of query qi.
+  auto compute_s = [&](const char* stage_base, int h, f32x16& s) {
+    const char* kb = stage_base + k_lane + 32 * h * kKRow;
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kb, 0), qop[0], zero16, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < 4; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kb, 32 * ks), qop[ks], s, 0, 0, 0);
+  };
+  // O^T += V^T P^T over one half tile; pop[tt] covers its keys 16*tt .. +15.
+  auto compute_pv = [&](const char* stage_base, int h, const bf16x8 (&pop)[2]) {
+    const char* vb = stage_base + v_lane + 32 * h * kVRow;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const char* p = vb + 16 * tt * kVRow + 64 * db;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_vt(p, p + 8 * kVRow), pop[tt], acc[db], 0, 0, 0);
+      }
+  };
+  auto stage_base = [&](int j) { return lds + ((j >> 1) & (kStages - 1)) * kStageBytes; };
+
+  // Hidden keys of half tile j become -inf (ragged end, causal diagonal).
+  auto needs_mask = [&](int j) { return 32 * j + 32 > n || (kCausal && 32 * j + 31 > q_wave); };
+  auto apply_mask = [&](int j, f32x16& s) {
+    const int lim = kCausal ? min(qi, n - 1) : n - 1;  // last visible key
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * j + 8 * (r >> 2) + 4 * hi + (r & 3);
+      s[r] = key <= lim ? s[r] : -INFINITY;
     }
   };
 
-  // ---- per-lane constant LDS offsets
-  // K operand (A of S^T): row kb*32 + l32, chunk 2*ks + hi.
-  int k_off[4];
+  // exp2(c*s - m) for the 16 scores, packed into the two bf16 P operands;
+  // returns this lane's fp32 partial row sum.
+  auto exp_pack = [&](const f32x16& s, float m, bf16x8 (&pop)[2]) -> float {
+    float lsum = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) k_off[ks] = tile_off(l32, 2 * ks + hi);
-  // V^T operand via ds_read_b64_tr_b16: in each 16-lane group g, lane j
-  // points at row 16*t + 4*hi + (j >> 2) (+8 for the second half of the
-  // operand) and feature 32*db + 16*(g & 1) + 4*(j & 3).
-  const int g = lane >> 4, j16 = lane & 15;
-  int v_off[2][2];  // [sec][db] for kb = t = 0
+    for (int tt = 0; tt < 2; ++tt) {
+      bf16x8 p8;
 #pragma unroll
-  for (int sec = 0; sec < 2; ++sec) {
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int row = 4 * hi + (j16 >> 2) + 8 * sec;
-      const int feat = 32 * db + 16 * (g & 1) + 4 * (j16 & 3);
-      const int byte = feat * 2;
-      v_off[sec][db] = row * 128 + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
+      for (int i = 0; i < 8; i += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * tt + i], c, -m));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * tt + i + 1], c, -m));
+        lsum += e0;
+        lsum += e1;
+        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        p8[i] = pr[0];
+        p8[i + 1] = pr[1];
+      }
+      pop[tt] = p8;
     }
-  }
-  // rows 16*t + 32*kb keep the swizzle of row (since swz uses bits 1..3 and
-  // 16*t + 32*kb only adds multiples of 16): offset += (16*t + 32*kb) * 128.
+    return lsum;
+  };
 
-  const float c = a.c;
-  f32x16 acc[kQBlocks][2];
-  float m_run[kQBlocks], l_run[kQBlocks];
+  // Softmax of one half tile with an exact tile max (general path and the
+  // rare redo).  m_run (log2 units, scale folded in) is the reference the
+  // probabilities are taken against; it is raised only when some row's max
+  // exceeds it by more than kTau.  Any reference gives the same O and LSE.
+  // Returns the factor acc must be scaled by (1 when unchanged).
+  auto softmax_exact = [&](const f32x16& s, bf16x8 (&pop)[2], bool& raised) -> float {
+    float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-  for (int qb = 0; qb < kQBlocks; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+    mx = half_swap_max(mx) * c;
+    raised = __any(mx > m_run + kTau);
+    const float m_new = raised ? fmaxf(m_run, mx) : m_run;
+    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+    l_run = l_run * alpha + exp_pack(s, msub, pop);
+    return alpha;
+  };
+  auto rescale = [&](float alpha) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
-  }
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+  };
 
+  // General step (any j): j is the half tile being softmaxed; s_cur/p_cur its
+  // buffers, s_nxt receives S(j+1), p_prv holds P(j-1).
+  auto step_general = [&](int j, f32x16& s_cur, bf16x8 (&p_cur)[2], f32x16& s_nxt,
+                          const bf16x8 (&p_prv)[2]) {
+    if (j >= 1 && j - 1 <= last_h) compute_pv(stage_base(j - 1), (j - 1) & 1, p_prv);
+    if (j + 1 < n_half && j + 1 <= last_h) compute_s(stage_base(j + 1), (j + 1) & 1, s_nxt);
+    if (j <= last_h) {
+      if (needs_mask(j)) apply_mask(j, s_cur);
+      bool raised;
+      const float alpha = softmax_exact(s_cur, p_cur, raised);
+      if (raised) rescale(alpha);
+    }
+  };
+
+  // Operands of one steady-state step: V^T for PV(j-1) and K for S(j+1).
+  struct Ops {
+    bf16x8 v[2][2];
+    bf16x8 k[4];
+  };
+  auto load_ops = [&](const char* pv_base, int pv_h, const char* s_base, int s_h, Ops& o) {
+    const char* vb = pv_base + v_lane + 32 * pv_h * kVRow;
+    const char* kb = s_base + k_lane + 32 * s_h * kKRow;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const char* p = vb + 16 * tt * kVRow + 64 * db;
+        o.v[tt][db] = lds_read_vt(p, p + 8 * kVRow);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) o.k[ks] = lds_read_b128(kb, 32 * ks);
+  };
+
+  // Steady-state step: the operands `cur` (read during the previous step)
+  // feed PV(j-1) and S(j+1); the reads for the next step go out right after
+  // the first MFMA; the softmax of S(j) uses the current reference.  One
+  // basic block: 8 slots of one MFMA (PV and S alternating, so dependent
+  // MFMAs are two slots apart) and one vector-ALU chunk (two exponentials
+  // with their FMA, sum and bf16 packing).
+  auto step_fast = [&](const Ops& cur, Ops& nxt, const char* npv_base, int npv_h,
+                       const char* ns_base, int ns_h, f32x16& s_cur, bf16x8 (&p_cur)[2],
+                       f32x16& s_nxt, const bf16x8 (&p_prv)[2]) {
+    __builtin_amdgcn_sched_barrier(0);
+    const float m = m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int slot = 0; slot < 8; ++slot) {
+      if ((slot & 1) == 0) {
+        const int i = slot >> 1, tt = i >> 1, db = i & 1;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[tt][db], p_prv[tt], acc[db], 0, 0, 0);
+      } else {
+        const int ks = slot >> 1;
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.k[ks], qop[ks], ks == 0 ? zero16 : s_nxt, 0, 0, 0);
+      }
+      if (slot == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_ops(npv_base, npv_h, ns_base, ns_h, nxt);
+      }
+      const int r = 2 * slot;
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], c, -m));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r + 1], c, -m));
+      lsum += e0;
+      lsum += e1;
+      const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+      p_cur[r >> 3][r & 7] = pr[0];
+      p_cur[r >> 3][(r & 7) + 1] = pr[1];
+      // keep this slot's sum here: without it the adds sink to the end of the
+      // step and all sixteen probabilities stay live
+      asm volatile("" : "+v"(lsum));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // A partial row sum above 2^32 means a score far above the reference
+    // (or an overflow): remember it; the wave then recomputes its rows from
+    // scratch after the main loop.  No branch here, so the accumulators keep
+    // their registers through the steady state.
+    stale |= !(lsum <= kRedo);
+    l_run += lsum;
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  f32x16 sA, sB;
+  bf16x8 pA[2], pB[2];
+
+  // one tile t (half tiles 2t, 2t+1) on the general path
+  auto tile_general = [&](int t) {
+    step_general(2 * t, sA, pA, sB, pB);
+    if (2 * t + 1 < n_half) step_general(2 * t + 1, sB, pB, sA, pA);
+    if (t + 2 < n_tiles) store_tile((t + 2) & (kStages - 1));
+    __syncthreads();
+    if (t + 3 < n_tiles) load_tile(t + 3);
+  };
+  // one tile t whose stage is known at compile time, both steps fast.  Step
+  // 2t uses operands A and reads B for step 2t+1 (PV(2t) from this tile's
+  // first half, S(2t+2) from the next tile's first half); step 2t+1 reads A
+  // for step 2t+2 (PV(2t+1), S(2t+3): second halves).
+  Ops opA, opB;
+  auto tile_fast = [&](int t, auto stage_tag) {
+    constexpr int st = decltype(stage_tag)::value;
+    char* const b_cur = lds + st * kStageBytes;
+    char* const b_next = lds + ((st + 1) & 3) * kStageBytes;
+    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB);  // j = 2t
+    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA);  // j = 2t + 1
+    if (t + 2 < n_tiles) store_regs(lds + ((st + 2) & 3) * kStageBytes);
+    __syncthreads();
+    if (t + 3 < n_tiles) load_tile(t + 3);
+  };
+
+  // ---- prologue: tiles 0 and 1 into LDS, tile 2 in flight, S(0)
   load_tile(0);
   store_tile(0);
+  if (n_tiles > 1) {
+    load_tile(1);
+    store_tile(1);
+  }
   __syncthreads();
+  if (n_tiles > 2) load_tile(2);
+  if (last_h >= 0) compute_s(lds, 0, sA);
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < n_tiles) load_tile(kt + 1);
+  // ---- tiles: 0 on the general path, then the steady state (both half
+  // steps fast) unrolled over the 4 stages, then the rest on the general path
+  tile_general(0);
+  // tile t is steady when 2t+2 < n_half, 2t+2 <= last_h and neither 2t nor
+  // 2t+1 needs a mask; all three conditions only get stricter with t
+  int t_fast_end = 1;
+  {
+    int lim = min((n_half - 3) / 2, (last_h - 2) / 2);  // 2t+2 < n_half, 2t+2 <= last_h
+    if (last_h < 2) lim = 0;
+    int full = n / 32;                                   // halves with no ragged key
+    if (kCausal) full = min(full, q_wave / 32);          // halves before the diagonal
+    lim = min(lim, (full - 2) / 2);                      // 2t+1 < full
+    if (full < 2) lim = 0;
+    t_fast_end = max(1, lim + 1);
+  }
+  int t = 1;
+  // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
+  if (t + 3 < t_fast_end) load_ops(lds, 1, lds + kStageBytes, 1, opA);
+  for (; t + 3 < t_fast_end; t += 4) {
+    tile_fast(t, std::integral_constant<int, 1>());
+    tile_fast(t + 1, std::integral_constant<int, 2>());
+    tile_fast(t + 2, std::integral_constant<int, 3>());
+    tile_fast(t + 3, std::integral_constant<int, 0>());
+  }
+  for (; t < n_tiles; ++t) tile_general(t);
+  // the last half tile's PV
+  if (n_half - 1 <= last_h) {
+    if ((n_half - 1) & 1) compute_pv(stage_base(n_half - 1), 1, pB);
+    else compute_pv(stage_base(n_half - 1), 0, pA);
+  }
 
-    const int key0 = kt * kBc;
-    if (key0 <= wave_last_key) {
-      const char* kbase = lds + stage * kStageBytes;
-      const char* vbase = kbase + kTileBytes;
-
-      // ---- S^T = K Q^T : s[qb][kb] holds keys key0 + 32*kb + (8*(r/4) + 4*hi + r%4)
-      f32x16 s[kQBlocks][2];
+  // ---- rare fallback: this wave's steady state saw a score more than 2^32
+  // above its reference max.  Recompute its rows with an exact max on every
+  // half tile, reading K and V from global memory (other waves may still be
+  // using the LDS ring; this path takes no barrier).
+  if (__any(stale)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int qb = 0; qb < kQBlocks; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+    for (int j = 0; j <= last_h; ++j) {
+      f32x16 s;
+      {
+        const int key = 32 * j + l32;
+        bf16x8 kop[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kop = *(const bf16x8*)(kbase + kb * 32 * 128 + k_off[ks]);
-#pragma unroll
-          for (int qb = 0; qb < kQBlocks; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][ks], s[qb][kb], 0, 0, 0);
+          u32x4 w = {0u, 0u, 0u, 0u};
+          if (key < n) w = *(const u32x4*)(kg + (size_t)key * kD + 16 * ks + 8 * hi);
+          kop[ks] = __builtin_bit_cast(bf16x8, w);
         }
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[0], zero16, 0, 0, 0);
+#pragma unroll
+        for (int ks = 1; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
       }
-
-      // ---- masking (wave-uniform branch: only the ragged last tile and the
-      // causal diagonal tile pay for it).  Hidden scores become -inf; c > 0,
-      // so fma(-inf, c, -m) stays -inf and exp2 gives exactly 0.
-      const bool ragged = key0 + kBc > n;
-      const bool diag = kCausal && key0 + kBc - 1 > q_wave;
-      if (ragged || diag) {
+      if (needs_mask(j)) apply_mask(j, s);
+      bf16x8 pop[2];
+      bool raised;
+      const float alpha = softmax_exact(s, pop, raised);
+      if (raised) {
 #pragma unroll
-        for (int qb = 0; qb < kQBlocks; ++qb) {
-          const int qi = q_wave + qb * 32 + l32;
-          const int lim = kCausal ? min(qi, n - 1) : n - 1;  // last visible key
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-              s[qb][kb][r] = key <= lim ? s[qb][kb][r] : -INFINITY;
-            }
-        }
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       }
-
-      // ---- online softmax, per query block.  m_run is the reference the
-      // probabilities are taken against (log2 units, scale folded in).  It is
-      // raised only when some row's tile max exceeds it by more than kTau; any
-      // reference gives the same O and LSE, and this one keeps p <= 2^kTau
-      // while skipping the O rescale on almost every tile.
-      bf16x8 pop[kQBlocks][2][2];  // [qb][kb][t]: B operand of O^T += V^T P^T
 #pragma unroll
-      for (int qb = 0; qb < kQBlocks; ++qb) {
-        float mx = -INFINITY;
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < 2; ++db) {
+          // V^T operand: element i is V[key(i)][32*db + l32], key(i) as in P^T
+          bf16x8 vop;
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
-        mx = half_swap_max(mx) * c;
-        if (__any(mx > m_run[qb] + kTau)) {
-          const float m_new = fmaxf(m_run[qb], mx);
-          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          m_run[qb] = m_new;
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
-        }
-        const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            bf16x8 p8;
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-              const int r = 8 * tt + i;
-              const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c, -msub));
-              const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r + 1], c, -msub));
-              lsum += e0;
-              lsum += e1;
-              const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-              p8[i] = pr[0];
-              p8[i + 1] = pr[1];
-            }
-            pop[qb][kb][tt] = p8;
+          for (int i = 0; i < 8; ++i) {
+            const int key = 32 * j + 16 * tt + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const uint16_t bits = key < n ? vg[(size_t)key * kD + 32 * db + l32] : (uint16_t)0;
+            vop[i] = __builtin_bit_cast(__bf16, bits);
           }
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[tt], acc[db], 0, 0, 0);
         }
-        l_run[qb] += lsum;
-      }
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const int base = (32 * kb + 16 * tt) * 128;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(vbase + base + v_off[0][db]));
-            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(vbase + base + v_off[1][db]));
-            const i16x8 both = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, both);
-#pragma unroll
-            for (int qb = 0; qb < kQBlocks; ++qb)
-              acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[qb][kb][tt], acc[qb][db], 0, 0, 0);
-          }
-        }
-      }
     }
-
-    if (kt + 1 < n_tiles) store_tile(stage ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+  const float l_tot = half_swap_sum(l_run);
+  if (qi < n) {
+    const float inv = 1.f / l_tot;
+    uint16_t* orow = a.o + head + (size_t)qi * kD;
 #pragma unroll
-  for (int qb = 0; qb < kQBlocks; ++qb) {
-    const int qi = q_wave + qb * 32 + l32;
-    const float l_tot = half_swap_sum(l_run[qb]);
-    if (qi < n) {
-      const float inv = 1.f / l_tot;
-      uint16_t* orow = a.o + head + (size_t)qi * kD;
+    for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int f0 = 32 * db + 8 * r4 + 4 * hi;
-          const bf16x2 p01 = {(__bf16)(acc[qb][db][4 * r4 + 0] * inv), (__bf16)(acc[qb][db][4 * r4 + 1] * inv)};
-          const bf16x2 p23 = {(__bf16)(acc[qb][db][4 * r4 + 2] * inv), (__bf16)(acc[qb][db][4 * r4 + 3] * inv)};
-          u32x2 w = {__builtin_bit_cast(unsigned, p01), __builtin_bit_cast(unsigned, p23)};
-          *(u32x2*)(orow + f0) = w;
-        }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int f0 = 32 * db + 8 * r4 + 4 * hi;
+        const bf16x2 p01 = {(__bf16)(acc[db][4 * r4 + 0] * inv), (__bf16)(acc[db][4 * r4 + 1] * inv)};
+        const bf16x2 p23 = {(__bf16)(acc[db][4 * r4 + 2] * inv), (__bf16)(acc[db][4 * r4 + 3] * inv)};
+        u32x2 w = {__builtin_bit_cast(unsigned, p01), __builtin_bit_cast(unsigned, p23)};
+        *(u32x2*)(orow + f0) = w;
       }
-      if (hi == 0) a.lse[(size_t)bh * n + qi] = (m_run[qb] + __log2f(l_tot)) * kLn2;
     }
+    if (hi == 0) a.lse[(size_t)bh * n + qi] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 

@@ -247,6 +247,38 @@ def test_one_hot_limit():
     assert torch.equal(o[0, 0].cpu(), v[0, 0, 137].expand(n, 64))
 
 
+def _growth_inputs(n, growth, reverse=False, peak_last=False, seed=500):
+    """q_i = 16 e_0 for every row; k_j = (16 * j / n) e_0 * growth/256, so the
+    scaled score of key j (scale 1) rises linearly from 0 to `growth` natural
+    units across the keys (falls, when reversed).  Small random values in the
+    other features keep rows distinct."""
+    rng = np.random.default_rng(seed)
+    q = 0.01 * rng.standard_normal((1, 2, n, 64)).astype(np.float32)
+    k = 0.01 * rng.standard_normal((1, 2, n, 64)).astype(np.float32)
+    v = rng.standard_normal((1, 2, n, 64)).astype(np.float32)
+    q[..., 0] = 16.0
+    ramp = np.arange(n, dtype=np.float32) / n * (growth / 16.0)
+    k[..., 0] = ramp[::-1] if reverse else ramp
+    if peak_last:
+        k[..., n - 1, 0] = growth / 16.0 + 4.0
+    return tuple(torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("growth, reverse, peak_last", [
+    (12.0, False, False),    # the max rises ~17 log2 units: steady state keeps p <= 2^17
+    (200.0, False, False),   # rises ~290 log2 units: the per-wave exact fallback
+    (200.0, True, False),    # max in the first tile, falling scores
+    (40.0, False, True),     # max in the ragged last tile
+])
+def test_score_growth_paths(growth, reverse, peak_last, causal):
+    n = 2000  # 63 half tiles, ragged end, long steady state
+    q, k, v = _growth_inputs(n, growth, reverse, peak_last)
+    w = Workload("growth", 1, 2, n, 64, "bf16", 1.0, 1.0, causal, 0, "")
+    o, lse = gpu_run(q, k, v, 1.0, causal)
+    compare(w, q, k, v, o, lse, what=f"growth={growth} reverse={reverse} peak_last={peak_last}")
+
+
 def test_deterministic_repeat():
     w = WORKLOADS["bert_large"]
     q, k, v = (t.to(DEV) for t in make_inputs(w))
