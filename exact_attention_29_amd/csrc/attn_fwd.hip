@@ -14,9 +14,11 @@
 // bf16 kernel.  One workgroup = 8 waves = 256 query rows of one head, one
 // workgroup per CU (two waves per SIMD):
 //   * each wave owns 32 query rows; their Q^T operands stay in VGPRs;
-//   * K and V tiles of 64 keys go through a 4-stage LDS ring, rows padded to
-//     144 B (K) and 192 B (V) so both read patterns below are bank-conflict
-//     free and every LDS address is a per-lane constant plus an immediate;
+//   * K and V tiles of 64 keys go through a 5-stage LDS ring, filled by
+//     global_load_lds_dwordx4 DMA three tiles ahead (no staging registers);
+//     16-byte chunks are XOR-swizzled per row so both read patterns below
+//     are bank-conflict free, and every LDS address is a per-lane constant
+//     plus an immediate (the steady state is unrolled over the stages);
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: lane l then holds 16 keys of
 //     ONE query (l % 32), so row reductions stay in the lane plus one
 //     exchange with lane l ^ 32;
@@ -66,13 +68,13 @@ constexpr int kBc = 64;                      // keys per K/V tile (two half tile
 constexpr int kWaves = 8;                    // waves per workgroup (2 per SIMD)
 constexpr int kBr = kWaves * 32;             // 256 queries per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kKRow = 144;                   // bytes per K row in LDS (128 + 16 pad)
-constexpr int kVRow = 192;                   // bytes per V row in LDS (128 + 64 pad)
-constexpr int kKTile = kBc * kKRow;          // 9216
-constexpr int kVTile = kBc * kVRow;          // 12288
-constexpr int kStageBytes = kKTile + kVTile; // 21504
-constexpr int kStages = 4;                   // LDS ring of K/V tiles
-constexpr int kLdsBytes = kStages * kStageBytes;  // 86016: one workgroup per CU
+constexpr int kRow = 128;                    // bytes per K or V row (64 bf16)
+constexpr int kTileBytes = kBc * kRow;       // 8192
+constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile: 16384
+constexpr int kStages = 5;                   // LDS ring of K/V tiles
+constexpr int kLead = 3;                     // tile t+kLead+1 is requested after tile t
+constexpr int kLdsBytes = kStages * kStageBytes;  // 81920: one workgroup per CU
+static_assert(kLdsBytes <= 160 * 1024, "LDS ring exceeds the 160 KiB of a gfx950 CU");
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -116,6 +118,15 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
 }
 
+// 16-byte chunk c of tile row r lives at chunk position c ^ swz(r) of that
+// row: the K reads (16 rows, one chunk) and the V^T transpose reads (4 rows,
+// 4 chunks per half wave) then hit 64 distinct banks.
+__device__ __forceinline__ int swz(int row) {
+  const int x = (row >> 1) & 7;
+  return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+}
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * kRow + ((chunk ^ swz(row)) << 4); }
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
   return *(const bf16x8*)(base + off);
 }
@@ -130,7 +141,17 @@ template <bool kCausal>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(Bf16Args a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+  // One LDS object per ring stage: with the stage known at compile time (the
+  // steady state), the compiler can tell a stage being filled by DMA from the
+  // stages being read and does not wait for the DMA before those reads.
+  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds4[kStageBytes];
+  auto stage_ptr = [&](int st) -> char* {
+    return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 : lds4;
+  };
 
   const int n = a.n;
   const int logical = xcd_remap(blockIdx.x, a.total_tiles);
@@ -172,42 +193,54 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 
   // ---- global -> LDS staging: thread tid moves 16-byte chunk tid of the K
   // tile and of the V tile (row tid / 8, chunk tid % 8).
-  constexpr int kChunks = 512 / kThreads;  // 16-byte chunks per thread per tile
-  const int st_row = tid >> 3, st_ch = tid & 7;  // chunk j adds kThreads/8 rows
-  const int st_koff = st_row * kKRow + st_ch * 16;
-  const int st_voff = kKTile + st_row * kVRow + st_ch * 16;
-  u32x4 kreg[kChunks], vreg[kChunks];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int jc = 0; jc < kChunks; ++jc) {
-      const int key = kt * kBc + st_row + jc * (kThreads / 8);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[jc] = z;
-      vreg[jc] = z;
-      if (key < n) {
-        kreg[jc] = *(const u32x4*)(kg + (size_t)key * kD + st_ch * 8);
-        vreg[jc] = *(const u32x4*)(vg + (size_t)key * kD + st_ch * 8);
-      }
-    }
+  // ---- global -> LDS staging by DMA (global_load_lds_dwordx4): lane l of
+  // wave w fills LDS chunk slot (row 8*w + l/8, position l%8) of the K tile
+  // and of the V tile, so it fetches global chunk (l%8) ^ swz(row) of that
+  // row.  Rows past N read row N-1 instead (finite data; those keys are
+  // masked and their probabilities are exactly 0).
+  const int dma_row = 8 * wave + (lane >> 3);
+  const int dma_chunk = (lane & 7) ^ swz(dma_row);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  auto dma_tile = [&](int kt, char* stage_base) {
+    const int key = min(kt * kBc + dma_row, n - 1);
+    const uint16_t* ks = kg + (size_t)key * kD + dma_chunk * 8;
+    const uint16_t* vs = vg + (size_t)key * kD + dma_chunk * 8;
+    char* kd = stage_base + wave_s * 1024;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ks,
+                                     (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vs,
+                                     (__attribute__((address_space(3))) void*)(kd + kTileBytes), 16, 0, 0);
   };
-  auto store_regs = [&](char* base) {
-#pragma unroll
-    for (int jc = 0; jc < kChunks; ++jc) {
-      *(u32x4*)(base + st_koff + jc * (kThreads / 8) * kKRow) = kreg[jc];
-      *(u32x4*)(base + st_voff + jc * (kThreads / 8) * kVRow) = vreg[jc];
-    }
+  // End of tile t: the barrier publishes tile t+2, whose two DMAs (issued
+  // two tiles earlier) must be done; the two of tile t+3, if issued, may
+  // still fly.  A plain s_barrier: __syncthreads() would also wait for those.
+  // Every LDS read of the stage the next DMA overwrites has already fed an
+  // MFMA, so the barrier needs no LDS wait.  The memory clobber keeps the
+  // compiler from moving memory operations across it.
+  auto dma_barrier = [&](bool newer_in_flight) {
+    if (newer_in_flight) asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  auto store_tile = [&](int stage) { store_regs(lds + stage * kStageBytes); };
 
-  // ---- per-lane LDS read offsets within a stage
-  // K operand (A of S^T), half h, step ks: row 32*h + l32, features 16*ks + 8*hi.
-  const int k_lane = l32 * kKRow + hi * 16;  // + 32*h*kKRow + 32*ks
-  // V^T operand via ds_read_b64_tr_b16 (half h, step tt, feature block db):
-  // in each 16-lane group g, lane j points at row 32*h + 16*tt + 4*hi + (j>>2)
-  // (+8 for the second half of the operand) and feature 32*db + 16*(g&1) + 4*(j&3).
+  // ---- per-lane LDS read offsets within a stage (swizzle constant per lane;
+  // half tile h adds 32 rows, PV step tt 16 rows: neither changes swz)
+  // K operand (A of S^T), step ks: row l32 (+32h), chunk 2*ks + hi.
+  int k_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) k_off[ks] = tile_off(l32, 2 * ks + hi);
+  // V^T operand via ds_read_b64_tr_b16: in each 16-lane group g, lane j
+  // points at row 16*tt + 4*hi + (j>>2) (+8 for the second half of the
+  // operand) and feature 32*db + 16*(g&1) + 4*(j&3).
   const int g = lane >> 4, j16 = lane & 15;
-  const int v_lane = kKTile + (4 * hi + (j16 >> 2)) * kVRow + 2 * (16 * (g & 1) + 4 * (j16 & 3));
-  // + (32*h + 16*tt + 8*sec) * kVRow + 64*db
+  int v_off[2][2];  // [sec][db]
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int row = 4 * hi + (j16 >> 2) + 8 * sec;
+      const int byte = 2 * (32 * db + 16 * (g & 1) + 4 * (j16 & 3));
+      v_off[sec][db] = kTileBytes + row * kRow + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
+    }
 
   const float c = a.c;
   f32x16 acc[2];  // O^T, feature blocks db = 0, 1
@@ -224,24 +257,24 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   //
   // S^T = K Q^T: s holds keys 32*j + 8*(r/4) + 4*hi + r%4 of query qi.
   auto compute_s = [&](const char* stage_base, int h, f32x16& s) {
-    const char* kb = stage_base + k_lane + 32 * h * kKRow;
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kb, 0), qop[0], zero16, 0, 0, 0);
+    const char* kb = stage_base + 32 * h * kRow;
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kb, k_off[0]), qop[0], zero16, 0, 0, 0);
 #pragma unroll
     for (int ks = 1; ks < 4; ++ks)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kb, 32 * ks), qop[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kb, k_off[ks]), qop[ks], s, 0, 0, 0);
   };
   // O^T += V^T P^T over one half tile; pop[tt] covers its keys 16*tt .. +15.
   auto compute_pv = [&](const char* stage_base, int h, const bf16x8 (&pop)[2]) {
-    const char* vb = stage_base + v_lane + 32 * h * kVRow;
+    const char* vb = stage_base + 32 * h * kRow;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const char* p = vb + 16 * tt * kVRow + 64 * db;
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_vt(p, p + 8 * kVRow), pop[tt], acc[db], 0, 0, 0);
+        const char* p = vb + 16 * tt * kRow;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_vt(p + v_off[0][db], p + v_off[1][db]), pop[tt], acc[db], 0, 0, 0);
       }
   };
-  auto stage_base = [&](int j) { return lds + ((j >> 1) & (kStages - 1)) * kStageBytes; };
+  auto stage_base = [&](int j) { return stage_ptr((j >> 1) % kStages); };
 
   // Hidden keys of half tile j become -inf (ragged end, causal diagonal).
   auto needs_mask = [&](int j) { return 32 * j + 32 > n || (kCausal && 32 * j + 31 > q_wave); };
@@ -321,17 +354,17 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     bf16x8 k[4];
   };
   auto load_ops = [&](const char* pv_base, int pv_h, const char* s_base, int s_h, Ops& o) {
-    const char* vb = pv_base + v_lane + 32 * pv_h * kVRow;
-    const char* kb = s_base + k_lane + 32 * s_h * kKRow;
+    const char* vb = pv_base + 32 * pv_h * kRow;
+    const char* kb = s_base + 32 * s_h * kRow;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const char* p = vb + 16 * tt * kVRow + 64 * db;
-        o.v[tt][db] = lds_read_vt(p, p + 8 * kVRow);
+        const char* p = vb + 16 * tt * kRow;
+        o.v[tt][db] = lds_read_vt(p + v_off[0][db], p + v_off[1][db]);
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.k[ks] = lds_read_b128(kb, 32 * ks);
+    for (int ks = 0; ks < 4; ++ks) o.k[ks] = lds_read_b128(kb, k_off[ks]);
   };
 
   // Steady-state step: the operands `cur` (read during the previous step)
@@ -348,7 +381,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     float lsum = 0.f;
 #pragma unroll
     for (int slot = 0; slot < 8; ++slot) {
-      if ((slot & 1) == 0) {
+      if ((slot & 1) == 1) {
         const int i = slot >> 1, tt = i >> 1, db = i & 1;
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[tt][db], p_prv[tt], acc[db], 0, 0, 0);
       } else {
@@ -388,9 +421,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   auto tile_general = [&](int t) {
     step_general(2 * t, sA, pA, sB, pB);
     if (2 * t + 1 < n_half) step_general(2 * t + 1, sB, pB, sA, pA);
-    if (t + 2 < n_tiles) store_tile((t + 2) & (kStages - 1));
-    __syncthreads();
-    if (t + 3 < n_tiles) load_tile(t + 3);
+    dma_barrier(t + kLead < n_tiles);
+    if (t + 1 + kLead < n_tiles) dma_tile(t + 1 + kLead, stage_ptr((t + 1 + kLead) % kStages));
   };
   // one tile t whose stage is known at compile time, both steps fast.  Step
   // 2t uses operands A and reads B for step 2t+1 (PV(2t) from this tile's
@@ -399,25 +431,23 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   Ops opA, opB;
   auto tile_fast = [&](int t, auto stage_tag) {
     constexpr int st = decltype(stage_tag)::value;
-    char* const b_cur = lds + st * kStageBytes;
-    char* const b_next = lds + ((st + 1) & 3) * kStageBytes;
+    char* const b_cur = stage_ptr(st);
+    char* const b_next = stage_ptr((st + 1) % kStages);
     step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB);  // j = 2t
     step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA);  // j = 2t + 1
-    if (t + 2 < n_tiles) store_regs(lds + ((st + 2) & 3) * kStageBytes);
-    __syncthreads();
-    if (t + 3 < n_tiles) load_tile(t + 3);
+    dma_barrier(t + kLead < n_tiles);
+    if (t + 1 + kLead < n_tiles) dma_tile(t + 1 + kLead, stage_ptr((st + 1 + kLead) % kStages));
   };
 
   // ---- prologue: tiles 0 and 1 into LDS, tile 2 in flight, S(0)
-  load_tile(0);
-  store_tile(0);
-  if (n_tiles > 1) {
-    load_tile(1);
-    store_tile(1);
-  }
-  __syncthreads();
-  if (n_tiles > 2) load_tile(2);
-  if (last_h >= 0) compute_s(lds, 0, sA);
+  // tiles 0 .. kLead in flight; tiles 0 and 1 must land before the first
+  // barrier (tile t+kLead is issued right after the barrier ending tile t-1)
+#pragma unroll
+  for (int tl = 0; tl <= kLead; ++tl)
+    if (tl < n_tiles) dma_tile(tl, stage_ptr(tl));
+  if (n_tiles > kLead) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (last_h >= 0) compute_s(lds0, 0, sA);
 
   // ---- tiles: 0 on the general path, then the steady state (both half
   // steps fast) unrolled over the 4 stages, then the rest on the general path
@@ -436,12 +466,13 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   }
   int t = 1;
   // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
-  if (t + 3 < t_fast_end) load_ops(lds, 1, lds + kStageBytes, 1, opA);
-  for (; t + 3 < t_fast_end; t += 4) {
+  if (t + 4 < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
+  for (; t + 4 < t_fast_end; t += 5) {
     tile_fast(t, std::integral_constant<int, 1>());
     tile_fast(t + 1, std::integral_constant<int, 2>());
     tile_fast(t + 2, std::integral_constant<int, 3>());
-    tile_fast(t + 3, std::integral_constant<int, 0>());
+    tile_fast(t + 3, std::integral_constant<int, 4>());
+    tile_fast(t + 4, std::integral_constant<int, 0>());
   }
   for (; t < n_tiles; ++t) tile_general(t);
   // the last half tile's PV
@@ -669,7 +700,7 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
   void* args[] = {&a};
   const void* fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true>)
                           : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false>);
-  const hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles), dim3(kThreads), args, kLdsBytes,
+  const hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles), dim3(kThreads), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
