@@ -194,8 +194,10 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU clock ramps for ~60 launches (~35 ms) from idle; 100 untimed
+    # warmup steps put the timed steps in steady state.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="patch_3mp")
     ap.add_argument("--n", type=int, default=None, help="override the sequence length")
     ap.add_argument("--causal", choices=["yes", "no"], default=None)
@@ -240,8 +242,9 @@ def main():
         with open(args.sweep, "w") as f:
             for w in cases:
                 steps = max(args.steps, 200) if w.flops < 2e10 else args.steps
+                warm = max(args.warmup, 1000) if w.flops < 2e10 else args.warmup
                 log(f"[bench] {w.name} {w.shape} causal={w.causal}")
-                line = bench_one(w, steps, args.warmup, False, 0)
+                line = bench_one(w, steps, warm, False, 0)
                 f.write(json.dumps(line) + "\n")
                 f.flush()
                 log(f"[bench] {w.name}: {line['value']} TFLOP/s, kernel {line['roofline']['kernel_ms']} ms")
