@@ -71,16 +71,29 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRow = 128;                    // bytes per K or V row (64 bf16)
 constexpr int kTileBytes = kBc * kRow;       // 8192
 constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile: 16384
-constexpr int kStages = 5;                   // LDS ring of K/V tiles
-constexpr int kLead = 3;                     // tile t+kLead+1 is requested after tile t
-constexpr int kLdsBytes = kStages * kStageBytes;  // 81920: one workgroup per CU
+// Prefetch distance: after the barrier that ends tile t, tile t+kLead+1 is
+// requested.  The ring then needs kLead+2 stages: tile t-1 is still read
+// during tile t (its PV), and tile t+1 is being published.
+#ifndef ATTN_LEAD
+#define ATTN_LEAD 3
+#endif
+#define ATTN_STAGES (ATTN_LEAD + 2)
+constexpr int kLead = ATTN_LEAD;
+constexpr int kStages = ATTN_STAGES;         // LDS ring of K/V tiles
+constexpr int kLdsBytes = kStages * kStageBytes;  // one workgroup per CU
+static_assert(kLead >= 2 && kStages <= 8, "prefetch distance out of range");
 static_assert(kLdsBytes <= 160 * 1024, "LDS ring exceeds the 160 KiB of a gfx950 CU");
+
+// Fourth word of a gfx950 buffer resource: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kTau = 8.0f;                 // slack when the reference max is set
-constexpr float kRedo = 4294967296.0f;       // 2^32: a partial row sum above this
-                                             // means the reference max is stale
+constexpr unsigned kRedoBits = 0x4f800000u;  // bit pattern of 2^32: a partial
+                                             // row sum above it means the
+                                             // reference max is stale
+constexpr unsigned kInfBits = 0x7f800000u;   // bit pattern of +inf
 
 struct Bf16Args {
   const uint16_t* q;
@@ -93,6 +106,39 @@ struct Bf16Args {
   int total_tiles;  // B * H * q_tiles
   float c;          // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign;  // 0x80008000 when scale < 0 (Q negated), else 0
+};
+
+// s_waitcnt vmcnt(N) followed by s_barrier.  A plain s_barrier: the
+// compiler's __syncthreads() would also wait for every newer DMA.  The memory
+// clobber keeps the compiler from moving memory operations across it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// Calls vm_wait_barrier<2 * c>() for a wave-uniform c in [0, kMax].
+template <int kMax>
+__device__ __forceinline__ void vm_wait_barrier_tiles(int c) {
+  if constexpr (kMax > 0) {
+    if (c >= kMax) {
+      vm_wait_barrier<2 * kMax>();
+      return;
+    }
+    vm_wait_barrier_tiles<kMax - 1>(c);
+  } else {
+    vm_wait_barrier<0>();
+  }
+}
+
+// Calls f(std::integral_constant<int, I>()) for I = kFirst .. kEnd-1.
+template <int kFirst, int kEnd>
+struct Unroll {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    if constexpr (kFirst < kEnd) {
+      f(std::integral_constant<int, kFirst>());
+      Unroll<kFirst + 1, kEnd>::run(f);
+    }
+  }
 };
 
 // max(x[lane], x[lane ^ 32]) in every lane, via v_permlane32_swap (which
@@ -149,8 +195,27 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds4[kStageBytes];
+#if ATTN_STAGES > 5
+  __shared__ __attribute__((aligned(1024))) char lds5[kStageBytes];
+#endif
+#if ATTN_STAGES > 6
+  __shared__ __attribute__((aligned(1024))) char lds6[kStageBytes];
+#endif
+#if ATTN_STAGES > 7
+  __shared__ __attribute__((aligned(1024))) char lds7[kStageBytes];
+#endif
   auto stage_ptr = [&](int st) -> char* {
-    return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 : lds4;
+    char* p = st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 : lds4;
+#if ATTN_STAGES > 5
+    p = st == 5 ? lds5 : p;
+#endif
+#if ATTN_STAGES > 6
+    p = st == 6 ? lds6 : p;
+#endif
+#if ATTN_STAGES > 7
+    p = st == 7 ? lds7 : p;
+#endif
+    return p;
   };
 
   const int n = a.n;
@@ -191,36 +256,53 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const int wave_last_key = q_wave >= n ? -1 : (kCausal ? min(n - 1, q_wave + 31) : n - 1);
   const int last_h = wave_last_key < 0 ? -1 : wave_last_key / 32;
 
-  // ---- global -> LDS staging: thread tid moves 16-byte chunk tid of the K
-  // tile and of the V tile (row tid / 8, chunk tid % 8).
-  // ---- global -> LDS staging by DMA (global_load_lds_dwordx4): lane l of
-  // wave w fills LDS chunk slot (row 8*w + l/8, position l%8) of the K tile
-  // and of the V tile, so it fetches global chunk (l%8) ^ swz(row) of that
-  // row.  Rows past N read row N-1 instead (finite data; those keys are
-  // masked and their probabilities are exactly 0).
+  // ---- global -> LDS staging by DMA (buffer/global loads with the LDS
+  // bit, 16 bytes per lane): lane l of wave w fills LDS chunk slot (row
+  // 8*w + l/8, position l%8) of the K tile and of the V tile, so it fetches
+  // global chunk (l%8) ^ swz(row) of that row.  In the ragged last tile, rows
+  // past N read row N-1 instead (finite data; those keys are masked and their
+  // probabilities are exactly 0).
   const int dma_row = 8 * wave + (lane >> 3);
   const int dma_chunk = (lane & 7) ^ swz(dma_row);
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const unsigned dma_lane_off = (unsigned)(dma_row * kRow + dma_chunk * 16);
+  // Buffer resources over this head's K and V: a whole tile is fetched with
+  // the tile's byte offset in a scalar register and this lane's constant
+  // offset, so the steady state spends no vector instruction on addresses.
+  const int head_bytes = (int)((unsigned)n * (unsigned)kRow);
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_bytes, kBufferWord3);
   auto dma_tile = [&](int kt, char* stage_base) {
-    const int key = min(kt * kBc + dma_row, n - 1);
-    const uint16_t* ks = kg + (size_t)key * kD + dma_chunk * 8;
-    const uint16_t* vs = vg + (size_t)key * kD + dma_chunk * 8;
     char* kd = stage_base + wave_s * 1024;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ks,
-                                     (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vs,
-                                     (__attribute__((address_space(3))) void*)(kd + kTileBytes), 16, 0, 0);
+    if ((kt + 1) * kBc <= n) {
+      const int tile = kt * kTileBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void*)kd, 16,
+                                               (int)dma_lane_off, tile, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (__attribute__((address_space(3))) void*)(kd + kTileBytes),
+                                               16, (int)dma_lane_off, tile, 0, 0);
+    } else {
+      // ragged last tile: rows past N re-read row N-1
+      const int key = min(kt * kBc + dma_row, n - 1);
+      const uint16_t* ks = kg + (size_t)key * kD + dma_chunk * 8;
+      const uint16_t* vs = vg + (size_t)key * kD + dma_chunk * 8;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ks,
+                                       (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vs,
+                                       (__attribute__((address_space(3))) void*)(kd + kTileBytes), 16, 0, 0);
+    }
   };
-  // End of tile t: the barrier publishes tile t+2, whose two DMAs (issued
-  // two tiles earlier) must be done; the two of tile t+3, if issued, may
-  // still fly.  A plain s_barrier: __syncthreads() would also wait for those.
-  // Every LDS read of the stage the next DMA overwrites has already fed an
-  // MFMA, so the barrier needs no LDS wait.  The memory clobber keeps the
-  // compiler from moving memory operations across it.
-  auto dma_barrier = [&](bool newer_in_flight) {
-    if (newer_in_flight) asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+
+  // End of tile t: the barrier publishes tile t+2, whose DMAs must be done;
+  // those of tiles t+3 .. t+kLead (the ones that exist) may still fly.  Every
+  // LDS read of the stage the next DMA overwrites has already fed an MFMA, so
+  // the barrier needs no LDS wait.
+  auto dma_barrier = [&](int t) {
+    vm_wait_barrier_tiles<kLead - 2>(min(kLead - 2, max(0, n_tiles - 3 - t)));
   };
+
 
   // ---- per-lane LDS read offsets within a stage (swizzle constant per lane;
   // half tile h adds 32 rows, PV step tt 16 rows: neither changes swz)
@@ -249,7 +331,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  bool stale = false;  // set when the steady state saw a stale reference max
+  float l_part_max = 0.f;  // largest partial row sum of a steady-state step
   const f32x16 zero16 = {};
 
   // ---- the three pieces of work on one half tile (32 keys).  Half tile j
@@ -397,19 +479,23 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r + 1], c, -m));
       lsum += e0;
       lsum += e1;
+      // the packed pair goes into its 32-bit word of the P operand; the empty
+      // asm statements keep the conversion and this slot's sum here (without
+      // them they sink to the end of the step, past the MFMAs they should
+      // overlap, and all sixteen probabilities stay live)
       const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-      p_cur[r >> 3][r & 7] = pr[0];
-      p_cur[r >> 3][(r & 7) + 1] = pr[1];
-      // keep this slot's sum here: without it the adds sink to the end of the
-      // step and all sixteen probabilities stay live
+      unsigned pw = __builtin_bit_cast(unsigned, pr);
+      asm volatile("" : "+v"(pw));
+      u32x4 words = __builtin_bit_cast(u32x4, p_cur[r >> 3]);
+      words[(r & 7) >> 1] = pw;
+      p_cur[r >> 3] = __builtin_bit_cast(bf16x8, words);
       asm volatile("" : "+v"(lsum));
       __builtin_amdgcn_sched_barrier(0);
     }
-    // A partial row sum above 2^32 means a score far above the reference
-    // (or an overflow): remember it; the wave then recomputes its rows from
-    // scratch after the main loop.  No branch here, so the accumulators keep
-    // their registers through the steady state.
-    stale |= !(lsum <= kRedo);
+    // Track the largest partial sum (checked once, after the loop): a plain
+    // max keeps the step free of compares into scalar registers.  A partial
+    // sum is never NaN (a sum of exp2 results, +inf at worst).
+    l_part_max = fmaxf(l_part_max, lsum);
     l_run += lsum;
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -421,7 +507,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   auto tile_general = [&](int t) {
     step_general(2 * t, sA, pA, sB, pB);
     if (2 * t + 1 < n_half) step_general(2 * t + 1, sB, pB, sA, pA);
-    dma_barrier(t + kLead < n_tiles);
+    dma_barrier(t);
     if (t + 1 + kLead < n_tiles) dma_tile(t + 1 + kLead, stage_ptr((t + 1 + kLead) % kStages));
   };
   // one tile t whose stage is known at compile time, both steps fast.  Step
@@ -435,7 +521,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     char* const b_next = stage_ptr((st + 1) % kStages);
     step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB);  // j = 2t
     step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA);  // j = 2t + 1
-    dma_barrier(t + kLead < n_tiles);
+    dma_barrier(t);
     if (t + 1 + kLead < n_tiles) dma_tile(t + 1 + kLead, stage_ptr((st + 1 + kLead) % kStages));
   };
 
@@ -445,12 +531,14 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
   for (int tl = 0; tl <= kLead; ++tl)
     if (tl < n_tiles) dma_tile(tl, stage_ptr(tl));
-  if (n_tiles > kLead) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  // tiles 0 and 1 must have landed; the rest of the min(n_tiles, kLead+1)
+  // issued may still fly
+  vm_wait_barrier_tiles<kLead - 1>(max(0, min(n_tiles, kLead + 1) - 2));
   if (last_h >= 0) compute_s(lds0, 0, sA);
 
   // ---- tiles: 0 on the general path, then the steady state (both half
-  // steps fast) unrolled over the 4 stages, then the rest on the general path
+  // steps fast) unrolled over the ring's stages, then the rest on the general
+  // path
   tile_general(0);
   // tile t is steady when 2t+2 < n_half, 2t+2 <= last_h and neither 2t nor
   // 2t+1 needs a mask; all three conditions only get stricter with t
@@ -466,13 +554,13 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   }
   int t = 1;
   // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
-  if (t + 4 < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
-  for (; t + 4 < t_fast_end; t += 5) {
-    tile_fast(t, std::integral_constant<int, 1>());
-    tile_fast(t + 1, std::integral_constant<int, 2>());
-    tile_fast(t + 2, std::integral_constant<int, 3>());
-    tile_fast(t + 3, std::integral_constant<int, 4>());
-    tile_fast(t + 4, std::integral_constant<int, 0>());
+  if (t + kStages - 1 < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
+  for (; t + kStages - 1 < t_fast_end; t += kStages) {
+    // tiles t .. t+kStages-1 sit in stages 1, 2, .., kStages-1, 0
+    Unroll<0, kStages>::run([&](auto i) {
+      constexpr int I = decltype(i)::value;
+      tile_fast(t + I, std::integral_constant<int, (I + 1) % kStages>());
+    });
   }
   for (; t < n_tiles; ++t) tile_general(t);
   // the last half tile's PV
@@ -481,10 +569,16 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     else compute_pv(stage_base(n_half - 1), 0, pA);
   }
 
-  // ---- rare fallback: this wave's steady state saw a score more than 2^32
-  // above its reference max.  Recompute its rows with an exact max on every
-  // half tile, reading K and V from global memory (other waves may still be
-  // using the LDS ring; this path takes no barrier).
+  // ---- rare fallback: some steady-state step of this wave had a partial
+  // row sum above 2^32, i.e. a score far above the reference max (or an
+  // overflow to inf; a later rescale by 0 would then turn the row sum into
+  // NaN).  The test compares bit patterns: both values are non-negative or
+  // NaN, and an integer compare cannot be folded away by the compiler's
+  // no-NaN assumption.  Such a wave recomputes its rows with an exact max on
+  // every half tile, reading K and V from global memory (other waves may
+  // still be using the LDS ring; this path takes no barrier).
+  const bool stale = __builtin_bit_cast(unsigned, l_part_max) > kRedoBits ||
+                     (__builtin_bit_cast(unsigned, l_run) & 0x7fffffffu) >= kInfBits;
   if (__any(stale)) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
