@@ -178,7 +178,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds):
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_fwd_bf16_kernel<%s>" % ("true" if w.causal else "false"),
+            "kernel": "attn_fwd_bf16_kernel<%s>" % ("true, 4" if w.causal else "false, 8"),
             "kernel_ms": round(kern * 1e3, 4),
             "algorithmic_bytes": 4 * B * H * N * d * 2 + 4 * B * H * N,
         },

@@ -12,7 +12,8 @@
 // GPU's shared memory; the tiles below are sized for gfx950 instead.
 //
 // bf16 kernel.  One workgroup = 8 waves = 256 query rows of one head, one
-// workgroup per CU (two waves per SIMD):
+// workgroup per CU, two waves per SIMD (causal: 4 waves = 128 rows, two
+// workgroups per CU, for a better balanced triangle):
 //   * each wave owns 32 query rows; their Q^T operands stay in VGPRs;
 //   * K and V tiles of 64 keys go through a 5-stage LDS ring, filled by
 //     global_load_lds_dwordx4 DMA three tiles ahead (no staging registers);
@@ -65,9 +66,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kD = 64;                       // head size
 constexpr int kBc = 64;                      // keys per K/V tile (two half tiles)
-constexpr int kWaves = 8;                    // waves per workgroup (2 per SIMD)
-constexpr int kBr = kWaves * 32;             // 256 queries per workgroup
-constexpr int kThreads = kWaves * 64;
+// Waves per workgroup (each owns 32 query rows): 8 (256 rows, one workgroup
+// per CU) without a mask, 4 (128 rows, two workgroups per CU) when causal,
+// where shorter rows per workgroup balance the triangle better.
+constexpr int kWavesFull = 8;
+constexpr int kWavesCausal = 4;
 constexpr int kRow = 128;                    // bytes per K or V row (64 bf16)
 constexpr int kTileBytes = kBc * kRow;       // 8192
 constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile: 16384
@@ -80,7 +83,8 @@ constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile: 16384
 #define ATTN_STAGES (ATTN_LEAD + 2)
 constexpr int kLead = ATTN_LEAD;
 constexpr int kStages = ATTN_STAGES;         // LDS ring of K/V tiles
-constexpr int kLdsBytes = kStages * kStageBytes;  // one workgroup per CU
+constexpr int kLdsBytes = kStages * kStageBytes;  // 80 KiB at the default lead:
+                                                  // two 4-wave workgroups fit a CU
 static_assert(kLead >= 2 && kStages <= 8, "prefetch distance out of range");
 static_assert(kLdsBytes <= 160 * 1024, "LDS ring exceeds the 160 KiB of a gfx950 CU");
 
@@ -102,7 +106,7 @@ struct Bf16Args {
   uint16_t* o;
   float* lse;
   int n;            // sequence length
-  int q_tiles;      // ceil(n / kBr)
+  int q_tiles;      // ceil(n / rows per workgroup)
   int total_tiles;  // B * H * q_tiles
   float c;          // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign;  // 0x80008000 when scale < 0 (Q negated), else 0
@@ -115,15 +119,16 @@ template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-// Calls vm_wait_barrier<2 * c>() for a wave-uniform c in [0, kMax].
-template <int kMax>
+// Calls vm_wait_barrier<kPer * c>() for a wave-uniform c in [0, kMax]: c
+// tiles of kPer DMAs each may stay in flight.
+template <int kPer, int kMax>
 __device__ __forceinline__ void vm_wait_barrier_tiles(int c) {
   if constexpr (kMax > 0) {
     if (c >= kMax) {
-      vm_wait_barrier<2 * kMax>();
+      vm_wait_barrier<kPer * kMax>();
       return;
     }
-    vm_wait_barrier_tiles<kMax - 1>(c);
+    vm_wait_barrier_tiles<kPer, kMax - 1>(c);
   } else {
     vm_wait_barrier<0>();
   }
@@ -183,10 +188,14 @@ __device__ __forceinline__ bf16x8 lds_read_vt(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <bool kCausal>
-__global__ void __launch_bounds__(kThreads)
+template <bool kCausal, int kWaves>
+__global__ void __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(Bf16Args a) {
+  constexpr int kBr = kWaves * 32;        // query rows per workgroup
+  constexpr int kDmaPasses = 8 / kWaves;  // a DMA instruction covers 8 rows per wave
+  constexpr int kDmaPerTile = 2 * kDmaPasses;
+  static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
   // One LDS object per ring stage: with the stage known at compile time (the
   // steady state), the compiler can tell a stage being filled by DMA from the
   // stages being read and does not wait for the DMA before those reads.
@@ -257,11 +266,15 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const int last_h = wave_last_key < 0 ? -1 : wave_last_key / 32;
 
   // ---- global -> LDS staging by DMA (buffer/global loads with the LDS
-  // bit, 16 bytes per lane): lane l of wave w fills LDS chunk slot (row
-  // 8*w + l/8, position l%8) of the K tile and of the V tile, so it fetches
-  // global chunk (l%8) ^ swz(row) of that row.  In the ragged last tile, rows
-  // past N read row N-1 instead (finite data; those keys are masked and their
-  // probabilities are exactly 0).
+  // bit, 16 bytes per lane): in pass p, lane l of wave w fills LDS chunk slot
+  // (row 8*w + l/8 + 8*kWaves*p, position l%8) of the K tile and of the V
+  // tile, so it fetches global chunk (l%8) ^ swz(row) of that row (the same
+  // chunk in every pass: swz depends on row bits 1-3 only).  In the ragged
+  // last tile, rows past N read row N-1 instead (finite data; those keys are
+  // masked and their probabilities are exactly 0).
+  constexpr int kPassRows = 8 * kWaves;
+  constexpr int kPassBytes = kPassRows * kRow;
+  static_assert(kPassRows % 16 == 0, "a pass must not change the row swizzle");
   const int dma_row = 8 * wave + (lane >> 3);
   const int dma_chunk = (lane & 7) ^ swz(dma_row);
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -277,22 +290,31 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   auto dma_tile = [&](int kt, char* stage_base) {
     char* kd = stage_base + wave_s * 1024;
     if ((kt + 1) * kBc <= n) {
-      const int tile = kt * kTileBytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void*)kd, 16,
-                                               (int)dma_lane_off, tile, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (__attribute__((address_space(3))) void*)(kd + kTileBytes),
-                                               16, (int)dma_lane_off, tile, 0, 0);
+#pragma unroll
+      for (int ps = 0; ps < kDmaPasses; ++ps) {
+        const int off = kt * kTileBytes + ps * kPassBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void*)(kd + ps * kPassBytes),
+                                                 16, (int)dma_lane_off, off, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc,
+                                                 (__attribute__((address_space(3))) void*)(kd + kTileBytes + ps * kPassBytes),
+                                                 16, (int)dma_lane_off, off, 0, 0);
+      }
     } else {
       // ragged last tile: rows past N re-read row N-1
-      const int key = min(kt * kBc + dma_row, n - 1);
-      const uint16_t* ks = kg + (size_t)key * kD + dma_chunk * 8;
-      const uint16_t* vs = vg + (size_t)key * kD + dma_chunk * 8;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ks,
-                                       (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vs,
-                                       (__attribute__((address_space(3))) void*)(kd + kTileBytes), 16, 0, 0);
+#pragma unroll
+      for (int ps = 0; ps < kDmaPasses; ++ps) {
+        const int key = min(kt * kBc + dma_row + ps * kPassRows, n - 1);
+        const uint16_t* ks = kg + (size_t)key * kD + dma_chunk * 8;
+        const uint16_t* vs = vg + (size_t)key * kD + dma_chunk * 8;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ks,
+                                         (__attribute__((address_space(3))) void*)(kd + ps * kPassBytes), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vs,
+                                         (__attribute__((address_space(3))) void*)(kd + kTileBytes + ps * kPassBytes),
+                                         16, 0, 0);
+      }
     }
   };
+
 
 
   // End of tile t: the barrier publishes tile t+2, whose DMAs must be done;
@@ -300,7 +322,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // LDS read of the stage the next DMA overwrites has already fed an MFMA, so
   // the barrier needs no LDS wait.
   auto dma_barrier = [&](int t) {
-    vm_wait_barrier_tiles<kLead - 2>(min(kLead - 2, max(0, n_tiles - 3 - t)));
+    vm_wait_barrier_tiles<kDmaPerTile, kLead - 2>(min(kLead - 2, max(0, n_tiles - 3 - t)));
   };
 
 
@@ -461,35 +483,51 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     __builtin_amdgcn_sched_barrier(0);
     const float m = m_run;
     float lsum = 0.f;
+    // The vector-ALU work on score pair k (FMA, exp2, sum, bf16 pack) is
+    // spread over three slots: slot k-1 does its FMA, slot k its exp2, slot
+    // k+1 its sum and pack.  No instruction then waits on the one just before
+    // it (exp2 results in particular arrive late), so the wave keeps issuing
+    // under its MFMAs.  The empty asm statements pin each piece to its slot
+    // (left alone, the compiler sinks sums and packs to the end of the step).
+    float t0 = __builtin_fmaf(s_cur[0], c, -m), t1 = __builtin_fmaf(s_cur[1], c, -m);
+    float e0 = 0.f, e1 = 0.f;
 #pragma unroll
-    for (int slot = 0; slot < 8; ++slot) {
-      if ((slot & 1) == 1) {
-        const int i = slot >> 1, tt = i >> 1, db = i & 1;
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[tt][db], p_prv[tt], acc[db], 0, 0, 0);
-      } else {
-        const int ks = slot >> 1;
-        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.k[ks], qop[ks], ks == 0 ? zero16 : s_nxt, 0, 0, 0);
+    for (int slot = 0; slot <= 8; ++slot) {
+      if (slot < 8) {
+        if ((slot & 1) == 1) {
+          const int i = slot >> 1, tt = i >> 1, db = i & 1;
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[tt][db], p_prv[tt], acc[db], 0, 0, 0);
+        } else {
+          const int ks = slot >> 1;
+          s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.k[ks], qop[ks], ks == 0 ? zero16 : s_nxt, 0, 0, 0);
+        }
+        if (slot == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_ops(npv_base, npv_h, ns_base, ns_h, nxt);
+        }
       }
-      if (slot == 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        load_ops(npv_base, npv_h, ns_base, ns_h, nxt);
+      if (slot >= 1) {
+        // sum and pack pair slot-1 into its 32-bit word of the P operand
+        const int r = 2 * (slot - 1);
+        lsum += e0;
+        lsum += e1;
+        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        unsigned pw = __builtin_bit_cast(unsigned, pr);
+        asm volatile("" : "+v"(pw));
+        u32x4 words = __builtin_bit_cast(u32x4, p_cur[r >> 3]);
+        words[(r & 7) >> 1] = pw;
+        p_cur[r >> 3] = __builtin_bit_cast(bf16x8, words);
+        asm volatile("" : "+v"(lsum));
       }
-      const int r = 2 * slot;
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], c, -m));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r + 1], c, -m));
-      lsum += e0;
-      lsum += e1;
-      // the packed pair goes into its 32-bit word of the P operand; the empty
-      // asm statements keep the conversion and this slot's sum here (without
-      // them they sink to the end of the step, past the MFMAs they should
-      // overlap, and all sixteen probabilities stay live)
-      const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-      unsigned pw = __builtin_bit_cast(unsigned, pr);
-      asm volatile("" : "+v"(pw));
-      u32x4 words = __builtin_bit_cast(u32x4, p_cur[r >> 3]);
-      words[(r & 7) >> 1] = pw;
-      p_cur[r >> 3] = __builtin_bit_cast(bf16x8, words);
-      asm volatile("" : "+v"(lsum));
+      if (slot < 8) {
+        e0 = __builtin_amdgcn_exp2f(t0);
+        e1 = __builtin_amdgcn_exp2f(t1);
+        if (slot < 7) {
+          t0 = __builtin_fmaf(s_cur[2 * slot + 2], c, -m);
+          t1 = __builtin_fmaf(s_cur[2 * slot + 3], c, -m);
+        }
+        asm volatile("" : "+v"(e0), "+v"(e1), "+v"(t0), "+v"(t1));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // Track the largest partial sum (checked once, after the loop): a plain
@@ -499,6 +537,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     l_run += lsum;
     __builtin_amdgcn_sched_barrier(0);
   };
+
 
   f32x16 sA, sB;
   bf16x8 pA[2], pB[2];
@@ -533,7 +572,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     if (tl < n_tiles) dma_tile(tl, stage_ptr(tl));
   // tiles 0 and 1 must have landed; the rest of the min(n_tiles, kLead+1)
   // issued may still fly
-  vm_wait_barrier_tiles<kLead - 1>(max(0, min(n_tiles, kLead + 1) - 2));
+  vm_wait_barrier_tiles<kDmaPerTile, kLead - 1>(max(0, min(n_tiles, kLead + 1) - 2));
   if (last_h >= 0) compute_s(lds0, 0, sA);
 
   // ---- tiles: 0 on the general path, then the steady state (both half
@@ -783,7 +822,9 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   a.n = N;
-  a.q_tiles = (N + kBr - 1) / kBr;
+  const int waves = causal ? kWavesCausal : kWavesFull;
+  const int rows = waves * 32;
+  a.q_tiles = (N + rows - 1) / rows;
   a.total_tiles = B * H * a.q_tiles;
   // c must be > 0: masked scores are -inf and fma(-inf, c, -m) must stay
   // -inf.  A zero (or denormal) scale becomes FLT_MIN, whose scores differ by
@@ -792,9 +833,9 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
   a.q_sign = scale < 0.f ? 0x80008000u : 0u;
 
   void* args[] = {&a};
-  const void* fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true>)
-                          : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false>);
-  const hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles), dim3(kThreads), args, 0,
+  const void* fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal>)
+                          : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull>);
+  const hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles), dim3(waves * 64), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
