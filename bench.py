@@ -9,6 +9,13 @@ to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--n N]
   python bench.py --sweep FILE   # one JSON line per workload into FILE
+  python bench.py --workspace-sweep   # device memory beyond O and LSE vs P, with fits
+
+Besides the contract fields, the line carries per-launch kernel time (mean,
+median, min) from HIP events on the launch stream, a cold-cache variant
+(caches flushed by rewriting a 512 MiB buffer before each launch), the shader
+clock sampled with amd-smi and the roofline fraction at that clock, the
+workspace a call needs, and the fp64 oracle timed on a sample on the host.
 
 FLOPs per step are the algorithmic 4*B*H*N^2*d (QK^T plus PV), halved when
 causal; exponentials are not counted.  The roofline peak is MI355X's
@@ -59,20 +66,121 @@ def traffic_for(workload_name):
 
 
 def time_gpu(fn, steps, warmup, stream):
+    """Wall seconds per step (synchronised on both sides of the timed steps)
+    and the per-launch durations from HIP events recorded on the launch
+    stream between consecutive launches."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall / steps, start.elapsed_time(end) * 1e-3 / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(steps)]
+    return wall / steps, ev[0].elapsed_time(ev[steps]) * 1e-3 / steps, per
+
+
+def time_cold(fn, launches, stream, scratch_mib=512):
+    """Per-launch kernel durations with the caches flushed before each launch:
+    a 512 MiB scratch buffer (twice the 256 MB MALL) is rewritten between
+    launches, outside the timed events."""
+    import torch
+    scratch = torch.empty(scratch_mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+    per = []
+    for i in range(launches):
+        scratch.fill_(float(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e-3)
+    del scratch
+    return per
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def _find_gfx_clock(node):
+    """The shader (GFX) clock in MHz from amd-smi's JSON: the mean over the
+    entries whose key names gfx (one per XCD) and whose 'clk' is a number or
+    a {'value': number} dict, taken in the first dict that has any."""
+    if isinstance(node, dict):
+        vals = []
+        for key, val in node.items():
+            if "gfx" in str(key).lower() and isinstance(val, dict) and "clk" in val:
+                clk = val["clk"]
+                clk = clk.get("value") if isinstance(clk, dict) else clk
+                try:
+                    vals.append(float(clk))
+                except (TypeError, ValueError):
+                    pass
+        if vals:
+            return sum(vals) / len(vals)
+        for val in node.values():
+            found = _find_gfx_clock(val)
+            if found is not None:
+                return found
+    elif isinstance(node, list):
+        for val in node:
+            found = _find_gfx_clock(val)
+            if found is not None:
+                return found
+    return None
+
+
+class ClockSampler:
+    """Samples the GPU shader clock with amd-smi in a background thread while
+    the GPU is kept busy.  Reports None when amd-smi or its output is not
+    usable; the clock is context, not part of the result."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.error = [], None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _query(self):
+        import subprocess
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"],
+                             capture_output=True, text=True, timeout=20).stdout
+        val = _find_gfx_clock(json.loads(out))
+        if val is None:
+            raise ValueError("no gfx clock in amd-smi output: " + out[:300])
+        return val
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._query())
+            except Exception as e:  # noqa: BLE001
+                self.error = repr(e)[:400]
+                return
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=30)
+
+    def summary(self):
+        if not self.samples:
+            return {"gfx_mhz_median": None, "samples": 0, "source": "amd-smi", "error": self.error}
+        return {"gfx_mhz_median": median(self.samples), "gfx_mhz_min": min(self.samples),
+                "gfx_mhz_max": max(self.samples), "samples": len(self.samples), "source": "amd-smi",
+                "window": "sampled while the same launches ran back to back for about 4 s"}
 
 
 def cpu_baseline(w, q, k, v, seconds):
@@ -118,7 +226,7 @@ def cpu_baseline(w, q, k, v, seconds):
     }
 
 
-def bench_one(w, steps, warmup, with_cpu, cpu_seconds):
+def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=False):
     import torch
     import exact_attention_29_amd as ea
     from workloads import make_inputs
@@ -131,22 +239,35 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    # workspace: extra device memory a call needs beyond its outputs
+    # workspace: device memory a call needs beyond its outputs.  O and LSE
+    # are allocated first (the allocator rounds blocks, so their own sizes
+    # are not subtracted afterwards); then the call's peak allocation above
+    # the level before it and the change of free device memory are read.
+    out_bytes = o.numel() * o.element_size() + lse.numel() * 4
+    # one call first: the first launch makes the runtime load the code object
+    ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
     free0 = torch.cuda.mem_get_info(dev)[0]
-    o_tmp, lse_tmp = ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal)
+    ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
     torch.cuda.synchronize()
-    out_bytes = o_tmp.numel() * o_tmp.element_size() + lse_tmp.numel() * 4
-    extra = torch.cuda.max_memory_allocated(dev) - base - out_bytes
+    extra = torch.cuda.max_memory_allocated(dev) - base
     free_delta = free0 - torch.cuda.mem_get_info(dev)[0]
-    del o_tmp, lse_tmp
 
     def step():
         ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
 
-    wall, kern = time_gpu(step, steps, warmup, stream)
+    wall, kern, per = time_gpu(step, steps, warmup, stream)
+    clock_info = None
+    if clock:
+        # amd-smi takes about a second per query: keep the GPU busy with the
+        # same launches for ~4 s while a thread samples it
+        with ClockSampler() as clk:
+            for _ in range(max(1, int(4.0 / kern))):
+                step()
+            torch.cuda.synchronize()
+        clock_info = clk.summary()
     flops = w.flops
     value = flops / wall / 1e12
     achieved = flops / kern / 1e12
@@ -184,11 +305,72 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds):
         },
         "workspace": {"extra_bytes": int(extra), "mem_get_info_delta": int(free_delta),
                       "output_bytes": int(out_bytes)},
+        "timing": {"kernel_ms_mean": round(kern * 1e3, 4), "kernel_ms_median": round(median(per) * 1e3, 4),
+                   "kernel_ms_min": round(min(per) * 1e3, 4), "launches": steps,
+                   "tflops_at_median": round(flops / median(per) / 1e12, 2),
+                   "cache": "warm: inputs stay resident in L2/MALL between launches"},
     }
+    if clock_info is not None:
+        line["clock"] = clock_info
+        mhz = clock_info.get("gfx_mhz_median")
+        if mhz:
+            peak_at_clock = PEAK_BF16_TFLOPS * mhz / 2400.0
+            line["clock"]["bf16_peak_at_clock"] = round(peak_at_clock, 1)
+            line["clock"]["pct_of_peak_at_clock"] = round(100.0 * achieved / peak_at_clock, 2)
+    if cold_launches:
+        cper = time_cold(step, cold_launches, stream)
+        line["cold"] = {"kernel_ms_median": round(median(cper) * 1e3, 4),
+                        "kernel_ms_min": round(min(cper) * 1e3, 4), "launches": cold_launches,
+                        "tflops_at_median": round(flops / median(cper) / 1e12, 2),
+                        "cache": "cold: a 512 MiB buffer is rewritten before every launch"}
     if with_cpu:
         log("[bench] timing the fp64 oracle on a sample ...")
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, cpu_seconds)
     return line
+
+
+def workspace_sweep():
+    """Device memory one call needs beyond its outputs, over the patch counts
+    of the 0.5-8 MP workloads, with the two fits: extra = c*P + d and
+    extra = a*P^2 + b*P (a materialised score table would give a = 2*H
+    bytes per P^2 for bf16)."""
+    import numpy as np
+    import torch
+    import exact_attention_29_amd as ea
+    from workloads import PATCH_SWEEP, WORKLOADS, make_inputs
+
+    dev = "cuda:0"
+    rows = []
+    for n in list(PATCH_SWEEP) + [WORKLOADS["patch_3mp"].N, WORKLOADS["patch_8mp"].N]:
+        w = WORKLOADS["patch_3mp"].with_n(n)
+        q, k, v = (t.to(dev) for t in make_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, n), dtype=torch.float32, device=dev)
+        out_bytes = o.numel() * o.element_size() + lse.numel() * 4
+        # one call first: the first launch makes the runtime load the code object
+        ea.forward(q, k, v, scale=w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        free0 = torch.cuda.mem_get_info(dev)[0]
+        ea.forward(q, k, v, scale=w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        peak_extra = torch.cuda.max_memory_allocated(dev) - base
+        free_delta = free0 - torch.cuda.mem_get_info(dev)[0]
+        rows.append({"P": n, "extra_bytes": int(peak_extra), "output_bytes": int(out_bytes),
+                     "mem_get_info_delta": int(free_delta),
+                     "score_table_bytes_avoided": int(w.B * w.H * n * n * 2)})
+        log(f"[workspace] P={n}: extra {peak_extra} B beyond {out_bytes} B of outputs")
+        del q, k, v, o, lse
+    P = np.array([r["P"] for r in rows], dtype=np.float64)
+    E = np.array([r["extra_bytes"] for r in rows], dtype=np.float64)
+    lin = np.linalg.lstsq(np.stack([P, np.ones_like(P)], 1), E, rcond=None)[0]
+    quad = np.linalg.lstsq(np.stack([P * P, P], 1), E, rcond=None)[0]
+    return {"workspace_sweep": rows,
+            "fit_linear": {"c_bytes_per_P": float(lin[0]), "d_bytes": float(lin[1])},
+            "fit_quadratic": {"a_bytes_per_P2": float(quad[0]), "b_bytes_per_P": float(quad[1])},
+            "method": "O and LSE allocated first; then torch max_memory_allocated during the "
+                      "call minus allocated before it, and the hipMemGetInfo free-memory delta"}
 
 
 def main():
@@ -204,6 +386,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", default=None, help="write one JSON line per workload to this file")
+    ap.add_argument("--cold", type=int, default=30,
+                    help="launches timed with flushed caches after the warm steps (0: skip)")
+    ap.add_argument("--no-clock", action="store_true", help="do not sample the clock with amd-smi")
+    ap.add_argument("--workspace-sweep", action="store_true",
+                    help="only measure the device memory a call needs beyond O and LSE, "
+                         "at P = 1,944 .. 38,400, and fit it against P")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -233,6 +421,10 @@ def main():
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 3}))
         return
 
+    if args.workspace_sweep:
+        print(json.dumps(workspace_sweep()), flush=True)
+        return
+
     if args.sweep:
         cases = [WORKLOADS[n] for n in ("bert_large", "gpt2_small_causal")]
         cases += [WORKLOADS["patch_3mp"].with_n(n) for n in PATCH_SWEEP]
@@ -257,7 +449,8 @@ def main():
         from dataclasses import replace
         w = replace(w, causal=args.causal == "yes")
     log(f"[bench] {w.name} {w.shape} {w.dtype} causal={w.causal} steps={args.steps} warmup={args.warmup}")
-    line = bench_one(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
+    line = bench_one(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds,
+                     cold_launches=args.cold, clock=not args.no_clock)
     print(json.dumps(line), flush=True)
 
 

@@ -290,6 +290,29 @@ def test_deterministic_repeat():
 
 # ------------------------------------------------------------ memory behaviour
 
+@pytest.mark.parametrize("n", list(PATCH_SWEEP) + [WORKLOADS["patch_3mp"].N, WORKLOADS["patch_8mp"].N])
+def test_workspace_is_zero_across_patch_counts(n):
+    """Device memory a call needs beyond O and LSE, over the patch counts of
+    the 0.5-8 MP workloads: none (a score table would need 2*H*P^2 bytes,
+    47 GB at P=38,400).  O and LSE are allocated first, so the allocator's
+    rounding of their blocks does not enter the measurement."""
+    w = WORKLOADS["patch_3mp"].with_n(n)
+    q, k, v = (t.to(DEV) for t in make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, n, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    free0 = torch.cuda.mem_get_info()[0]
+    ea.forward(q, k, v, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() - base == 0
+    assert torch.cuda.mem_get_info()[0] == free0
+    # and the result is right on sampled rows
+    rows = sample_rows(n, 64, seed=n)
+    compare(w, q.cpu(), k.cpu(), v.cpu(), o, lse, rows=rows, what=f"P={n}")
+
+
 def test_no_workspace_and_no_out_of_bounds_writes():
     """The call allocates nothing beyond O and LSE, and writes nothing outside
     them: O and LSE sit inside guard bands filled with a canary."""
