@@ -18,7 +18,12 @@ plainest lower-triangular reading with the diagonal kept, so no row is empty.
 Optional ``key_valid`` [B, N] (True = the key takes part) is the additive
 -inf key-padding bias described on the Qiita page, section 4 and section 6:
 a padded key gets -inf added to its score.  A row that sees no key at all
-has no defined softmax; the oracle returns NaN for it.
+has no softmax; the pages say nothing about it.  Reading taken here: its row
+sum is the empty sum 0, so LSE = ln 0 = -inf, and O is the empty weighted
+sum, the zero vector.  These are the values under which merging the results
+of two disjoint key sets (the combination rule of the FlashAttention reading
+notes, section "proposed method": m = max(m1, m2), l = e^(m1-m) l1 +
+e^(m2-m) l2) leaves the other set's result unchanged when one set is empty.
 
 LSE: the forward pass keeps, besides O, the softmax statistics m (row max)
 and l (row sum of exp(s - m)) for the backward pass (FlashAttention reading
@@ -85,6 +90,18 @@ def _lse(m, l):
     return m + np.log(l)
 
 
+def _empty_rows(vis):
+    """Rows that see no key at all."""
+    return ~vis.any(axis=1)
+
+
+def _empty_row_result(o, lse, empty):
+    """An empty row: O = 0 (empty weighted sum), LSE = ln 0 = -inf."""
+    o = np.where(empty[:, None], 0.0, o)
+    lse = np.where(empty, -np.inf, lse)
+    return o, lse
+
+
 def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
@@ -117,11 +134,16 @@ def attention(q, k, v, scale, causal=False, key_valid=None, rows=None,
                     s = _scores(q[b, h, r], k[b, h], scale)
                     vis = _visible(r, N, causal, None if kv is None else kv[b])
                     s = np.where(vis, s, -np.inf)
+                    empty = _empty_rows(vis)
                     m = _row_max(s)
+                    m = np.where(empty, 0.0, m)   # any finite shift: every e_ij is 0
                     e = _exp_shifted(s, m)
                     l = _row_sum(e)
-                    o[b, h, c0:c0 + len(r)] = _normalise(_weighted_values(e, v[b, h]), l)
-                    lse[b, h, c0:c0 + len(r)] = _lse(m, l)
+                    o_r = _normalise(_weighted_values(e, v[b, h]), l)
+                    lse_r = _lse(m, l)
+                    o_r, lse_r = _empty_row_result(o_r, lse_r, empty)
+                    o[b, h, c0:c0 + len(r)] = o_r
+                    lse[b, h, c0:c0 + len(r)] = lse_r
     return o, lse
 
 
@@ -149,6 +171,11 @@ def attention_materialised(q, k, v, scale, causal=False, key_valid=None):
         p = w / z
         o = np.matmul(p, v)
         lse = (top + np.log(z))[..., 0]
+    # a row with every key hidden: P row 0, O = 0, LSE = -inf
+    empty = np.broadcast_to(hide.all(axis=-1), lse.shape)
+    p = np.where(empty[..., None], 0.0, p)
+    o = np.where(empty[..., None], 0.0, o)
+    lse = np.where(empty, -np.inf, lse)
     return o, lse, p
 
 
@@ -171,8 +198,8 @@ def attention_fsum(q, k, v, scale, causal=False, key_valid=None):
                         if (not causal or j <= i)
                         and (key_valid is None or key_valid[b][j])]
                 if not keys:
-                    o[b, h, i] = np.nan
-                    lse[b, h, i] = np.nan
+                    o[b, h, i] = 0.0
+                    lse[b, h, i] = -math.inf
                     continue
                 s = {j: scale * math.fsum(q[b, h, i, t] * k[b, h, j, t] for t in range(d))
                      for j in keys}

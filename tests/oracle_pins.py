@@ -298,6 +298,63 @@ def pin_row_sampling():
         _close(ls, lse[:, :, rows], 1e-14, "sampled rows LSE")
 
 
+def _merge(o1, l1, o2, l2):
+    """Combine the results of two disjoint key sets (the blockwise rule of the
+    FlashAttention reading notes, section "proposed method", written with
+    LSE = m + ln l): LSE = ln(e^LSE1 + e^LSE2), O = sum_g e^(LSE_g - LSE) O_g."""
+    lse = np.logaddexp(l1, l2)
+    w1 = np.exp(l1 - lse)[..., None]
+    w2 = np.exp(l2 - lse)[..., None]
+    return w1 * o1 + w2 * o2, lse
+
+
+def pin_key_shard_merge():
+    """Hiding complementary key sets and merging the two results gives the
+    unmasked result, for random sets and for the split where one set is empty
+    (whose result must then be O = 0, LSE = -inf: nothing else leaves the
+    merge unchanged).  Causal masking on top must combine the same way."""
+    rng = _rng(21)
+    B, H, N, d = 2, 2, 23, 8
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    for causal in (False, True):
+        full_o, full_l = O.attention(q, k, v, 0.4, causal=causal)
+        for split in ("random", "empty"):
+            a = rng.random((B, N)) < 0.5 if split == "random" else np.ones((B, N), dtype=bool)
+            oa, la = O.attention(q, k, v, 0.4, causal=causal, key_valid=a)
+            ob, lb = O.attention(q, k, v, 0.4, causal=causal, key_valid=~a)
+            if split == "empty":
+                assert np.all(ob == 0.0) and np.all(lb == -np.inf), "empty key set: O = 0, LSE = -inf"
+            with np.errstate(invalid="ignore", divide="ignore"):
+                o, l = _merge(oa, la, ob, lb)
+            # rows empty in both shards cannot occur: the union is every key
+            _close(o, full_o, 1e-12, f"merged O ({split}, causal={causal})")
+            _close(l, full_l, 1e-12, f"merged LSE ({split}, causal={causal})")
+
+
+def pin_padding_prefix_uniform():
+    """Key padding as a valid prefix of length L_b per batch entry, with Q = 0:
+    a row averages V over the first L_b keys and LSE = ln L_b; with L_b = 0 the
+    row sees nothing: O = 0, LSE = -inf.  Causal rows see min(i+1, L_b) keys."""
+    rng = _rng(22)
+    B, H, N, d = 4, 2, 19, 8
+    lens = np.array([19, 7, 1, 0])
+    valid = np.arange(N)[None, :] < lens[:, None]
+    q = np.zeros((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    for causal in (False, True):
+        o, lse = O.attention(q, k, v, 0.7, causal=causal, key_valid=valid, row_chunk=5)
+        for b in range(B):
+            for i in range(N):
+                cnt = min(i + 1, lens[b]) if causal else lens[b]
+                if cnt == 0:
+                    assert np.all(o[b, :, i] == 0.0) and np.all(lse[b, :, i] == -np.inf), \
+                        f"padding: empty row b={b} i={i}"
+                    continue
+                _close(o[b, :, i], v[b, :, :cnt].mean(axis=1), 1e-12, f"padding O b={b} i={i}")
+                _close(lse[b, :, i], np.full(H, math.log(cnt)), 1e-12, f"padding LSE b={b} i={i}")
+
+
 INDEPENDENT_PINS = [
     pin_uniform_closed_form,
     pin_identity_closed_form,
@@ -309,6 +366,8 @@ INDEPENDENT_PINS = [
     pin_score_shift,
     pin_one_hot_limit,
     pin_page_mask_example,
+    pin_key_shard_merge,
+    pin_padding_prefix_uniform,
 ]
 
 ALL_PINS = INDEPENDENT_PINS + [

@@ -37,6 +37,14 @@ MUTANTS = {
     "lse_without_max": ("_lse", lambda m, l: np.log(l)),
     "lse_base_two": ("_lse", lambda m, l: m + np.log2(l)),
     "lse_of_sum_only": ("_lse", lambda m, l: m),
+    "key_mask_inverted": ("_visible", lambda rows, n, causal, kv: (
+        (np.arange(n)[None, :] <= rows[:, None]) if causal else np.ones((len(rows), n), bool))
+        & (True if kv is None else ~kv[None, :])),
+    "empty_rows_nan": ("_empty_row_result", lambda o, lse, empty: (
+        np.where(empty[:, None], np.nan, o), np.where(empty, np.nan, lse))),
+    "empty_rows_lse_zero": ("_empty_row_result", lambda o, lse, empty: (
+        np.where(empty[:, None], 0.0, o), np.where(empty, 0.0, lse))),
+    "empty_rows_uniform": ("_empty_row_result", lambda o, lse, empty: (o, lse)),
 }
 
 
