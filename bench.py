@@ -226,7 +226,7 @@ def cpu_baseline(w, q, k, v, seconds):
     }
 
 
-def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=False):
+def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=False, mask="none"):
     import torch
     import exact_attention_29_amd as ea
     from workloads import make_inputs
@@ -238,6 +238,14 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     o = torch.empty_like(qd)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # key padding as the pages' layer passes it: every key valid (an all-False
+    # padding mask), given as a per-entry length or as a byte mask
+    masks = {}
+    if mask == "len":
+        masks["key_len"] = torch.full((B,), N, dtype=torch.int32, device=dev)
+    elif mask == "bytes":
+        # packed once, outside the timed calls (attn_pack_key_mask)
+        masks["key_bits"] = ea.pack_key_mask(torch.ones((B, N), dtype=torch.bool, device=dev))
 
     # workspace: device memory a call needs beyond its outputs.  O and LSE
     # are allocated first (the allocator rounds blocks, so their own sizes
@@ -245,18 +253,18 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     # the level before it and the change of free device memory are read.
     out_bytes = o.numel() * o.element_size() + lse.numel() * 4
     # one call first: the first launch makes the runtime load the code object
-    ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, **masks)
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
     free0 = torch.cuda.mem_get_info(dev)[0]
-    ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, **masks)
     torch.cuda.synchronize()
     extra = torch.cuda.max_memory_allocated(dev) - base
     free_delta = free0 - torch.cuda.mem_get_info(dev)[0]
 
     def step():
-        ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, **masks)
 
     wall, kern, per = time_gpu(step, steps, warmup, stream)
     clock_info = None
@@ -289,6 +297,8 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
             "workload": f"{w.name}: {w.what}",
             "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "scale": w.scale,
             "inputs": f"i.i.d. N(0,{w.sigma}^2), seed {w.seed}",
+            "key_mask": {"none": "none", "len": "key_len = N per entry (attn_fwd_masked)",
+                         "bytes": "key mask all true, packed to bits (attn_fwd_masked, mask path)"}[mask],
             "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
         },
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
@@ -299,7 +309,8 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_fwd_bf16_kernel<%s>" % ("true, 4" if w.causal else "false, 8"),
+            "kernel": "attn_fwd_bf16_kernel<%s, %s>" % ("true, 4" if w.causal else "false, 8",
+                                                        "true" if mask == "bytes" else "false"),
             "kernel_ms": round(kern * 1e3, 4),
             "algorithmic_bytes": 4 * B * H * N * d * 2 + 4 * B * H * N,
         },
@@ -389,6 +400,8 @@ def main():
     ap.add_argument("--cold", type=int, default=30,
                     help="launches timed with flushed caches after the warm steps (0: skip)")
     ap.add_argument("--no-clock", action="store_true", help="do not sample the clock with amd-smi")
+    ap.add_argument("--mask", choices=["none", "len", "bytes"], default="none",
+                    help="time attn_fwd_masked with every key valid, as a length or a byte mask")
     ap.add_argument("--workspace-sweep", action="store_true",
                     help="only measure the device memory a call needs beyond O and LSE, "
                          "at P = 1,944 .. 38,400, and fit it against P")
@@ -431,12 +444,15 @@ def main():
         cases += [WORKLOADS["patch_3mp"], WORKLOADS["patch_8mp"]]
         from dataclasses import replace
         cases.append(replace(WORKLOADS["patch_3mp"], causal=True, name="patch_3mp_causal"))
+        cases = [(c, "none") for c in cases]
+        cases += [(WORKLOADS["patch_3mp"], "len"), (WORKLOADS["patch_3mp"], "bytes"),
+                  (WORKLOADS["bert_large"], "bytes")]
         with open(args.sweep, "w") as f:
-            for w in cases:
+            for w, mask in cases:
                 steps = max(args.steps, 200) if w.flops < 2e10 else args.steps
                 warm = max(args.warmup, 1000) if w.flops < 2e10 else args.warmup
-                log(f"[bench] {w.name} {w.shape} causal={w.causal}")
-                line = bench_one(w, steps, warm, False, 0)
+                log(f"[bench] {w.name} {w.shape} causal={w.causal} mask={mask}")
+                line = bench_one(w, steps, warm, False, 0, mask=mask)
                 f.write(json.dumps(line) + "\n")
                 f.flush()
                 log(f"[bench] {w.name}: {line['value']} TFLOP/s, kernel {line['roofline']['kernel_ms']} ms")
@@ -450,7 +466,7 @@ def main():
         w = replace(w, causal=args.causal == "yes")
     log(f"[bench] {w.name} {w.shape} {w.dtype} causal={w.causal} steps={args.steps} warmup={args.warmup}")
     line = bench_one(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds,
-                     cold_launches=args.cold, clock=not args.no_clock)
+                     cold_launches=args.cold, clock=not args.no_clock, mask=args.mask)
     print(json.dumps(line), flush=True)
 
 

@@ -1,8 +1,10 @@
 """Exact attention forward on MI355X: a thin Python binding over libattn.so.
 
-The functions ``attn_fwd``, ``attn_fwd_fp32`` and ``attn_strerror`` carry the
-names and arguments of the C entry points declared in include/attn.h and only
-marshal arguments; every step of the computation runs in the HIP kernels.
+The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
+``attn_fwd_fp32_masked``, ``attn_pack_key_mask`` and ``attn_strerror`` carry
+the names and arguments
+of the C entry points declared in include/attn.h and only marshal arguments;
+every step of the computation runs in the HIP kernels.
 ``forward`` is a convenience wrapper that allocates the outputs with torch
 and launches on torch's current stream.  There is no CPU fallback: without
 the built library (or without a gfx950 device) every call raises.
@@ -13,7 +15,8 @@ import os
 
 import torch  # imported first: the library then binds to torch's HIP runtime
 
-__all__ = ["attn_fwd", "attn_fwd_fp32", "attn_strerror", "forward", "AttnError",
+__all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
+           "attn_pack_key_mask", "attn_strerror", "forward", "pack_key_mask", "AttnError",
            "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -21,7 +24,8 @@ _LIB_PATH = os.path.join(_PKG, "libattn.so")
 _lib = None
 
 ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH = range(5)
-EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_strerror")
+EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked", "attn_pack_key_mask",
+            "attn_strerror")
 
 
 class AttnError(RuntimeError):
@@ -50,6 +54,13 @@ def load_library():
     lib.attn_fwd.restype = i32
     lib.attn_fwd_fp32.argtypes = sig
     lib.attn_fwd_fp32.restype = i32
+    msig = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32, ptr, ptr, ptr]
+    lib.attn_fwd_masked.argtypes = msig
+    lib.attn_fwd_masked.restype = i32
+    lib.attn_fwd_fp32_masked.argtypes = msig
+    lib.attn_fwd_fp32_masked.restype = i32
+    lib.attn_pack_key_mask.argtypes = [ptr, ptr, i32, i32, ptr]
+    lib.attn_pack_key_mask.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -75,16 +86,53 @@ def attn_fwd_fp32(q, k, v, o, lse, B, H, N, d, scale, causal, stream):
     _check(load_library().attn_fwd_fp32(q, k, v, o, lse, B, H, N, d, float(scale), int(bool(causal)), stream))
 
 
+def attn_fwd_masked(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, key_bits, stream):
+    """C entry point attn_fwd_masked: raw addresses; key_len and key_bits may be 0 (NULL)."""
+    _check(load_library().attn_fwd_masked(q, k, v, o, lse, B, H, N, d, float(scale), int(bool(causal)),
+                                          key_len, key_bits, stream))
+
+
+def attn_fwd_fp32_masked(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, key_bits, stream):
+    """C entry point attn_fwd_fp32_masked: raw addresses as in attn_fwd_masked."""
+    _check(load_library().attn_fwd_fp32_masked(q, k, v, o, lse, B, H, N, d, float(scale), int(bool(causal)),
+                                               key_len, key_bits, stream))
+
+
+def attn_pack_key_mask(key_valid, key_bits, B, N, stream):
+    """C entry point attn_pack_key_mask: raw addresses of the byte mask and the bit words."""
+    _check(load_library().attn_pack_key_mask(key_valid, key_bits, B, N, stream))
+
+
+def pack_key_mask(key_valid):
+    """Bit words [B, ceil(N/32)] (int32) of a bool or uint8 [B, N] device mask,
+    built by attn_pack_key_mask on torch's current stream."""
+    if key_valid.dtype not in (torch.bool, torch.uint8) or key_valid.dim() != 2 \
+            or not key_valid.is_contiguous() or not key_valid.is_cuda:
+        raise ValueError("key_valid must be a contiguous bool or uint8 [B, N] GPU tensor")
+    B, N = key_valid.shape
+    bits = torch.empty((B, (N + 31) // 32), dtype=torch.int32, device=key_valid.device)
+    with torch.cuda.device(key_valid.device):
+        attn_pack_key_mask(key_valid.data_ptr(), bits.data_ptr(), B, N, _stream_handle(key_valid.device))
+    return bits
+
+
 def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def forward(q, k, v, scale=None, causal=False, out=None, lse=None):
+def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None, key_valid=None,
+            key_bits=None):
     """O, LSE for contiguous [B, H, N, d] tensors on one device.
 
     bf16 tensors use attn_fwd, fp32 tensors attn_fwd_fp32.  ``scale``
     defaults to 1/sqrt(d).  ``out`` and ``lse`` may be given to reuse buffers.
-    Launches on torch's current stream and returns without synchronising.
+    Key padding: ``key_len`` an int32 [B] tensor (keys j >= key_len[b] take no
+    part) and/or ``key_valid`` a bool or uint8 [B, N] tensor (key j of entry b
+    takes part where it is True / non-zero; packed to bits by
+    attn_pack_key_mask first) or ``key_bits`` the packed int32 [B, ceil(N/32)]
+    words, all on the same device; then the masked entry points are called.  Rows that see no key get O = 0 and
+    LSE = -inf.  Launches on torch's current stream and returns without
+    synchronising.
     """
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k, v must share one dtype")
@@ -107,8 +155,31 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None):
         raise ValueError("out must be a contiguous tensor like q")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_fp32
+    if key_valid is not None:
+        if key_bits is not None:
+            raise ValueError("give key_valid or key_bits, not both")
+        if key_valid.shape != (B, N) or key_valid.device != q.device:
+            raise ValueError("key_valid must be a [B, N] tensor on q's device")
+        key_bits = pack_key_mask(key_valid)
+    if key_len is None and key_bits is None:
+        fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_fp32
+        with torch.cuda.device(q.device):
+            fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+               B, H, N, d, scale, causal, _stream_handle(q.device))
+        return out, lse
+    kl_ptr = kv_ptr = 0
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or key_len.shape != (B,) or not key_len.is_contiguous() \
+                or key_len.device != q.device:
+            raise ValueError("key_len must be a contiguous int32 [B] tensor on q's device")
+        kl_ptr = key_len.data_ptr()
+    if key_bits is not None:
+        if key_bits.dtype != torch.int32 or key_bits.shape != (B, (N + 31) // 32) \
+                or not key_bits.is_contiguous() or key_bits.device != q.device:
+            raise ValueError("key_bits must be a contiguous int32 [B, ceil(N/32)] tensor on q's device")
+        kv_ptr = key_bits.data_ptr()
+    fn = attn_fwd_masked if q.dtype == torch.bfloat16 else attn_fwd_fp32_masked
     with torch.cuda.device(q.device):
         fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-           B, H, N, d, scale, causal, _stream_handle(q.device))
+           B, H, N, d, scale, causal, kl_ptr, kv_ptr, _stream_handle(q.device))
     return out, lse

@@ -110,6 +110,10 @@ struct Bf16Args {
   int total_tiles;  // B * H * q_tiles
   float c;          // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign;  // 0x80008000 when scale < 0 (Q negated), else 0
+  int heads;        // H: batch entry of head bh is bh / H
+  const int* key_len;         // [B] or null: keys j >= key_len[b] are hidden
+  const uint32_t* key_bits;   // [B][ceil(N/32)] or null: bit j%32 of word j/32
+                              // clear hides key j of entry b
 };
 
 // s_waitcnt vmcnt(N) followed by s_barrier.  A plain s_barrier: the
@@ -188,7 +192,7 @@ __device__ __forceinline__ bf16x8 lds_read_vt(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <bool kCausal, int kWaves>
+template <bool kCausal, int kWaves, bool kKeyMask>
 __global__ void __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(Bf16Args a) {
@@ -256,13 +260,16 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     qop[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
-  // ---- key range
-  int kv_end = n;
-  if (kCausal) kv_end = min(n, qt * kBr + kBr);
+  // ---- key range.  n_k: keys of this batch entry that may be visible (a
+  // per-entry valid length hides the rest, like keys past the end).
+  const int b_entry = bh / a.heads;
+  const int n_k = a.key_len ? min(max(a.key_len[b_entry], 0), n) : n;
+  int kv_end = n_k;
+  if (kCausal) kv_end = min(n_k, qt * kBr + kBr);
   const int n_half = (kv_end + 31) / 32;  // half tiles of 32 keys
   const int n_tiles = (n_half + 1) / 2;
   // last key / half tile with any visible key for this wave
-  const int wave_last_key = q_wave >= n ? -1 : (kCausal ? min(n - 1, q_wave + 31) : n - 1);
+  const int wave_last_key = (q_wave >= n || n_k == 0) ? -1 : (kCausal ? min(n_k - 1, q_wave + 31) : n_k - 1);
   const int last_h = wave_last_key < 0 ? -1 : wave_last_key / 32;
 
   // ---- global -> LDS staging by DMA (buffer/global loads with the LDS
@@ -380,14 +387,32 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   };
   auto stage_base = [&](int j) { return stage_ptr((j >> 1) % kStages); };
 
-  // Hidden keys of half tile j become -inf (ragged end, causal diagonal).
-  auto needs_mask = [&](int j) { return 32 * j + 32 > n || (kCausal && 32 * j + 31 > q_wave); };
-  auto apply_mask = [&](int j, f32x16& s) {
-    const int lim = kCausal ? min(qi, n - 1) : n - 1;  // last visible key
+  // Hidden keys of half tile j become -inf (ragged end or valid length,
+  // causal diagonal, and with a key mask every key it hides).
+  const uint32_t* const mask_row = kKeyMask ? a.key_bits + (size_t)b_entry * ((n + 31) / 32) : nullptr;
+  auto needs_lim = [&](int j) { return 32 * j + 32 > n_k || (kCausal && 32 * j + 31 > q_wave); };
+  auto needs_mask = [&](int j) { return kKeyMask || needs_lim(j); };
+  // One mask word covers a half tile's 32 keys, the same for every lane (a
+  // scalar load).  Register r holds key 8*(r/4) + 4*hi + r%4: its 64-lane
+  // condition is built on the scalar unit and selects with one v_cndmask.
+  auto apply_bits = [&](uint32_t vis, f32x16& s) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 32 * j + 8 * (r >> 2) + 4 * hi + (r & 3);
-      s[r] = key <= lim ? s[r] : -INFINITY;
+      const int k0 = 8 * (r >> 2) + (r & 3);
+      const uint64_t lanes = (((vis >> k0) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                             (((vis >> (k0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+      s[r] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? s[r] : -INFINITY;
+    }
+  };
+  auto apply_mask = [&](int j, f32x16& s) {
+    if (kKeyMask) apply_bits(mask_row[j], s);  // j < n_half <= ceil(N/32)
+    if (!kKeyMask || needs_lim(j)) {
+      const int lim = kCausal ? min(qi, n_k - 1) : n_k - 1;  // last visible key
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * j + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[r] = key <= lim ? s[r] : -INFINITY;
+      }
     }
   };
 
@@ -479,7 +504,10 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // with their FMA, sum and bf16 packing).
   auto step_fast = [&](const Ops& cur, Ops& nxt, const char* npv_base, int npv_h,
                        const char* ns_base, int ns_h, f32x16& s_cur, bf16x8 (&p_cur)[2],
-                       f32x16& s_nxt, const bf16x8 (&p_prv)[2]) {
+                       f32x16& s_nxt, const bf16x8 (&p_prv)[2], uint32_t vis) {
+    // with a key mask, hide the masked keys of this half tile first (nothing
+    // to do, and no instruction spent, when all 32 keys take part)
+    if (kKeyMask && vis != 0xffffffffu) apply_bits(vis, s_cur);
     __builtin_amdgcn_sched_barrier(0);
     const float m = m_run;
     float lsum = 0.f;
@@ -558,8 +586,10 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     constexpr int st = decltype(stage_tag)::value;
     char* const b_cur = stage_ptr(st);
     char* const b_next = stage_ptr((st + 1) % kStages);
-    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB);  // j = 2t
-    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA);  // j = 2t + 1
+    const uint32_t vis0 = kKeyMask ? mask_row[2 * t] : 0xffffffffu;
+    const uint32_t vis1 = kKeyMask ? mask_row[2 * t + 1] : 0xffffffffu;
+    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0);  // j = 2t
+    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1);  // j = 2t + 1
     dma_barrier(t);
     if (t + 1 + kLead < n_tiles) dma_tile(t + 1 + kLead, stage_ptr((st + 1 + kLead) % kStages));
   };
@@ -585,11 +615,16 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   {
     int lim = min((n_half - 3) / 2, (last_h - 2) / 2);  // 2t+2 < n_half, 2t+2 <= last_h
     if (last_h < 2) lim = 0;
-    int full = n / 32;                                   // halves with no ragged key
+    int full = n_k / 32;                                 // halves with no ragged key
     if (kCausal) full = min(full, q_wave / 32);          // halves before the diagonal
     lim = min(lim, (full - 2) / 2);                      // 2t+1 < full
     if (full < 2) lim = 0;
     t_fast_end = max(1, lim + 1);
+    // The steady state needs a finite reference in every row: with a key
+    // mask, a row whose first tile was all hidden has none yet, so such a
+    // wave stays on the exact-max path (no -inf - -inf, no NaN).  Without a
+    // key mask, key 0 is visible to every row.
+    if (kKeyMask && __any(m_run == -INFINITY)) t_fast_end = 1;
   }
   int t = 1;
   // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
@@ -603,21 +638,21 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   }
   for (; t < n_tiles; ++t) tile_general(t);
   // the last half tile's PV
-  if (n_half - 1 <= last_h) {
+  if (n_half >= 1 && n_half - 1 <= last_h) {
     if ((n_half - 1) & 1) compute_pv(stage_base(n_half - 1), 1, pB);
     else compute_pv(stage_base(n_half - 1), 0, pA);
   }
 
   // ---- rare fallback: some steady-state step of this wave had a partial
-  // row sum above 2^32, i.e. a score far above the reference max (or an
-  // overflow to inf; a later rescale by 0 would then turn the row sum into
-  // NaN).  The test compares bit patterns: both values are non-negative or
-  // NaN, and an integer compare cannot be folded away by the compiler's
-  // no-NaN assumption.  Such a wave recomputes its rows with an exact max on
-  // every half tile, reading K and V from global memory (other waves may
-  // still be using the LDS ring; this path takes no barrier).
+  // row sum above 2^32, i.e. a score far above the reference max, or an
+  // overflow to +inf.  The steady state runs only with a finite reference,
+  // so no NaN arises from finite inputs and the largest partial sum is a
+  // plain non-negative number (compared as bits), +inf at worst.  Such a
+  // wave recomputes its rows with an exact max on every half tile, reading
+  // K and V from global memory (other waves may still be using the LDS
+  // ring; this path takes no barrier).
   const bool stale = __builtin_bit_cast(unsigned, l_part_max) > kRedoBits ||
-                     (__builtin_bit_cast(unsigned, l_run) & 0x7fffffffu) >= kInfBits;
+                     __builtin_bit_cast(unsigned, l_run) >= kInfBits;
   if (__any(stale)) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -667,10 +702,12 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     }
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  A row that saw no
+  // key (all hidden by the valid length or the mask) has l = 0: O = 0 and
+  // LSE = -inf, the empty sum.
   const float l_tot = half_swap_sum(l_run);
   if (qi < n) {
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = a.o + head + (size_t)qi * kD;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
@@ -683,7 +720,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
         *(u32x2*)(orow + f0) = w;
       }
     }
-    if (hi == 0) a.lse[(size_t)bh * n + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    if (hi == 0) a.lse[(size_t)bh * n + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -699,6 +736,9 @@ struct F32Args {
   int q_tiles;  // ceil(n / 64)
   float scale;
   int causal;
+  int heads;
+  const int* key_len;         // [B] or null
+  const uint32_t* key_bits;   // [B][ceil(N/32)] or null
 };
 
 constexpr int kF32Keys = 32;  // keys per LDS tile in the fp32 kernel
@@ -721,8 +761,11 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
   }
   const float c = a.scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.f;
-  const int kv_end = a.causal ? min(n, qt * 64 + 64) : n;
-  const int row_last = a.causal ? min(qi, n - 1) : n - 1;
+  const int b_entry = bh / a.heads;
+  const int n_k = a.key_len ? min(max(a.key_len[b_entry], 0), n) : n;
+  const uint32_t* const mask_row = a.key_bits ? a.key_bits + (size_t)b_entry * ((n + 31) / 32) : nullptr;
+  const int kv_end = a.causal ? min(n_k, qt * 64 + 64) : n_k;
+  const int row_last = a.causal ? min(qi, n_k - 1) : n_k - 1;
 
   for (int k0 = 0; k0 < kv_end; k0 += kF32Keys) {
     __syncthreads();
@@ -735,12 +778,15 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     __syncthreads();
     float t[kF32Keys];
     float mx = -INFINITY;
+    // the tile's 32 keys are one mask word (k0 is a multiple of 32, k0 < N)
+    static_assert(kF32Keys == 32, "one mask word per key tile");
+    const uint32_t word = mask_row ? mask_row[k0 >> 5] : 0xffffffffu;
 #pragma unroll
     for (int r = 0; r < kF32Keys; ++r) {
       float s = 0.f;
 #pragma unroll
       for (int f = 0; f < kD; ++f) s = __builtin_fmaf(qv[f], ks[r][f], s);
-      const bool vis = k0 + r <= row_last;
+      const bool vis = k0 + r <= row_last && ((word >> r) & 1u);
       t[r] = vis ? s * c : -INFINITY;
       mx = fmaxf(mx, t[r]);
     }
@@ -760,11 +806,30 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     }
   }
   if (live) {
-    const float inv = 1.f / l_run;
+    // a row that saw no key: O = 0, LSE = -inf (the empty sum)
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
     for (int f = 0; f < kD; ++f) a.o[head + (size_t)qi * kD + f] = acc[f] * inv;
-    a.lse[(size_t)bh * n + qi] = (m_run + __log2f(l_run)) * kLn2;
+    a.lse[(size_t)bh * n + qi] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   }
+}
+
+// ------------------------------------------------------- key mask packing
+
+// Bit j%32 of word j/32 of row b = (key_valid[b][j] != 0); bits past N are 0.
+// One thread per output word.
+__global__ void __launch_bounds__(256) attn_pack_key_mask_kernel(const uint8_t* key_valid,
+                                                                 uint32_t* key_bits, int n,
+                                                                 int words, long long total) {
+  const long long w = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (w >= total) return;
+  const int b = (int)(w / words);
+  const int j0 = (int)(w - (long long)b * words) * 32;
+  const uint8_t* row = key_valid + (size_t)b * n;
+  uint32_t bits = 0;
+  const int cnt = min(32, n - j0);
+  for (int i = 0; i < cnt; ++i) bits |= (row[j0 + i] != 0 ? 1u : 0u) << i;
+  key_bits[w] = bits;
 }
 
 // ---------------------------------------------------------------- host side
@@ -805,13 +870,12 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
   return ATTN_OK;
 }
 
-}  // namespace
-
-extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                                int B, int H, int N, int d, float scale, int causal,
-                                void* stream) {
+attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int N, int d, float scale, int causal, const int* key_len,
+                        const uint32_t* key_bits, void* stream) {
   attn_status st = validate(q, k, v, o, lse, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
+  if (misaligned(key_len, 4) || misaligned(key_bits, 4)) return ATTN_E_ALIGN;
   st = check_device();
   if (st != ATTN_OK) return st;
 
@@ -831,20 +895,29 @@ extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, voi
   // far less than one fp32 ulp of exp2's result, i.e. the same uniform rows.
   a.c = std::fmax(std::fabs(scale) * kLog2e, 1.17549435e-38f);
   a.q_sign = scale < 0.f ? 0x80008000u : 0u;
+  a.heads = H;
+  a.key_len = key_len;
+  a.key_bits = key_bits;
 
   void* args[] = {&a};
-  const void* fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal>)
-                          : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull>);
+  const void* fn;
+  if (key_bits)
+    fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal, true>)
+                : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, true>);
+  else
+    fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal, false>)
+                : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, false>);
   const hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles), dim3(waves * 64), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
-extern "C" attn_status attn_fwd_fp32(const float* q, const float* k, const float* v, float* o,
-                                     float* lse, int B, int H, int N, int d, float scale,
-                                     int causal, void* stream) {
+attn_status launch_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
+                        int B, int H, int N, int d, float scale, int causal, const int* key_len,
+                        const uint32_t* key_bits, void* stream) {
   attn_status st = validate(q, k, v, o, lse, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
+  if (misaligned(key_len, 4) || misaligned(key_bits, 4)) return ATTN_E_ALIGN;
   st = check_device();
   if (st != ATTN_OK) return st;
 
@@ -858,9 +931,60 @@ extern "C" attn_status attn_fwd_fp32(const float* q, const float* k, const float
   a.q_tiles = (N + 63) / 64;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
+  a.heads = H;
+  a.key_len = key_len;
+  a.key_bits = key_bits;
   void* args[] = {&a};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_f32_kernel),
                                        dim3(B * H * a.q_tiles), dim3(64), args, 0,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int N, int d, float scale, int causal,
+                                void* stream) {
+  return launch_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, nullptr, stream);
+}
+
+extern "C" attn_status attn_fwd_fp32(const float* q, const float* k, const float* v, float* o,
+                                     float* lse, int B, int H, int N, int d, float scale,
+                                     int causal, void* stream) {
+  return launch_fp32(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, nullptr, stream);
+}
+
+extern "C" attn_status attn_fwd_masked(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int B, int H, int N, int d, float scale,
+                                       int causal, const int* key_len, const unsigned* key_bits,
+                                       void* stream) {
+  return launch_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, key_bits, stream);
+}
+
+extern "C" attn_status attn_fwd_fp32_masked(const float* q, const float* k, const float* v,
+                                            float* o, float* lse, int B, int H, int N, int d,
+                                            float scale, int causal, const int* key_len,
+                                            const unsigned* key_bits, void* stream) {
+  return launch_fp32(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, key_bits, stream);
+}
+
+extern "C" attn_status attn_pack_key_mask(const unsigned char* key_valid, unsigned* key_bits,
+                                          int B, int N, void* stream) {
+  if (!key_valid || !key_bits || B < 1 || N < 1) return ATTN_E_INVALID;
+  if ((long long)B * N >= (1LL << 31)) return ATTN_E_INVALID;
+  if (misaligned(key_bits, 4)) return ATTN_E_ALIGN;
+  const attn_status st = check_device();
+  if (st != ATTN_OK) return st;
+  const int words = (N + 31) / 32;
+  const long long total = (long long)B * words;
+  const int blocks = (int)((total + 255) / 256);
+  const uint8_t* kv = key_valid;
+  uint32_t* kb = key_bits;
+  int n = N;
+  void* args[] = {&kv, &kb, &n, (void*)&words, (void*)&total};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_pack_key_mask_kernel),
+                                       dim3(blocks), dim3(256), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }

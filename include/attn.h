@@ -31,7 +31,7 @@
  *   - scale: any finite float; scale < 0 is allowed.  The usual choice is
  *     1/sqrt(d).
  *   - causal: 0 = every query sees all N keys; non-zero = query i sees keys
- *     0..i (the diagonal included, so no row is empty).
+ *     0..i (the diagonal included, so no row is empty without a key mask).
  *   - Numerics: scores, the online softmax and both products accumulate in
  *     fp32.  Non-finite inputs are not scrubbed; they propagate as the
  *     definition says.
@@ -86,6 +86,56 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o,
 attn_status attn_fwd_fp32(const float *q, const float *k, const float *v,
                           float *o, float *lse, int B, int H, int N, int d,
                           float scale, int causal, void *stream);
+
+/*
+ * attn_fwd_masked: attn_fwd with a key-padding mask.  The Qiita page on the
+ * patch-attention layer ("flash-attnの代役がVRAMを18GB溶かしていたので87%削った
+ * 話"), sections 4 and 6, describes the mask as a per-key additive bias: 0
+ * for a key that takes part, -inf for a padded key, the same for every query
+ * of a batch entry.  Two forms, either or both (a key must pass both):
+ *   key_len  : const int [B] device array, or NULL.  Key j of batch entry b
+ *              takes part only when j < key_len[b] (the usual right
+ *              padding).  Values are clamped to [0, N].  4-byte aligned.
+ *              This form costs nothing: it only shortens the key loop.
+ *   key_bits : const unsigned [B][ceil(N/32)] device array, or NULL: bit
+ *              j % 32 of word j / 32 of row b set = key j of entry b takes
+ *              part (bits past N are ignored).  4-byte aligned.  Any
+ *              pattern is allowed; attn_pack_key_mask builds it from one
+ *              byte per key.  Every key tile then takes the masked path.
+ * Causal masking, when asked for, applies on top.
+ * A query row that sees no key at all (every key padded) gets O = 0 and
+ * LSE = -inf: its row sum is the empty sum.  These are the values under
+ * which the blockwise combination of the FlashAttention reading notes
+ * (section "proposed method") leaves another key set's result unchanged.
+ * With both masks NULL this is exactly attn_fwd.  Errors as attn_fwd, plus
+ * ATTN_E_ALIGN for a key_len or key_bits not 4-byte aligned.
+ */
+attn_status attn_fwd_masked(const void *q, const void *k, const void *v,
+                            void *o, float *lse, int B, int H, int N, int d,
+                            float scale, int causal, const int *key_len,
+                            const unsigned *key_bits, void *stream);
+
+/* attn_fwd_masked for fp32 tensors: attn_fwd_fp32 with the same two mask
+ * forms and the same empty-row result. */
+attn_status attn_fwd_fp32_masked(const float *q, const float *k,
+                                 const float *v, float *o, float *lse, int B,
+                                 int H, int N, int d, float scale, int causal,
+                                 const int *key_len, const unsigned *key_bits,
+                                 void *stream);
+
+/*
+ * attn_pack_key_mask: one byte per key -> the bit form attn_fwd_masked
+ * reads.  key_valid: const unsigned char [B][N] device array (non-zero =
+ * the key takes part); key_bits: unsigned [B][ceil(N/32)] device array,
+ * 4-byte aligned, written in full (bits past N are 0).  Enqueued on
+ * `stream` like the attention calls; the caller owns both buffers.
+ * ATTN_E_INVALID for a null pointer, B or N below 1 or B*N >= 2^31;
+ * ATTN_E_ALIGN for a misaligned key_bits; ATTN_E_DEVICE, ATTN_E_LAUNCH as
+ * attn_fwd.
+ */
+attn_status attn_pack_key_mask(const unsigned char *key_valid,
+                               unsigned *key_bits, int B, int N,
+                               void *stream);
 
 /* Static, human-readable text for a status code; never NULL. */
 const char *attn_strerror(attn_status status);

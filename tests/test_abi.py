@@ -50,17 +50,48 @@ def test_strerror_covers_every_status():
 ALIGNED = 0x100000  # a fake, 16-byte aligned address; never dereferenced
 
 
+MASKED = ("attn_fwd_masked", "attn_fwd_fp32_masked")
+
+
 def call(fn, **kw):
     args = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, o=ALIGNED, lse=ALIGNED,
-                B=1, H=1, N=8, d=64, scale=0.125, causal=0, stream=None)
+                B=1, H=1, N=8, d=64, scale=0.125, causal=0, key_len=None, key_bits=None,
+                stream=None)
     args.update(kw)
     lib = ea.load_library()
-    return getattr(lib, fn)(args["q"], args["k"], args["v"], args["o"], args["lse"],
-                            args["B"], args["H"], args["N"], args["d"], args["scale"],
-                            args["causal"], args["stream"])
+    head = (args["q"], args["k"], args["v"], args["o"], args["lse"],
+            args["B"], args["H"], args["N"], args["d"], args["scale"], args["causal"])
+    if fn in MASKED:
+        return getattr(lib, fn)(*head, args["key_len"], args["key_bits"], args["stream"])
+    return getattr(lib, fn)(*head, args["stream"])
 
 
-@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_fp32"])
+ALL_FWD = ["attn_fwd", "attn_fwd_fp32", *MASKED]
+
+
+@pytest.mark.parametrize("fn", MASKED)
+def test_masked_validation(fn):
+    # misaligned key_len or key_bits are refused before any device check
+    assert call(fn, key_len=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    assert call(fn, key_bits=ALIGNED + 1) == ea.ATTN_E_ALIGN
+    assert call(fn, q=None, key_len=ALIGNED) == ea.ATTN_E_INVALID
+    assert call(fn, N=0, key_bits=ALIGNED) == ea.ATTN_E_INVALID
+
+
+def test_pack_key_mask_validation():
+    lib = ea.load_library()
+    assert lib.attn_pack_key_mask(None, ALIGNED, 1, 8, None) == ea.ATTN_E_INVALID
+    assert lib.attn_pack_key_mask(ALIGNED, None, 1, 8, None) == ea.ATTN_E_INVALID
+    assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 0, 8, None) == ea.ATTN_E_INVALID
+    assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 1, 0, None) == ea.ATTN_E_INVALID
+    assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 1 << 16, 1 << 15, None) == ea.ATTN_E_INVALID
+    assert lib.attn_pack_key_mask(ALIGNED + 1, ALIGNED + 2, 1, 8, None) == ea.ATTN_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.attn_pack_key_mask(ALIGNED + 1, ALIGNED, 2, 33, None) == ea.ATTN_E_DEVICE
+
+
+@pytest.mark.parametrize("fn", ALL_FWD)
 @pytest.mark.parametrize("bad, status", [
     (dict(q=None), ea.ATTN_E_INVALID),
     (dict(lse=None), ea.ATTN_E_INVALID),
@@ -81,13 +112,15 @@ def test_validation_rejects(fn, bad, status):
     assert call(fn, **bad) == status
 
 
-@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_fp32"])
+@pytest.mark.parametrize("fn", ALL_FWD)
 def test_valid_arguments_without_a_gpu_report_no_device(fn):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert call(fn) == ea.ATTN_E_DEVICE
     assert call(fn, lse=ALIGNED + 4, causal=1, scale=-0.5, N=1) == ea.ATTN_E_DEVICE
+    if fn in MASKED:
+        assert call(fn, key_len=ALIGNED + 4, key_bits=ALIGNED + 8) == ea.ATTN_E_DEVICE
 
 
 def test_binding_raises_without_compute_on_cpu_tensors():
