@@ -226,15 +226,24 @@ def cpu_baseline(w, q, k, v, seconds):
     }
 
 
-def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=False, mask="none"):
+def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=False, mask="none",
+              layout="contiguous"):
     import torch
     import exact_attention_29_amd as ea
     from workloads import make_inputs
 
     dev = "cuda:0"
     q, k, v = make_inputs(w)
-    qd, kd, vd = (t.to(dev) for t in (q, k, v))
     B, H, N, d = w.shape
+    if layout == "packed":
+        # the same values in one [B, N, 3*H*d] input-projection output, read
+        # in place through head views (attn_fwd_strided)
+        x = torch.empty(B, N, 3 * H * d, dtype=q.dtype, device=dev)
+        qd, kd, vd = (t.view(B, N, H, d).transpose(1, 2) for t in x.chunk(3, dim=-1))
+        for dst, src in ((qd, q), (kd, k), (vd, v)):
+            dst.copy_(src.to(dev))
+    else:
+        qd, kd, vd = (t.to(dev) for t in (q, k, v))
     o = torch.empty_like(qd)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -297,6 +306,8 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
             "workload": f"{w.name}: {w.what}",
             "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "scale": w.scale,
             "inputs": f"i.i.d. N(0,{w.sigma}^2), seed {w.seed}",
+            "layout": {"contiguous": "[B,H,N,d] contiguous",
+                       "packed": "head views of one packed [B,N,3*H*d] projection (attn_fwd_strided)"}[layout],
             "key_mask": {"none": "none", "len": "key_len = N per entry (attn_fwd_masked)",
                          "bytes": "key mask all true, packed to bits (attn_fwd_masked, mask path)"}[mask],
             "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
@@ -400,6 +411,8 @@ def main():
     ap.add_argument("--cold", type=int, default=30,
                     help="launches timed with flushed caches after the warm steps (0: skip)")
     ap.add_argument("--no-clock", action="store_true", help="do not sample the clock with amd-smi")
+    ap.add_argument("--layout", choices=["contiguous", "packed"], default="contiguous",
+                    help="read q, k, v as head views of one packed projection output")
     ap.add_argument("--mask", choices=["none", "len", "bytes"], default="none",
                     help="time attn_fwd_masked with every key valid, as a length or a byte mask")
     ap.add_argument("--workspace-sweep", action="store_true",
@@ -444,15 +457,16 @@ def main():
         cases += [WORKLOADS["patch_3mp"], WORKLOADS["patch_8mp"]]
         from dataclasses import replace
         cases.append(replace(WORKLOADS["patch_3mp"], causal=True, name="patch_3mp_causal"))
-        cases = [(c, "none") for c in cases]
-        cases += [(WORKLOADS["patch_3mp"], "len"), (WORKLOADS["patch_3mp"], "bytes"),
-                  (WORKLOADS["bert_large"], "bytes")]
+        cases = [(c, "none", "contiguous") for c in cases]
+        cases += [(WORKLOADS["patch_3mp"], "len", "contiguous"), (WORKLOADS["patch_3mp"], "bytes", "contiguous"),
+                  (WORKLOADS["bert_large"], "bytes", "contiguous"), (WORKLOADS["patch_3mp"], "none", "packed"),
+                  (WORKLOADS["patch_8mp"], "none", "packed")]
         with open(args.sweep, "w") as f:
-            for w, mask in cases:
+            for w, mask, layout in cases:
                 steps = max(args.steps, 200) if w.flops < 2e10 else args.steps
                 warm = max(args.warmup, 1000) if w.flops < 2e10 else args.warmup
-                log(f"[bench] {w.name} {w.shape} causal={w.causal} mask={mask}")
-                line = bench_one(w, steps, warm, False, 0, mask=mask)
+                log(f"[bench] {w.name} {w.shape} causal={w.causal} mask={mask} layout={layout}")
+                line = bench_one(w, steps, warm, False, 0, mask=mask, layout=layout)
                 f.write(json.dumps(line) + "\n")
                 f.flush()
                 log(f"[bench] {w.name}: {line['value']} TFLOP/s, kernel {line['roofline']['kernel_ms']} ms")
@@ -466,7 +480,8 @@ def main():
         w = replace(w, causal=args.causal == "yes")
     log(f"[bench] {w.name} {w.shape} {w.dtype} causal={w.causal} steps={args.steps} warmup={args.warmup}")
     line = bench_one(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds,
-                     cold_launches=args.cold, clock=not args.no_clock, mask=args.mask)
+                     cold_launches=args.cold, clock=not args.no_clock, mask=args.mask,
+                     layout=args.layout)
     print(json.dumps(line), flush=True)
 
 

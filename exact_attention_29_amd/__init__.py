@@ -1,8 +1,8 @@
 """Exact attention forward on MI355X: a thin Python binding over libattn.so.
 
 The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
-``attn_fwd_fp32_masked``, ``attn_pack_key_mask`` and ``attn_strerror`` carry
-the names and arguments
+``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_pack_key_mask`` and
+``attn_strerror`` carry the names and arguments
 of the C entry points declared in include/attn.h and only marshal arguments;
 every step of the computation runs in the HIP kernels.
 ``forward`` is a convenience wrapper that allocates the outputs with torch
@@ -16,7 +16,7 @@ import os
 import torch  # imported first: the library then binds to torch's HIP runtime
 
 __all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-           "attn_pack_key_mask", "attn_strerror", "forward", "pack_key_mask", "AttnError",
+           "attn_fwd_strided", "attn_pack_key_mask", "AttnLayout", "attn_strerror", "forward", "pack_key_mask", "AttnError",
            "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -24,8 +24,13 @@ _LIB_PATH = os.path.join(_PKG, "libattn.so")
 _lib = None
 
 ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH = range(5)
-EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked", "attn_pack_key_mask",
-            "attn_strerror")
+EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked", "attn_fwd_strided",
+            "attn_pack_key_mask", "attn_strerror")
+
+
+class AttnLayout(ctypes.Structure):
+    """attn_layout: element strides (batch, head, row) of a [B, H, N, d] tensor."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("row", ctypes.c_longlong)]
 
 
 class AttnError(RuntimeError):
@@ -59,6 +64,10 @@ def load_library():
     lib.attn_fwd_masked.restype = i32
     lib.attn_fwd_fp32_masked.argtypes = msig
     lib.attn_fwd_fp32_masked.restype = i32
+    lay = ctypes.POINTER(AttnLayout)
+    lib.attn_fwd_strided.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32,
+                                     lay, lay, lay, lay, ptr, ptr, ptr]
+    lib.attn_fwd_strided.restype = i32
     lib.attn_pack_key_mask.argtypes = [ptr, ptr, i32, i32, ptr]
     lib.attn_pack_key_mask.restype = i32
     lib.attn_strerror.argtypes = [i32]
@@ -98,6 +107,15 @@ def attn_fwd_fp32_masked(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, ke
                                                key_len, key_bits, stream))
 
 
+def attn_fwd_strided(q, k, v, o, lse, B, H, N, d, scale, causal, q_layout, k_layout, v_layout,
+                     o_layout, key_len, key_bits, stream):
+    """C entry point attn_fwd_strided: raw addresses; layouts are AttnLayout or None (contiguous)."""
+    ref = lambda l: None if l is None else ctypes.byref(l)  # noqa: E731
+    _check(load_library().attn_fwd_strided(q, k, v, o, lse, B, H, N, d, float(scale), int(bool(causal)),
+                                           ref(q_layout), ref(k_layout), ref(v_layout), ref(o_layout),
+                                           key_len, key_bits, stream))
+
+
 def attn_pack_key_mask(key_valid, key_bits, B, N, stream):
     """C entry point attn_pack_key_mask: raw addresses of the byte mask and the bit words."""
     _check(load_library().attn_pack_key_mask(key_valid, key_bits, B, N, stream))
@@ -120,19 +138,30 @@ def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _layout(t):
+    """AttnLayout of a [B, H, N, d] tensor view with contiguous features."""
+    sb, sh, sn, sf = t.stride()
+    if sf != 1:
+        raise ValueError("the d features of q, k, v and out must be contiguous (stride 1)")
+    return AttnLayout(sb, sh, sn)
+
+
 def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None, key_valid=None,
             key_bits=None):
-    """O, LSE for contiguous [B, H, N, d] tensors on one device.
+    """O, LSE for [B, H, N, d] tensors on one device.
 
     bf16 tensors use attn_fwd, fp32 tensors attn_fwd_fp32.  ``scale``
     defaults to 1/sqrt(d).  ``out`` and ``lse`` may be given to reuse buffers.
+    bf16 q, k, v and out may be strided views (features contiguous, every
+    stride a multiple of 8 elements), e.g. head views of one packed input
+    projection; then attn_fwd_strided reads them in place.
     Key padding: ``key_len`` an int32 [B] tensor (keys j >= key_len[b] take no
     part) and/or ``key_valid`` a bool or uint8 [B, N] tensor (key j of entry b
     takes part where it is True / non-zero; packed to bits by
-    attn_pack_key_mask first) or ``key_bits`` the packed int32 [B, ceil(N/32)]
-    words, all on the same device; then the masked entry points are called.  Rows that see no key get O = 0 and
-    LSE = -inf.  Launches on torch's current stream and returns without
-    synchronising.
+    attn_pack_key_mask first) or ``key_bits`` the packed int32
+    [B, ceil(N/32)] words, all on the same device; then the masked entry
+    points are called.  Rows that see no key get O = 0 and LSE = -inf.
+    Launches on torch's current stream and returns without synchronising.
     """
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k, v must share one dtype")
@@ -140,33 +169,28 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
         raise TypeError(f"unsupported dtype {q.dtype}; use bfloat16 or float32")
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one 4-D shape [B, H, N, d]")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous [B, H, N, d]")
     if not (q.is_cuda and k.device == q.device and v.device == q.device):
         raise ValueError("q, k, v must live on one GPU")
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must be a [B, H, N, d] tensor like q")
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous tensor like q")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    strided = not all(t.is_contiguous() for t in (q, k, v, out))
+    if strided and q.dtype != torch.bfloat16:
+        raise ValueError("fp32 q, k, v and out must be contiguous [B, H, N, d]")
     if key_valid is not None:
         if key_bits is not None:
             raise ValueError("give key_valid or key_bits, not both")
         if key_valid.shape != (B, N) or key_valid.device != q.device:
             raise ValueError("key_valid must be a [B, N] tensor on q's device")
         key_bits = pack_key_mask(key_valid)
-    if key_len is None and key_bits is None:
-        fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_fp32
-        with torch.cuda.device(q.device):
-            fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-               B, H, N, d, scale, causal, _stream_handle(q.device))
-        return out, lse
     kl_ptr = kv_ptr = 0
     if key_len is not None:
         if key_len.dtype != torch.int32 or key_len.shape != (B,) or not key_len.is_contiguous() \
@@ -178,8 +202,16 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
                 or not key_bits.is_contiguous() or key_bits.device != q.device:
             raise ValueError("key_bits must be a contiguous int32 [B, ceil(N/32)] tensor on q's device")
         kv_ptr = key_bits.data_ptr()
-    fn = attn_fwd_masked if q.dtype == torch.bfloat16 else attn_fwd_fp32_masked
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
-        fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-           B, H, N, d, scale, causal, kl_ptr, kv_ptr, _stream_handle(q.device))
+        stream = _stream_handle(q.device)
+        if strided:
+            attn_fwd_strided(*ptrs, B, H, N, d, scale, causal, _layout(q), _layout(k), _layout(v),
+                             _layout(out), kl_ptr, kv_ptr, stream)
+        elif kl_ptr or kv_ptr:
+            fn = attn_fwd_masked if q.dtype == torch.bfloat16 else attn_fwd_fp32_masked
+            fn(*ptrs, B, H, N, d, scale, causal, kl_ptr, kv_ptr, stream)
+        else:
+            fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_fp32
+            fn(*ptrs, B, H, N, d, scale, causal, stream)
     return out, lse

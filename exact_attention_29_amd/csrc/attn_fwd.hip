@@ -111,6 +111,10 @@ struct Bf16Args {
   float c;          // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign;  // 0x80008000 when scale < 0 (Q negated), else 0
   int heads;        // H: batch entry of head bh is bh / H
+  // element strides of q, k, v, o (index 0..3) between batch entries, heads
+  // and rows; the 64 features of a row are contiguous
+  long long sb[4], sh[4];
+  int sn[4];
   const int* key_len;         // [B] or null: keys j >= key_len[b] are hidden
   const uint32_t* key_bits;   // [B][ceil(N/32)] or null: bit j%32 of word j/32
                               // clear hides key j of entry b
@@ -236,10 +240,13 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const int bh = logical / a.q_tiles;
   int qt = logical - bh * a.q_tiles;
   if (kCausal) qt = a.q_tiles - 1 - qt;  // longest rows first
-  const size_t head = (size_t)bh * n * kD;
-  const uint16_t* __restrict__ qg = a.q + head;
-  const uint16_t* __restrict__ kg = a.k + head;
-  const uint16_t* __restrict__ vg = a.v + head;
+  const int b_entry = bh / a.heads;
+  const int h_idx = bh - b_entry * a.heads;
+  auto head_off = [&](int t) { return (size_t)(b_entry * a.sb[t] + h_idx * a.sh[t]); };
+  const uint16_t* __restrict__ qg = a.q + head_off(0);
+  const uint16_t* __restrict__ kg = a.k + head_off(1);
+  const uint16_t* __restrict__ vg = a.v + head_off(2);
+  const int q_sn = a.sn[0], k_sn = a.sn[1], v_sn = a.sn[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -255,14 +262,13 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (qi < n) w = *(const u32x4*)(qg + (size_t)qi * kD + 16 * ks + 8 * hi);
+    if (qi < n) w = *(const u32x4*)(qg + (size_t)qi * q_sn + 16 * ks + 8 * hi);
     w ^= a.q_sign;
     qop[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
   // ---- key range.  n_k: keys of this batch entry that may be visible (a
   // per-entry valid length hides the rest, like keys past the end).
-  const int b_entry = bh / a.heads;
   const int n_k = a.key_len ? min(max(a.key_len[b_entry], 0), n) : n;
   int kv_end = n_k;
   if (kCausal) kv_end = min(n_k, qt * kBr + kBr);
@@ -285,34 +291,38 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const int dma_row = 8 * wave + (lane >> 3);
   const int dma_chunk = (lane & 7) ^ swz(dma_row);
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const unsigned dma_lane_off = (unsigned)(dma_row * kRow + dma_chunk * 16);
+  // byte offsets of this lane's chunk within a K and a V tile (row strides
+  // in bytes: 2 * k_sn, 2 * v_sn; the host keeps every offset below 2^31)
+  const int k_lane_off = dma_row * 2 * k_sn + dma_chunk * 16;
+  const int v_lane_off = dma_row * 2 * v_sn + dma_chunk * 16;
   // Buffer resources over this head's K and V: a whole tile is fetched with
   // the tile's byte offset in a scalar register and this lane's constant
   // offset, so the steady state spends no vector instruction on addresses.
-  const int head_bytes = (int)((unsigned)n * (unsigned)kRow);
+  const int k_bytes = (n - 1) * 2 * k_sn + kRow;
+  const int v_bytes = (n - 1) * 2 * v_sn + kRow;
   const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, head_bytes, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, k_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_bytes, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, v_bytes, kBufferWord3);
   auto dma_tile = [&](int kt, char* stage_base) {
     char* kd = stage_base + wave_s * 1024;
     if ((kt + 1) * kBc <= n) {
 #pragma unroll
       for (int ps = 0; ps < kDmaPasses; ++ps) {
-        const int off = kt * kTileBytes + ps * kPassBytes;
+        const int row0 = kt * kBc + ps * kPassRows;  // first row of this pass
         __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void*)(kd + ps * kPassBytes),
-                                                 16, (int)dma_lane_off, off, 0, 0);
+                                                 16, k_lane_off, row0 * 2 * k_sn, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc,
                                                  (__attribute__((address_space(3))) void*)(kd + kTileBytes + ps * kPassBytes),
-                                                 16, (int)dma_lane_off, off, 0, 0);
+                                                 16, v_lane_off, row0 * 2 * v_sn, 0, 0);
       }
     } else {
       // ragged last tile: rows past N re-read row N-1
 #pragma unroll
       for (int ps = 0; ps < kDmaPasses; ++ps) {
         const int key = min(kt * kBc + dma_row + ps * kPassRows, n - 1);
-        const uint16_t* ks = kg + (size_t)key * kD + dma_chunk * 8;
-        const uint16_t* vs = vg + (size_t)key * kD + dma_chunk * 8;
+        const uint16_t* ks = kg + (size_t)key * k_sn + dma_chunk * 8;
+        const uint16_t* vs = vg + (size_t)key * v_sn + dma_chunk * 8;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ks,
                                          (__attribute__((address_space(3))) void*)(kd + ps * kPassBytes), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vs,
@@ -668,7 +678,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           u32x4 w = {0u, 0u, 0u, 0u};
-          if (key < n) w = *(const u32x4*)(kg + (size_t)key * kD + 16 * ks + 8 * hi);
+          if (key < n) w = *(const u32x4*)(kg + (size_t)key * k_sn + 16 * ks + 8 * hi);
           kop[ks] = __builtin_bit_cast(bf16x8, w);
         }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[0], zero16, 0, 0, 0);
@@ -694,7 +704,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int key = 32 * j + 16 * tt + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const uint16_t bits = key < n ? vg[(size_t)key * kD + 32 * db + l32] : (uint16_t)0;
+            const uint16_t bits = key < n ? vg[(size_t)key * v_sn + 32 * db + l32] : (uint16_t)0;
             vop[i] = __builtin_bit_cast(__bf16, bits);
           }
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[tt], acc[db], 0, 0, 0);
@@ -708,7 +718,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const float l_tot = half_swap_sum(l_run);
   if (qi < n) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = a.o + head + (size_t)qi * kD;
+    uint16_t* orow = a.o + head_off(3) + (size_t)qi * a.sn[3];
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -870,12 +880,46 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
   return ATTN_OK;
 }
 
+// Element strides (batch, head, row) of the four tensors, checked: every
+// stride a multiple of 8 elements (16 bytes; the kernel moves 16-byte
+// chunks), none negative, o's rows at least 64 apart, and every byte offset
+// the K/V buffer loads form below 2^31.  NULL layouts are the contiguous
+// [B][H][N][64] one.
+attn_status check_layouts(const attn_layout* const lay[4], int H, int N, long long sb[4],
+                          long long sh[4], int sn[4]) {
+  for (int t = 0; t < 4; ++t) {
+    if (!lay[t]) {
+      sn[t] = kD;
+      sh[t] = (long long)N * kD;
+      sb[t] = (long long)H * N * kD;
+      continue;
+    }
+    const attn_layout& l = *lay[t];
+    if (l.batch < 0 || l.head < 0 || l.row < 0) return ATTN_E_INVALID;
+    if ((l.batch | l.head | l.row) & 7) return ATTN_E_ALIGN;
+    if (l.row > (1LL << 24)) return ATTN_E_INVALID;
+    sb[t] = l.batch;
+    sh[t] = l.head;
+    sn[t] = (int)l.row;
+  }
+  if (sn[3] < kD) return ATTN_E_INVALID;  // o's rows must not overlap
+  for (int t = 1; t <= 2; ++t)
+    if ((long long)(N - 1) * 2 * sn[t] + kRow >= (1LL << 31)) return ATTN_E_INVALID;
+  return ATTN_OK;
+}
+
 attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                         int H, int N, int d, float scale, int causal, const int* key_len,
-                        const uint32_t* key_bits, void* stream) {
+                        const uint32_t* key_bits, void* stream,
+                        const attn_layout* const layouts[4] = nullptr) {
   attn_status st = validate(q, k, v, o, lse, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
   if (misaligned(key_len, 4) || misaligned(key_bits, 4)) return ATTN_E_ALIGN;
+  long long sb[4], sh[4];
+  int sn[4];
+  const attn_layout* const none[4] = {nullptr, nullptr, nullptr, nullptr};
+  st = check_layouts(layouts ? layouts : none, H, N, sb, sh, sn);
+  if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
 
@@ -896,6 +940,11 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
   a.c = std::fmax(std::fabs(scale) * kLog2e, 1.17549435e-38f);
   a.q_sign = scale < 0.f ? 0x80008000u : 0u;
   a.heads = H;
+  for (int t = 0; t < 4; ++t) {
+    a.sb[t] = sb[t];
+    a.sh[t] = sh[t];
+    a.sn[t] = sn[t];
+  }
   a.key_len = key_len;
   a.key_bits = key_bits;
 
@@ -967,6 +1016,16 @@ extern "C" attn_status attn_fwd_fp32_masked(const float* q, const float* k, cons
                                             float scale, int causal, const int* key_len,
                                             const unsigned* key_bits, void* stream) {
   return launch_fp32(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, key_bits, stream);
+}
+
+extern "C" attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, int B, int H, int N, int d, float scale,
+                                        int causal, const attn_layout* q_layout,
+                                        const attn_layout* k_layout, const attn_layout* v_layout,
+                                        const attn_layout* o_layout, const int* key_len,
+                                        const unsigned* key_bits, void* stream) {
+  const attn_layout* const layouts[4] = {q_layout, k_layout, v_layout, o_layout};
+  return launch_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, key_bits, stream, layouts);
 }
 
 extern "C" attn_status attn_pack_key_mask(const unsigned char* key_valid, unsigned* key_bits,

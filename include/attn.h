@@ -124,6 +124,48 @@ attn_status attn_fwd_fp32_masked(const float *q, const float *k,
                                  void *stream);
 
 /*
+ * Element strides of one [B][H][N][d] tensor whose d features are
+ * contiguous: element (b, h, n, f) sits at b*batch + h*head + n*row + f.
+ */
+typedef struct attn_layout {
+    long long batch;
+    long long head;
+    long long row;
+} attn_layout;
+
+/*
+ * attn_fwd_strided: attn_fwd_masked on strided tensors, so that Q, K and V
+ * can be read where an input projection left them.  The Qiita page on the
+ * patch-attention layer, section 4 (its CPU reproduction of the layer's
+ * sdpa path), shows the usual route: one packed projection writes
+ * [B][N][3][H][d], it is split into q, k, v, viewed per head and
+ * transposed to [B][H][N][d] for the sdpa call, which then needs contiguous
+ * copies or strided reads.  With
+ * layouts q = {N*3*H*d, d, 3*H*d}, k and v the same (their base pointers d*H
+ * and 2*d*H elements further), this call reads the projection output as it
+ * is.  o may be strided too (e.g. [B][N][H][d] for the output projection);
+ * lse stays contiguous [B][H][N].
+ *   *_layout : element strides of q, k, v, o, or NULL for the contiguous
+ *              [B][H][N][d] layout.  Every stride must be >= 0 and a
+ *              multiple of 8 elements (16 bytes), o's row stride at least
+ *              d, and (N-1) * row * 2 + 128 below 2^31 for k and v
+ *              (ATTN_E_ALIGN / ATTN_E_INVALID otherwise).  Zero head or
+ *              batch strides are allowed for q, k, v (one K/V shared by
+ *              several heads); o's rows must not overlap each other (not
+ *              checked beyond the row stride).
+ *   key_len, key_bits : as attn_fwd_masked (NULL for none).
+ * With all layouts NULL this is exactly attn_fwd_masked.
+ */
+attn_status attn_fwd_strided(const void *q, const void *k, const void *v,
+                             void *o, float *lse, int B, int H, int N, int d,
+                             float scale, int causal,
+                             const attn_layout *q_layout,
+                             const attn_layout *k_layout,
+                             const attn_layout *v_layout,
+                             const attn_layout *o_layout, const int *key_len,
+                             const unsigned *key_bits, void *stream);
+
+/*
  * attn_pack_key_mask: one byte per key -> the bit form attn_fwd_masked
  * reads.  key_valid: const unsigned char [B][N] device array (non-zero =
  * the key takes part); key_bits: unsigned [B][ceil(N/32)] device array,

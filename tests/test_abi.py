@@ -67,6 +67,7 @@ def call(fn, **kw):
 
 
 ALL_FWD = ["attn_fwd", "attn_fwd_fp32", *MASKED]
+# attn_fwd_strided shares attn_fwd_masked's validation path; its own checks are below
 
 
 @pytest.mark.parametrize("fn", MASKED)
@@ -76,6 +77,27 @@ def test_masked_validation(fn):
     assert call(fn, key_bits=ALIGNED + 1) == ea.ATTN_E_ALIGN
     assert call(fn, q=None, key_len=ALIGNED) == ea.ATTN_E_INVALID
     assert call(fn, N=0, key_bits=ALIGNED) == ea.ATTN_E_INVALID
+
+
+def test_strided_validation():
+    lib = ea.load_library()
+
+    def strided(q_layout=None, k_layout=None, v_layout=None, o_layout=None, N=8, key_len=None):
+        lay = lambda t: None if t is None else ctypes.byref(ea.AttnLayout(*t))  # noqa: E731
+        return lib.attn_fwd_strided(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, N, 64, 0.125, 0,
+                                    lay(q_layout), lay(k_layout), lay(v_layout), lay(o_layout),
+                                    key_len, None, None)
+    assert strided(q_layout=(0, 64, -64)) == ea.ATTN_E_INVALID        # negative stride
+    assert strided(k_layout=(4096, 64, 196)) == ea.ATTN_E_ALIGN       # row not 16-byte multiple
+    assert strided(v_layout=(4096, 12, 192)) == ea.ATTN_E_ALIGN       # head not 16-byte multiple
+    assert strided(o_layout=(4096, 8, 56)) == ea.ATTN_E_INVALID       # o rows would overlap
+    assert strided(k_layout=(0, 0, 1 << 23), N=200) == ea.ATTN_E_INVALID  # K offsets >= 2^31
+    assert strided(key_len=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert strided() == ea.ATTN_E_DEVICE
+        assert strided(q_layout=(8192, 64, 128), k_layout=(0, 0, 64), o_layout=(8192, 64, 128)) \
+            == ea.ATTN_E_DEVICE
 
 
 def test_pack_key_mask_validation():
