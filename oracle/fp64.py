@@ -25,6 +25,13 @@ of two disjoint key sets (the combination rule of the FlashAttention reading
 notes, section "proposed method": m = max(m1, m2), l = e^(m1-m) l1 +
 e^(m2-m) l2) leaves the other set's result unchanged when one set is empty.
 
+Optional ``block_mask`` (M, bq, bk): the block-sparse variant of the
+FlashAttention reading notes, section "block-sparse FlashAttention": a
+predefined 0/1 matrix M over (query block, key block) pairs, query blocks of
+bq rows and key blocks of bk keys; only the blocks where M is 1 take part,
+i.e. key j is hidden from query i when M[i // bq][j // bk] = 0.  The same M
+serves every batch entry and head.  It combines with the other masks.
+
 LSE: the forward pass keeps, besides O, the softmax statistics m (row max)
 and l (row sum of exp(s - m)) for the backward pass (FlashAttention reading
 notes, section "recomputation").  They are returned folded into one number
@@ -58,6 +65,12 @@ def _visible(rows, n_keys, causal, key_valid):
     if key_valid is not None:
         vis &= key_valid[None, :]
     return vis
+
+
+def _block_visible(rows, n_keys, block_mask):
+    """bool [R, N]: M[i // bq][j // bk] for query rows[r] and key j."""
+    m, bq, bk = block_mask
+    return np.asarray(m, dtype=bool)[rows[:, None] // bq, np.arange(n_keys)[None, :] // bk]
 
 
 def _row_max(s):
@@ -107,7 +120,7 @@ def _f64(x):
 
 
 def attention(q, k, v, scale, causal=False, key_valid=None, rows=None,
-              row_chunk=512):
+              row_chunk=512, block_mask=None):
     """Exact attention forward, float64.
 
     q, k, v: arrays [B, H, N, d] (any real dtype; converted exactly to f64).
@@ -116,6 +129,8 @@ def attention(q, k, v, scale, causal=False, key_valid=None, rows=None,
     key_valid: optional bool [B, N]; False hides that key from every query.
     rows:    optional 1-D array of query indices, evaluated for every (b, h);
              default all N rows.  Lets large workloads be checked on a sample.
+    block_mask: optional (M, bq, bk): M a 0/1 array [ceil(N/bq), ceil(N/bk)];
+             key j is hidden from query i when M[i // bq][j // bk] == 0.
     Returns (o [B, H, R, d], lse [B, H, R]) in float64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -133,6 +148,8 @@ def attention(q, k, v, scale, causal=False, key_valid=None, rows=None,
                     r = rows[c0:c0 + row_chunk]
                     s = _scores(q[b, h, r], k[b, h], scale)
                     vis = _visible(r, N, causal, None if kv is None else kv[b])
+                    if block_mask is not None:
+                        vis &= _block_visible(r, N, block_mask)
                     s = np.where(vis, s, -np.inf)
                     empty = _empty_rows(vis)
                     m = _row_max(s)
@@ -147,7 +164,7 @@ def attention(q, k, v, scale, causal=False, key_valid=None, rows=None,
     return o, lse
 
 
-def attention_materialised(q, k, v, scale, causal=False, key_valid=None):
+def attention_materialised(q, k, v, scale, causal=False, key_valid=None, block_mask=None):
     """Standard attention with the full score and probability tables.
 
     This is the "standard attention" the FlashAttention reading notes contrast
@@ -163,6 +180,11 @@ def attention_materialised(q, k, v, scale, causal=False, key_valid=None):
         hide |= np.triu(np.ones((N, N), dtype=bool), k=1)[None, None]
     if key_valid is not None:
         hide |= ~np.asarray(key_valid, dtype=bool)[:, None, None, :]
+    if block_mask is not None:
+        m, bq, bk = block_mask
+        m = np.asarray(m, dtype=bool)
+        full = np.repeat(np.repeat(m, bq, axis=0), bk, axis=1)[:N, :N]
+        hide = hide | ~full[None, None]
     s = np.where(hide, -np.inf, s)
     with np.errstate(invalid="ignore", divide="ignore"):
         top = s.max(axis=-1, keepdims=True)

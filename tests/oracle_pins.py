@@ -273,6 +273,15 @@ def pin_materialised_brute_force():
             _close(o, ob, 1e-12, f"brute force O n={q.shape[2]} causal={causal}")
             _close(lse, lb, 1e-12, f"brute force LSE n={q.shape[2]} causal={causal}")
             _close(p.sum(axis=-1), np.ones(p.shape[:-1]), 1e-14 * q.shape[2], "rows of P")
+    # block masks: the materialised table with blocks cut out
+    q, k, v = (rng.standard_normal((2, 2, 37, 8)) for _ in range(3))
+    m = rng.random((5, 10)) < 0.6
+    m[:, 0] = True  # every row keeps a key
+    for causal in (False, True):
+        o, lse = O.attention(q, k, v, 0.3, causal=causal, block_mask=(m, 8, 4), row_chunk=9)
+        ob, lb, _ = O.attention_materialised(q, k, v, 0.3, causal=causal, block_mask=(m, 8, 4))
+        _close(o, ob, 1e-12, f"brute force block-sparse O causal={causal}")
+        _close(lse, lb, 1e-12, f"brute force block-sparse LSE causal={causal}")
 
 
 def pin_fsum_variant():
@@ -355,6 +364,52 @@ def pin_padding_prefix_uniform():
                 _close(lse[b, :, i], np.full(H, math.log(cnt)), 1e-12, f"padding LSE b={b} i={i}")
 
 
+def pin_block_sparse():
+    """Block-sparse attention (FlashAttention reading notes, section
+    "block-sparse FlashAttention") against facts that do not use it:
+    an all-ones M is dense attention; an M that gives each query block one
+    key block (a permutation) is dense attention of those rows against those
+    keys alone; and complementary masks M, 1-M merge (blockwise rule) into
+    the dense result."""
+    rng = _rng(23)
+    B, H, N, d = 2, 2, 40, 8
+    bq, bk = 8, 4
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    nbq, nbk = -(-N // bq), -(-N // bk)
+    dense_o, dense_l = O.attention(q, k, v, 0.5)
+    o, l = O.attention(q, k, v, 0.5, block_mask=(np.ones((nbq, nbk)), bq, bk))
+    _close(o, dense_o, 1e-12, "all-ones M O")
+    _close(l, dense_l, 1e-12, "all-ones M LSE")
+    # one key block per query block, a permutation c(i) != i: query block i
+    # (8 rows) sees exactly the 8 keys of block c(i), given at 8 x 8 and at
+    # 8 x 4 granularity (two 4-key blocks); equal to dense attention of those
+    # rows against those keys alone.  A small row chunk makes the block rows
+    # cross chunk boundaries (global query indices).
+    perm = [(3 * i + 1) % nbq for i in range(nbq)]
+    m88 = np.zeros((nbq, nbq), dtype=bool)
+    m84 = np.zeros((nbq, nbk), dtype=bool)
+    for i, c in enumerate(perm):
+        m88[i, c] = True
+        m84[i, 2 * c] = m84[i, 2 * c + 1] = True
+    for m, b_k in ((m88, 8), (m84, 4)):
+        o, l = O.attention(q, k, v, 0.5, block_mask=(m, bq, b_k), row_chunk=7)
+        for i, c in enumerate(perm):
+            rs, ks = slice(i * bq, (i + 1) * bq), slice(c * bq, (c + 1) * bq)
+            so, sl_l = O.attention(q[:, :, rs], k[:, :, ks], v[:, :, ks], 0.5)
+            _close(o[:, :, rs], so, 1e-12, f"permuted blocks O block {i} (bk={b_k})")
+            _close(l[:, :, rs], sl_l, 1e-12, f"permuted blocks LSE block {i} (bk={b_k})")
+    # complementary masks merge back to dense, causal or not
+    m = rng.random((nbq, nbk)) < 0.5
+    for causal in (False, True):
+        full_o, full_l = O.attention(q, k, v, 0.5, causal=causal)
+        oa, la = O.attention(q, k, v, 0.5, causal=causal, block_mask=(m, bq, bk), row_chunk=11)
+        ob, lb = O.attention(q, k, v, 0.5, causal=causal, block_mask=(~m, bq, bk), row_chunk=11)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            mo, ml = _merge(oa, la, ob, lb)
+        _close(mo, full_o, 1e-12, f"merged block-sparse O causal={causal}")
+        _close(ml, full_l, 1e-12, f"merged block-sparse LSE causal={causal}")
+
+
 INDEPENDENT_PINS = [
     pin_uniform_closed_form,
     pin_identity_closed_form,
@@ -368,6 +423,7 @@ INDEPENDENT_PINS = [
     pin_page_mask_example,
     pin_key_shard_merge,
     pin_padding_prefix_uniform,
+    pin_block_sparse,
 ]
 
 ALL_PINS = INDEPENDENT_PINS + [

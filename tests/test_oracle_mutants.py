@@ -45,6 +45,14 @@ MUTANTS = {
     "empty_rows_lse_zero": ("_empty_row_result", lambda o, lse, empty: (
         np.where(empty[:, None], 0.0, o), np.where(empty, 0.0, lse))),
     "empty_rows_uniform": ("_empty_row_result", lambda o, lse, empty: (o, lse)),
+    "block_mask_roles_swapped": ("_block_visible", lambda rows, n, bm: np.asarray(bm[0], dtype=bool)[
+        (np.arange(n)[None, :] // bm[2]) % np.asarray(bm[0]).shape[0],
+        (rows[:, None] // bm[1]) % np.asarray(bm[0]).shape[1]]),
+    "block_sizes_swapped": ("_block_visible", lambda rows, n, bm: np.asarray(bm[0], dtype=bool)[
+        (rows[:, None] // bm[2]) % np.asarray(bm[0]).shape[0], np.arange(n)[None, :] // bm[1]]),
+    "block_mask_ignored": ("_block_visible", lambda rows, n, bm: np.ones((len(rows), n), dtype=bool)),
+    "block_mask_local_rows": ("_block_visible", lambda rows, n, bm: np.asarray(bm[0], dtype=bool)[
+        (rows - rows[0])[:, None] // bm[1], np.arange(n)[None, :] // bm[2]]),
 }
 
 
