@@ -226,8 +226,19 @@ def cpu_baseline(w, q, k, v, seconds):
     }
 
 
+def sparse_flops(w, m):
+    """Algorithmic flops of a block-sparse call: 4*d per (query, key) pair of
+    every set (128-row, 64-key) block, clipped at N; non-causal only."""
+    import numpy as np
+    N = w.N
+    rows = np.minimum(128, N - 128 * np.arange(m.shape[0]))
+    keys = np.minimum(64, N - 64 * np.arange(m.shape[1]))
+    pairs = float((m * rows[:, None] * keys[None, :]).sum())
+    return 4.0 * w.B * w.H * pairs * w.d
+
+
 def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=False, mask="none",
-              layout="contiguous"):
+              layout="contiguous", block_density=None):
     import torch
     import exact_attention_29_amd as ea
     from workloads import make_inputs
@@ -255,6 +266,15 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     elif mask == "bytes":
         # packed once, outside the timed calls (attn_pack_key_mask)
         masks["key_bits"] = ea.pack_key_mask(torch.ones((B, N), dtype=torch.bool, device=dev))
+    flops = w.flops
+    if block_density is not None:
+        # a random block pattern with this fraction of (128-row, 64-key) blocks
+        # set; flops count only the set blocks
+        import numpy as np
+        rng = np.random.default_rng(1000)
+        m = rng.random((-(-N // 128), -(-N // 64))) < block_density
+        masks["block_mask"] = torch.from_numpy(m).to(dev)
+        flops = sparse_flops(w, m)
 
     # workspace: device memory a call needs beyond its outputs.  O and LSE
     # are allocated first (the allocator rounds blocks, so their own sizes
@@ -276,6 +296,11 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
         ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, **masks)
 
     wall, kern, per = time_gpu(step, steps, warmup, stream)
+    if block_density is not None:
+        # the same call without the block mask, for the time ratio
+        dense_masks = {kk: vv for kk, vv in masks.items() if kk != "block_mask"}
+        _, dense_kern, _ = time_gpu(lambda: ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o,
+                                                       lse=lse, **dense_masks), steps, warmup, stream)
     clock_info = None
     if clock:
         # amd-smi takes about a second per query: keep the GPU busy with the
@@ -285,7 +310,6 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
                 step()
             torch.cuda.synchronize()
         clock_info = clk.summary()
-    flops = w.flops
     value = flops / wall / 1e12
     achieved = flops / kern / 1e12
     traffic = traffic_for(w.name)
@@ -306,6 +330,11 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
             "workload": f"{w.name}: {w.what}",
             "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "scale": w.scale,
             "inputs": f"i.i.d. N(0,{w.sigma}^2), seed {w.seed}",
+            "block_sparse": None if block_density is None else {
+                "density_target": block_density, "blocks_set": int(masks["block_mask"].sum()),
+                "blocks": int(masks["block_mask"].numel()), "block": "128 queries x 64 keys",
+                "flops_counted": "set blocks only",
+                "time_vs_dense": round(kern / dense_kern, 4)},
             "layout": {"contiguous": "[B,H,N,d] contiguous",
                        "packed": "head views of one packed [B,N,3*H*d] projection (attn_fwd_strided)"}[layout],
             "key_mask": {"none": "none", "len": "key_len = N per entry (attn_fwd_masked)",
@@ -320,8 +349,10 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_fwd_bf16_kernel<%s, %s>" % ("true, 4" if w.causal else "false, 8",
-                                                        "true" if mask == "bytes" else "false"),
+            "kernel": ("attn_fwd_bf16_kernel<%s, 4, false, true>" % ("true" if w.causal else "false")
+                       if block_density is not None else
+                       "attn_fwd_bf16_kernel<%s, %s, false>" % ("true, 4" if w.causal else "false, 8",
+                                                                 "true" if mask == "bytes" else "false")),
             "kernel_ms": round(kern * 1e3, 4),
             "algorithmic_bytes": 4 * B * H * N * d * 2 + 4 * B * H * N,
         },
@@ -411,6 +442,8 @@ def main():
     ap.add_argument("--cold", type=int, default=30,
                     help="launches timed with flushed caches after the warm steps (0: skip)")
     ap.add_argument("--no-clock", action="store_true", help="do not sample the clock with amd-smi")
+    ap.add_argument("--block-density", type=float, default=None,
+                    help="time attn_fwd_block_sparse with this fraction of random blocks set")
     ap.add_argument("--layout", choices=["contiguous", "packed"], default="contiguous",
                     help="read q, k, v as head views of one packed projection output")
     ap.add_argument("--mask", choices=["none", "len", "bytes"], default="none",
@@ -457,16 +490,22 @@ def main():
         cases += [WORKLOADS["patch_3mp"], WORKLOADS["patch_8mp"]]
         from dataclasses import replace
         cases.append(replace(WORKLOADS["patch_3mp"], causal=True, name="patch_3mp_causal"))
-        cases = [(c, "none", "contiguous") for c in cases]
-        cases += [(WORKLOADS["patch_3mp"], "len", "contiguous"), (WORKLOADS["patch_3mp"], "bytes", "contiguous"),
-                  (WORKLOADS["bert_large"], "bytes", "contiguous"), (WORKLOADS["patch_3mp"], "none", "packed"),
-                  (WORKLOADS["patch_8mp"], "none", "packed")]
+        cases = [(c, "none", "contiguous", None) for c in cases]
+        cases += [(WORKLOADS["patch_3mp"], "len", "contiguous", None),
+                  (WORKLOADS["patch_3mp"], "bytes", "contiguous", None),
+                  (WORKLOADS["bert_large"], "bytes", "contiguous", None),
+                  (WORKLOADS["patch_3mp"], "none", "packed", None),
+                  (WORKLOADS["patch_8mp"], "none", "packed", None),
+                  (WORKLOADS["patch_3mp"], "none", "contiguous", 1.0),
+                  (WORKLOADS["patch_3mp"], "none", "contiguous", 0.5),
+                  (WORKLOADS["patch_3mp"], "none", "contiguous", 0.25),
+                  (WORKLOADS["patch_8mp"], "none", "contiguous", 0.25)]
         with open(args.sweep, "w") as f:
-            for w, mask, layout in cases:
+            for w, mask, layout, dens in cases:
                 steps = max(args.steps, 200) if w.flops < 2e10 else args.steps
                 warm = max(args.warmup, 1000) if w.flops < 2e10 else args.warmup
-                log(f"[bench] {w.name} {w.shape} causal={w.causal} mask={mask} layout={layout}")
-                line = bench_one(w, steps, warm, False, 0, mask=mask, layout=layout)
+                log(f"[bench] {w.name} {w.shape} causal={w.causal} mask={mask} layout={layout} density={dens}")
+                line = bench_one(w, steps, warm, False, 0, mask=mask, layout=layout, block_density=dens)
                 f.write(json.dumps(line) + "\n")
                 f.flush()
                 log(f"[bench] {w.name}: {line['value']} TFLOP/s, kernel {line['roofline']['kernel_ms']} ms")
@@ -481,7 +520,7 @@ def main():
     log(f"[bench] {w.name} {w.shape} {w.dtype} causal={w.causal} steps={args.steps} warmup={args.warmup}")
     line = bench_one(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds,
                      cold_launches=args.cold, clock=not args.no_clock, mask=args.mask,
-                     layout=args.layout)
+                     layout=args.layout, block_density=args.block_density)
     print(json.dumps(line), flush=True)
 
 

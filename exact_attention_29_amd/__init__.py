@@ -1,8 +1,8 @@
 """Exact attention forward on MI355X: a thin Python binding over libattn.so.
 
 The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
-``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_pack_key_mask`` and
-``attn_strerror`` carry the names and arguments
+``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_fwd_block_sparse``,
+``attn_pack_key_mask`` and ``attn_strerror`` carry the names and arguments
 of the C entry points declared in include/attn.h and only marshal arguments;
 every step of the computation runs in the HIP kernels.
 ``forward`` is a convenience wrapper that allocates the outputs with torch
@@ -16,7 +16,7 @@ import os
 import torch  # imported first: the library then binds to torch's HIP runtime
 
 __all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-           "attn_fwd_strided", "attn_pack_key_mask", "AttnLayout", "attn_strerror", "forward", "pack_key_mask", "AttnError",
+           "attn_fwd_strided", "attn_fwd_block_sparse", "attn_pack_key_mask", "AttnLayout", "attn_strerror", "forward", "pack_key_mask", "AttnError",
            "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -25,7 +25,8 @@ _lib = None
 
 ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH = range(5)
 EXPORTED = ("attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked", "attn_fwd_strided",
-            "attn_pack_key_mask", "attn_strerror")
+            "attn_fwd_block_sparse", "attn_pack_key_mask", "attn_strerror")
+SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 128, 64
 
 
 class AttnLayout(ctypes.Structure):
@@ -68,6 +69,8 @@ def load_library():
     lib.attn_fwd_strided.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32,
                                      lay, lay, lay, lay, ptr, ptr, ptr]
     lib.attn_fwd_strided.restype = i32
+    lib.attn_fwd_block_sparse.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32, ptr, ptr]
+    lib.attn_fwd_block_sparse.restype = i32
     lib.attn_pack_key_mask.argtypes = [ptr, ptr, i32, i32, ptr]
     lib.attn_pack_key_mask.restype = i32
     lib.attn_strerror.argtypes = [i32]
@@ -116,6 +119,12 @@ def attn_fwd_strided(q, k, v, o, lse, B, H, N, d, scale, causal, q_layout, k_lay
                                            key_len, key_bits, stream))
 
 
+def attn_fwd_block_sparse(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, stream):
+    """C entry point attn_fwd_block_sparse: raw addresses; block_mask [ceil(N/128)][ceil(N/64)] bytes."""
+    _check(load_library().attn_fwd_block_sparse(q, k, v, o, lse, B, H, N, d, float(scale), int(bool(causal)),
+                                                block_mask, stream))
+
+
 def attn_pack_key_mask(key_valid, key_bits, B, N, stream):
     """C entry point attn_pack_key_mask: raw addresses of the byte mask and the bit words."""
     _check(load_library().attn_pack_key_mask(key_valid, key_bits, B, N, stream))
@@ -147,7 +156,7 @@ def _layout(t):
 
 
 def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None, key_valid=None,
-            key_bits=None):
+            key_bits=None, block_mask=None):
     """O, LSE for [B, H, N, d] tensors on one device.
 
     bf16 tensors use attn_fwd, fp32 tensors attn_fwd_fp32.  ``scale``
@@ -161,6 +170,10 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
     attn_pack_key_mask first) or ``key_bits`` the packed int32
     [B, ceil(N/32)] words, all on the same device; then the masked entry
     points are called.  Rows that see no key get O = 0 and LSE = -inf.
+    Block-sparse: ``block_mask`` a bool or uint8 [ceil(N/128), ceil(N/64)]
+    tensor on the same device (query blocks of 128 rows, key blocks of 64
+    keys; only set blocks are computed), with contiguous bf16 q, k, v, out
+    and no key mask (attn_fwd_block_sparse).
     Launches on torch's current stream and returns without synchronising.
     """
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -183,6 +196,18 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     strided = not all(t.is_contiguous() for t in (q, k, v, out))
+    if block_mask is not None:
+        nbq, nbk = -(-N // SPARSE_BLOCK_Q), -(-N // SPARSE_BLOCK_K)
+        if block_mask.dtype not in (torch.bool, torch.uint8) or block_mask.shape != (nbq, nbk) \
+                or not block_mask.is_contiguous() or block_mask.device != q.device:
+            raise ValueError(f"block_mask must be a contiguous bool or uint8 [{nbq}, {nbk}] tensor on q's device")
+        if strided or q.dtype != torch.bfloat16 or key_len is not None or key_valid is not None \
+                or key_bits is not None:
+            raise ValueError("block_mask takes contiguous bf16 tensors and no key mask")
+        with torch.cuda.device(q.device):
+            attn_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  B, H, N, d, scale, causal, block_mask.data_ptr(), _stream_handle(q.device))
+        return out, lse
     if strided and q.dtype != torch.bfloat16:
         raise ValueError("fp32 q, k, v and out must be contiguous [B, H, N, d]")
     if key_valid is not None:

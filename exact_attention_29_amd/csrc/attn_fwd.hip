@@ -71,6 +71,12 @@ constexpr int kBc = 64;                      // keys per K/V tile (two half tile
 // where shorter rows per workgroup balance the triangle better.
 constexpr int kWavesFull = 8;
 constexpr int kWavesCausal = 4;
+// Block-sparse calls: one workgroup per 128-row query block (4 waves), a
+// 4-stage ring (prefetch distance 2) and the list of the block's key tiles
+// in LDS (at most this many: N <= 64 * 4096).
+constexpr int kSparseBlockQ = 128;
+constexpr int kSparseBlockK = 64;
+constexpr int kMaxSparseTiles = 4096;
 constexpr int kRow = 128;                    // bytes per K or V row (64 bf16)
 constexpr int kTileBytes = kBc * kRow;       // 8192
 constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile: 16384
@@ -115,6 +121,8 @@ struct Bf16Args {
   // and rows; the 64 features of a row are contiguous
   long long sb[4], sh[4];
   int sn[4];
+  const uint8_t* block_mask;  // block-sparse kernel: [ceil(N/128)][mask_cols]
+  int mask_cols;              // ceil(N/64)
   const int* key_len;         // [B] or null: keys j >= key_len[b] are hidden
   const uint32_t* key_bits;   // [B][ceil(N/32)] or null: bit j%32 of word j/32
                               // clear hides key j of entry b
@@ -196,7 +204,7 @@ __device__ __forceinline__ bf16x8 lds_read_vt(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <bool kCausal, int kWaves, bool kKeyMask>
+template <bool kCausal, int kWaves, bool kKeyMask, bool kSparse>
 __global__ void __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(Bf16Args a) {
@@ -204,6 +212,11 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   constexpr int kDmaPasses = 8 / kWaves;  // a DMA instruction covers 8 rows per wave
   constexpr int kDmaPerTile = 2 * kDmaPasses;
   static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
+  static_assert(!kSparse || (kWaves * 32 == kSparseBlockQ && !kKeyMask),
+                "a block-sparse workgroup owns one query block; no key mask on that path");
+  constexpr int kLeadK = kSparse ? 2 : kLead;  // prefetch distance
+  constexpr int kStagesK = kLeadK + 2;         // LDS ring stages
+  static_assert(kLeadK >= 2 && kStagesK <= ATTN_STAGES, "ring deeper than the declared stages");
   // One LDS object per ring stage: with the stage known at compile time (the
   // steady state), the compiler can tell a stage being filled by DMA from the
   // stages being read and does not wait for the DMA before those reads.
@@ -211,16 +224,19 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds4[kStageBytes];
+  // stages past this kernel's ring take 16 bytes (never selected)
+  __shared__ __attribute__((aligned(1024))) char lds4[kStagesK > 4 ? kStageBytes : 16];
 #if ATTN_STAGES > 5
-  __shared__ __attribute__((aligned(1024))) char lds5[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds5[kStagesK > 5 ? kStageBytes : 16];
 #endif
 #if ATTN_STAGES > 6
-  __shared__ __attribute__((aligned(1024))) char lds6[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds6[kStagesK > 6 ? kStageBytes : 16];
 #endif
 #if ATTN_STAGES > 7
-  __shared__ __attribute__((aligned(1024))) char lds7[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds7[kStagesK > 7 ? kStageBytes : 16];
 #endif
+  // block-sparse: the key tiles this workgroup's query block visits, ascending
+  __shared__ uint16_t tile_list[kSparse ? kMaxSparseTiles : 1];
   auto stage_ptr = [&](int st) -> char* {
     char* p = st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 : lds4;
 #if ATTN_STAGES > 5
@@ -272,11 +288,42 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const int n_k = a.key_len ? min(max(a.key_len[b_entry], 0), n) : n;
   int kv_end = n_k;
   if (kCausal) kv_end = min(n_k, qt * kBr + kBr);
-  const int n_half = (kv_end + 31) / 32;  // half tiles of 32 keys
-  const int n_tiles = (n_half + 1) / 2;
+  int n_half = (kv_end + 31) / 32;  // half tiles of 32 keys
+  int n_tiles = (n_half + 1) / 2;
   // last key / half tile with any visible key for this wave
   const int wave_last_key = (q_wave >= n || n_k == 0) ? -1 : (kCausal ? min(n_k - 1, q_wave + 31) : n_k - 1);
-  const int last_h = wave_last_key < 0 ? -1 : wave_last_key / 32;
+  int last_h = wave_last_key < 0 ? -1 : wave_last_key / 32;
+
+  // ---- block-sparse: compact the key tiles whose block of M is set for
+  // this query block into tile_list (wave 0 writes, every wave counts); from
+  // here on a tile or half-tile index is a position in that list, and
+  // kt_of / real_half map it back to key indices.  Tiles past the causal
+  // diagonal or the valid length are not listed (n_tiles bounds them).
+  int n_act = n_tiles;
+  if constexpr (kSparse) {
+    const uint8_t* mrow = a.block_mask + (size_t)qt * a.mask_cols;
+    n_act = 0;
+    for (int base = 0; base < n_tiles; base += 64) {
+      const int kt = base + lane;
+      const bool act = kt < n_tiles && mrow[kt] != 0;
+      const uint64_t bal = __ballot(act);
+      const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+      if (wave == 0 && act) tile_list[n_act + below] = (uint16_t)kt;
+      n_act += __popcll(bal);
+    }
+    __syncthreads();
+    n_tiles = n_act;
+    n_half = 2 * n_act;  // a listed ragged tile's hidden half is masked
+    last_h = (wave_last_key < 0 || n_act == 0) ? -1 : n_half - 1;
+  }
+  auto kt_of = [&](int pos) -> int {
+    if constexpr (kSparse) return __builtin_amdgcn_readfirstlane((int)tile_list[pos]);
+    else return pos;
+  };
+  auto real_half = [&](int j) -> int {
+    if constexpr (kSparse) return 2 * kt_of(j >> 1) + (j & 1);
+    else return j;
+  };
 
   // ---- global -> LDS staging by DMA (buffer/global loads with the LDS
   // bit, 16 bytes per lane): in pass p, lane l of wave w fills LDS chunk slot
@@ -304,7 +351,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, k_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t v_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, v_bytes, kBufferWord3);
-  auto dma_tile = [&](int kt, char* stage_base) {
+  auto dma_tile = [&](int pos, char* stage_base) {
+    const int kt = kt_of(pos);
     char* kd = stage_base + wave_s * 1024;
     if ((kt + 1) * kBc <= n) {
 #pragma unroll
@@ -335,11 +383,11 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 
 
   // End of tile t: the barrier publishes tile t+2, whose DMAs must be done;
-  // those of tiles t+3 .. t+kLead (the ones that exist) may still fly.  Every
+  // those of tiles t+3 .. t+kLeadK (the ones that exist) may still fly.  Every
   // LDS read of the stage the next DMA overwrites has already fed an MFMA, so
   // the barrier needs no LDS wait.
   auto dma_barrier = [&](int t) {
-    vm_wait_barrier_tiles<kDmaPerTile, kLead - 2>(min(kLead - 2, max(0, n_tiles - 3 - t)));
+    vm_wait_barrier_tiles<kDmaPerTile, kLeadK - 2>(min(kLeadK - 2, max(0, n_tiles - 3 - t)));
   };
 
 
@@ -395,12 +443,15 @@ attn_fwd_bf16_kernel(Bf16Args a) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_vt(p + v_off[0][db], p + v_off[1][db]), pop[tt], acc[db], 0, 0, 0);
       }
   };
-  auto stage_base = [&](int j) { return stage_ptr((j >> 1) % kStages); };
+  auto stage_base = [&](int j) { return stage_ptr((j >> 1) % kStagesK); };
 
   // Hidden keys of half tile j become -inf (ragged end or valid length,
   // causal diagonal, and with a key mask every key it hides).
   const uint32_t* const mask_row = kKeyMask ? a.key_bits + (size_t)b_entry * ((n + 31) / 32) : nullptr;
-  auto needs_lim = [&](int j) { return 32 * j + 32 > n_k || (kCausal && 32 * j + 31 > q_wave); };
+  auto needs_lim = [&](int j) {
+    const int jr = real_half(j);
+    return 32 * jr + 32 > n_k || (kCausal && 32 * jr + 31 > q_wave);
+  };
   auto needs_mask = [&](int j) { return kKeyMask || needs_lim(j); };
   // One mask word covers a half tile's 32 keys, the same for every lane (a
   // scalar load).  Register r holds key 8*(r/4) + 4*hi + r%4: its 64-lane
@@ -418,9 +469,10 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     if (kKeyMask) apply_bits(mask_row[j], s);  // j < n_half <= ceil(N/32)
     if (!kKeyMask || needs_lim(j)) {
       const int lim = kCausal ? min(qi, n_k - 1) : n_k - 1;  // last visible key
+      const int jr = real_half(j);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * j + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int key = 32 * jr + 8 * (r >> 2) + 4 * hi + (r & 3);
         s[r] = key <= lim ? s[r] : -INFINITY;
       }
     }
@@ -585,7 +637,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     step_general(2 * t, sA, pA, sB, pB);
     if (2 * t + 1 < n_half) step_general(2 * t + 1, sB, pB, sA, pA);
     dma_barrier(t);
-    if (t + 1 + kLead < n_tiles) dma_tile(t + 1 + kLead, stage_ptr((t + 1 + kLead) % kStages));
+    if (t + 1 + kLeadK < n_tiles) dma_tile(t + 1 + kLeadK, stage_ptr((t + 1 + kLeadK) % kStagesK));
   };
   // one tile t whose stage is known at compile time, both steps fast.  Step
   // 2t uses operands A and reads B for step 2t+1 (PV(2t) from this tile's
@@ -595,24 +647,24 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   auto tile_fast = [&](int t, auto stage_tag) {
     constexpr int st = decltype(stage_tag)::value;
     char* const b_cur = stage_ptr(st);
-    char* const b_next = stage_ptr((st + 1) % kStages);
-    const uint32_t vis0 = kKeyMask ? mask_row[2 * t] : 0xffffffffu;
-    const uint32_t vis1 = kKeyMask ? mask_row[2 * t + 1] : 0xffffffffu;
+    char* const b_next = stage_ptr((st + 1) % kStagesK);
+    const uint32_t vis0 = kKeyMask ? mask_row[real_half(2 * t)] : 0xffffffffu;
+    const uint32_t vis1 = kKeyMask ? mask_row[real_half(2 * t + 1)] : 0xffffffffu;
     step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0);  // j = 2t
     step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1);  // j = 2t + 1
     dma_barrier(t);
-    if (t + 1 + kLead < n_tiles) dma_tile(t + 1 + kLead, stage_ptr((st + 1 + kLead) % kStages));
+    if (t + 1 + kLeadK < n_tiles) dma_tile(t + 1 + kLeadK, stage_ptr((st + 1 + kLeadK) % kStagesK));
   };
 
   // ---- prologue: tiles 0 and 1 into LDS, tile 2 in flight, S(0)
-  // tiles 0 .. kLead in flight; tiles 0 and 1 must land before the first
-  // barrier (tile t+kLead is issued right after the barrier ending tile t-1)
+  // tiles 0 .. kLeadK in flight; tiles 0 and 1 must land before the first
+  // barrier (tile t+kLeadK is issued right after the barrier ending tile t-1)
 #pragma unroll
-  for (int tl = 0; tl <= kLead; ++tl)
+  for (int tl = 0; tl <= kLeadK; ++tl)
     if (tl < n_tiles) dma_tile(tl, stage_ptr(tl));
-  // tiles 0 and 1 must have landed; the rest of the min(n_tiles, kLead+1)
+  // tiles 0 and 1 must have landed; the rest of the min(n_tiles, kLeadK+1)
   // issued may still fly
-  vm_wait_barrier_tiles<kDmaPerTile, kLead - 1>(max(0, min(n_tiles, kLead + 1) - 2));
+  vm_wait_barrier_tiles<kDmaPerTile, kLeadK - 1>(max(0, min(n_tiles, kLeadK + 1) - 2));
   if (last_h >= 0) compute_s(lds0, 0, sA);
 
   // ---- tiles: 0 on the general path, then the steady state (both half
@@ -627,23 +679,36 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     if (last_h < 2) lim = 0;
     int full = n_k / 32;                                 // halves with no ragged key
     if (kCausal) full = min(full, q_wave / 32);          // halves before the diagonal
-    lim = min(lim, (full - 2) / 2);                      // 2t+1 < full
+    if constexpr (kSparse) {
+      // positions whose listed tile kt has 2kt+1 < full: a prefix of the
+      // ascending list; binary search for its length
+      const int kt_lim = (full - 2) / 2;
+      int lo = 0, up = n_act;
+      while (lo < up) {
+        const int mid = (lo + up) >> 1;
+        if (kt_of(mid) <= kt_lim) lo = mid + 1;
+        else up = mid;
+      }
+      lim = min(lim, lo - 1);
+    } else {
+      lim = min(lim, (full - 2) / 2);                    // 2t+1 < full
+    }
     if (full < 2) lim = 0;
     t_fast_end = max(1, lim + 1);
     // The steady state needs a finite reference in every row: with a key
     // mask, a row whose first tile was all hidden has none yet, so such a
     // wave stays on the exact-max path (no -inf - -inf, no NaN).  Without a
     // key mask, key 0 is visible to every row.
-    if (kKeyMask && __any(m_run == -INFINITY)) t_fast_end = 1;
+    if ((kKeyMask || kSparse) && __any(m_run == -INFINITY)) t_fast_end = 1;
   }
   int t = 1;
   // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
-  if (t + kStages - 1 < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
-  for (; t + kStages - 1 < t_fast_end; t += kStages) {
-    // tiles t .. t+kStages-1 sit in stages 1, 2, .., kStages-1, 0
-    Unroll<0, kStages>::run([&](auto i) {
+  if (t + kStagesK - 1 < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
+  for (; t + kStagesK - 1 < t_fast_end; t += kStagesK) {
+    // tiles t .. t+kStagesK-1 sit in stages 1, 2, .., kStagesK-1, 0
+    Unroll<0, kStagesK>::run([&](auto i) {
       constexpr int I = decltype(i)::value;
-      tile_fast(t + I, std::integral_constant<int, (I + 1) % kStages>());
+      tile_fast(t + I, std::integral_constant<int, (I + 1) % kStagesK>());
     });
   }
   for (; t < n_tiles; ++t) tile_general(t);
@@ -673,7 +738,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     for (int j = 0; j <= last_h; ++j) {
       f32x16 s;
       {
-        const int key = 32 * j + l32;
+        const int key = 32 * real_half(j) + l32;
         bf16x8 kop[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -703,7 +768,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
           bf16x8 vop;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const int key = 32 * j + 16 * tt + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const int key = 32 * real_half(j) + 16 * tt + 8 * (i >> 2) + 4 * hi + (i & 3);
             const uint16_t bits = key < n ? vg[(size_t)key * v_sn + 32 * db + l32] : (uint16_t)0;
             vop[i] = __builtin_bit_cast(__bf16, bits);
           }
@@ -911,7 +976,8 @@ attn_status check_layouts(const attn_layout* const lay[4], int H, int N, long lo
 attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                         int H, int N, int d, float scale, int causal, const int* key_len,
                         const uint32_t* key_bits, void* stream,
-                        const attn_layout* const layouts[4] = nullptr) {
+                        const attn_layout* const layouts[4] = nullptr,
+                        const uint8_t* block_mask = nullptr) {
   attn_status st = validate(q, k, v, o, lse, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
   if (misaligned(key_len, 4) || misaligned(key_bits, 4)) return ATTN_E_ALIGN;
@@ -920,6 +986,7 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
   const attn_layout* const none[4] = {nullptr, nullptr, nullptr, nullptr};
   st = check_layouts(layouts ? layouts : none, H, N, sb, sh, sn);
   if (st != ATTN_OK) return st;
+  if (block_mask && (key_bits || N > kSparseBlockK * kMaxSparseTiles)) return ATTN_E_INVALID;
   st = check_device();
   if (st != ATTN_OK) return st;
 
@@ -930,9 +997,11 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   a.n = N;
-  const int waves = causal ? kWavesCausal : kWavesFull;
+  const int waves = block_mask ? kSparseBlockQ / 32 : causal ? kWavesCausal : kWavesFull;
   const int rows = waves * 32;
   a.q_tiles = (N + rows - 1) / rows;
+  a.block_mask = block_mask;
+  a.mask_cols = (N + kSparseBlockK - 1) / kSparseBlockK;
   a.total_tiles = B * H * a.q_tiles;
   // c must be > 0: masked scores are -inf and fma(-inf, c, -m) must stay
   // -inf.  A zero (or denormal) scale becomes FLT_MIN, whose scores differ by
@@ -950,12 +1019,15 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
 
   void* args[] = {&a};
   const void* fn;
-  if (key_bits)
-    fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal, true>)
-                : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, true>);
+  if (block_mask)
+    fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, 4, false, true>)
+                : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, 4, false, true>);
+  else if (key_bits)
+    fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal, true, false>)
+                : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, true, false>);
   else
-    fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal, false>)
-                : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, false>);
+    fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal, false, false>)
+                : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, false, false>);
   const hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles), dim3(waves * 64), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
@@ -1026,6 +1098,15 @@ extern "C" attn_status attn_fwd_strided(const void* q, const void* k, const void
                                         const unsigned* key_bits, void* stream) {
   const attn_layout* const layouts[4] = {q_layout, k_layout, v_layout, o_layout};
   return launch_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, key_bits, stream, layouts);
+}
+
+extern "C" attn_status attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
+                                             float* lse, int B, int H, int N, int d, float scale,
+                                             int causal, const unsigned char* block_mask,
+                                             void* stream) {
+  if (!block_mask) return ATTN_E_INVALID;
+  return launch_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, nullptr, stream, nullptr,
+                     block_mask);
 }
 
 extern "C" attn_status attn_pack_key_mask(const unsigned char* key_valid, unsigned* key_bits,

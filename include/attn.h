@@ -166,6 +166,27 @@ attn_status attn_fwd_strided(const void *q, const void *k, const void *v,
                              const unsigned *key_bits, void *stream);
 
 /*
+ * attn_fwd_block_sparse: block-sparse attention, the variant described on
+ * the FlashAttention reading notes page, section "block-sparse
+ * FlashAttention": a predefined 0/1 matrix M over (query block, key block)
+ * pairs; only the blocks where M is 1 are computed, so compute and K/V
+ * traffic shrink with the fraction of set blocks.  Key j is hidden from
+ * query i when M[i / 128][j / 64] == 0 (query blocks of 128 rows, key
+ * blocks of 64 keys; the same M for every batch entry and head).  Causal
+ * masking, when asked for, applies on top.
+ *   block_mask : const unsigned char [ceil(N/128)][ceil(N/64)] device array,
+ *                row-major, non-zero = the block takes part.
+ * A query row that sees no key gets O = 0 and LSE = -inf (as
+ * attn_fwd_masked).  Same layout, ownership, stream and error rules as
+ * attn_fwd; N may be at most 262144 (ATTN_E_INVALID above).
+ */
+attn_status attn_fwd_block_sparse(const void *q, const void *k, const void *v,
+                                  void *o, float *lse, int B, int H, int N,
+                                  int d, float scale, int causal,
+                                  const unsigned char *block_mask,
+                                  void *stream);
+
+/*
  * attn_pack_key_mask: one byte per key -> the bit form attn_fwd_masked
  * reads.  key_valid: const unsigned char [B][N] device array (non-zero =
  * the key takes part); key_bits: unsigned [B][ceil(N/32)] device array,

@@ -100,6 +100,20 @@ def test_strided_validation():
             == ea.ATTN_E_DEVICE
 
 
+def test_block_sparse_validation():
+    lib = ea.load_library()
+    f = lambda **kw: lib.attn_fwd_block_sparse(kw.get("q", ALIGNED), ALIGNED, ALIGNED, ALIGNED, ALIGNED,  # noqa: E731
+                                                1, 1, kw.get("N", 300), 64, 0.125, 0,
+                                                kw.get("m", ALIGNED + 3), None)
+    assert f(m=None) == ea.ATTN_E_INVALID
+    assert f(q=None) == ea.ATTN_E_INVALID
+    assert f(N=64 * 4096 + 1) == ea.ATTN_E_INVALID
+    assert f(q=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert f() == ea.ATTN_E_DEVICE
+
+
 def test_pack_key_mask_validation():
     lib = ea.load_library()
     assert lib.attn_pack_key_mask(None, ALIGNED, 1, 8, None) == ea.ATTN_E_INVALID

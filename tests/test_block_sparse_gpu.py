@@ -1,0 +1,104 @@
+"""Block-sparse forward on the GPU (attn_fwd_block_sparse) against the fp64
+oracle.
+
+FlashAttention reading notes, section "block-sparse FlashAttention": a
+predefined 0/1 matrix M over (query block, key block) pairs; only the set
+blocks take part.  Here query blocks are 128 rows and key blocks 64 keys,
+one M for every batch entry and head.  Rows that see no key at all get
+O = 0 and LSE = -inf exactly (the oracle's reading), the rest are compared
+to the bf16 bars.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_29_amd as ea
+from oracle import attention as oracle_attention
+from tests.parity import BF16, assert_within, errors
+from workloads import WORKLOADS, Workload, make_inputs, sample_rows, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BQ, BK = ea.SPARSE_BLOCK_Q, ea.SPARSE_BLOCK_K
+
+
+def blocks(n):
+    return -(-n // BQ), -(-n // BK)
+
+
+def run(q, k, v, m, scale, causal):
+    mt = torch.from_numpy(np.asarray(m, dtype=bool)).to(DEV)
+    o, lse = ea.forward(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal, block_mask=mt)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(q, k, v, o, lse, m, scale, causal, what, rows=None):
+    o_ref, l_ref = oracle_attention(to_f64(q), to_f64(k), to_f64(v), scale, causal=causal, rows=rows,
+                                    block_mask=(m, BQ, BK))
+    o_h, l_h = to_f64(o), to_f64(lse)
+    if rows is not None:
+        o_h, l_h = o_h[:, :, rows], l_h[:, :, rows]
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(l_h), empty), f"{what}: empty rows differ"
+    assert np.all(o_h[empty] == 0.0), f"{what}: an empty row has O != 0"
+    if (~empty).any():
+        assert_within(errors(o_h[~empty], l_h[~empty], o_ref[~empty], l_ref[~empty]), BF16, what)
+    return int(empty.sum())
+
+
+def inputs(B, H, N, seed, sigma=1.0):
+    return make_inputs(Workload("sparse", B, H, N, 64, "bf16", sigma, 0.125, False, seed, ""))
+
+
+@pytest.mark.parametrize("n", [200, 1000, 2000])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("density", [0.3, 0.7])
+def test_random_block_masks(n, causal, density):
+    B, H = 2, 3
+    rng = np.random.default_rng(900 + n + 7 * causal + int(10 * density))
+    m = rng.random(blocks(n)) < density
+    m[0, :] = False  # the first query block sees nothing: empty rows
+    q, k, v = inputs(B, H, n, seed=901 + n)
+    o, lse = run(q, k, v, m, 0.125, causal)
+    empty = check(q, k, v, o, lse, m, 0.125, causal, f"random M n={n} causal={causal} density={density}")
+    assert empty >= B * H * min(n, BQ)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_ones_matches_dense_bitwise(causal):
+    """Every block set: the same arithmetic as the dense kernel, row for row
+    (same key tiles in the same order), so the very same bits."""
+    B, H, N = 2, 2, 1500
+    q, k, v = (t.to(DEV) for t in inputs(B, H, N, seed=910 + causal))
+    m = torch.ones(blocks(N), dtype=torch.bool, device=DEV)
+    o_s, l_s = ea.forward(q, k, v, scale=0.125, causal=causal, block_mask=m)
+    o_d, l_d = ea.forward(q, k, v, scale=0.125, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_d) and torch.equal(l_s, l_d)
+
+
+def test_first_listed_tile_hidden_by_causality():
+    """Causal, with each query block's first set key block lying past some of
+    its rows' diagonals: those waves start with no reference max."""
+    B, H, N = 1, 2, 1024
+    nbq, nbk = blocks(N)
+    m = np.zeros((nbq, nbk), dtype=bool)
+    for i in range(nbq):
+        m[i, 2 * i + 1] = True     # the block's second key tile only
+        m[i, 0] = i % 2 == 0       # and key tile 0 for every other block
+    q, k, v = inputs(B, H, N, seed=920)
+    o, lse = run(q, k, v, m, 0.125, True)
+    check(q, k, v, o, lse, m, 0.125, True, "first listed tile past the diagonal")
+
+
+def test_patch_3mp_sparse_sampled():
+    """The 3 MP patch shape with a quarter of the blocks set, sampled rows."""
+    w = WORKLOADS["patch_3mp"]
+    B, H, N, d = w.shape
+    rng = np.random.default_rng(930)
+    m = rng.random(blocks(N)) < 0.25
+    q, k, v = make_inputs(w)
+    o, lse = run(q, k, v, m, w.scale, False)
+    check(q, k, v, o, lse, m, w.scale, False, "3 MP block-sparse", rows=sample_rows(N, 64, seed=31))
