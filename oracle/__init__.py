@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the exact attention forward pass.
+"""Plain fp64 CPU oracle for exact attention: forward pass and gradients.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
 in ``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import
@@ -16,9 +16,13 @@ exactly rounded ``math.fsum`` variant, torch's float64 SDPA, closed forms
 (uniform, identity, single peak, causal prefix means), invariants (rows of P
 sum to one, constant V, one key, causal row 0, key/value permutation, score
 shift), the one-hot limit, and the worked mask example printed on the page
-"flash-attnの代役がVRAMを18GB溶かしていたので87%削った話" (Qiita), section 6.
+"flash-attnの代役がVRAMを18GB溶かしていたので87%削った話" (Qiita), section 6;
+key-padding and block-sparse masks against shard merges and sub-problems.
+Gradients (``oracle.backward``): central finite differences of the forward
+oracle and torch's float64 autograd.
 """
 
+from .backward import attention_backward  # noqa: F401
 from .fp64 import (  # noqa: F401
     attention,
     attention_fsum,

@@ -257,6 +257,24 @@ def pin_torch_sdpa_float64():
 
 # ------------------------------------------------------- other implementations
 
+def pin_backward_torch_autograd():
+    """torch's float64 autograd through the materialised softmax attention
+    (a library routine) agrees with the backward oracle."""
+    from oracle.backward import attention_backward
+    rng = _rng(26)
+    B, H, N, d = 2, 2, 33, 16
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    for causal in (False, True):
+        tq, tk, tv = (torch.tensor(t, requires_grad=True) for t in (q, k, v))
+        mask = torch.ones(N, N, dtype=torch.bool).tril() if causal else None
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3)
+        out.backward(torch.tensor(do))
+        dq, dk, dv = attention_backward(q, k, v, do, 0.3, causal=causal)
+        _close(dq, tq.grad.numpy(), 1e-11, f"dQ vs torch autograd (causal={causal})")
+        _close(dk, tk.grad.numpy(), 1e-11, f"dK vs torch autograd (causal={causal})")
+        _close(dv, tv.grad.numpy(), 1e-11, f"dV vs torch autograd (causal={causal})")
+
+
 def pin_materialised_brute_force():
     """The materialised (standard) attention agrees on the tiny workload and
     on random small shapes; its rows of P sum to one."""
@@ -410,6 +428,57 @@ def pin_block_sparse():
         _close(ml, full_l, 1e-12, f"merged block-sparse LSE causal={causal}")
 
 
+def pin_backward_finite_differences():
+    """The gradients of L = sum(dO * O) against central finite differences of
+    the forward oracle (step 1e-6, float64): every entry of dQ, dK and dV,
+    causal or not, on a tiny problem."""
+    from oracle.backward import attention_backward
+    rng = _rng(24)
+    B, H, N, d = 1, 2, 6, 4
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    scale, h = 0.7, 1e-6
+    for causal in (False, True):
+        dq, dk, dv = attention_backward(q, k, v, do, scale, causal=causal)
+
+        def loss(qq, kk, vv):
+            return float((O.attention(qq, kk, vv, scale, causal=causal)[0] * do).sum())
+
+        for name, x, g in (("dQ", q, dq), ("dK", k, dk), ("dV", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [xp if t is x else t for t in (q, k, v)]
+                args_m = [xm if t is x else t for t in (q, k, v)]
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(g, num, 1e-7, f"{name} vs finite differences (causal={causal})")
+
+
+def pin_backward_invariants():
+    """Facts of the softmax: dQ and dK rows do not change when every key's
+    score moves by the same amount (adding a constant to a row of S leaves P
+    alone), dV's column sums equal dO's (rows of P sum to one), and
+    sum_j dS_ij = 0 shows up as dK summing to zero over keys when Q rows are
+    equal."""
+    from oracle.backward import attention_backward
+    rng = _rng(25)
+    B, H, N, d = 2, 2, 9, 5
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    dq, dk, dv = attention_backward(q, k, v, do, 0.6)
+    _close(dv.sum(axis=2), do.sum(axis=2), 1e-12, "column sums of dV = column sums of dO")
+    # equal query rows: dS rows sum to zero, so the keys' gradients sum to zero
+    q_eq = np.broadcast_to(q[:, :, :1], q.shape).copy()
+    _, dk_eq, _ = attention_backward(q_eq, k, v, do, 0.6)
+    _close(dk_eq.sum(axis=2), np.zeros((B, H, d)), 1e-12, "sum over keys of dK with equal queries")
+    # a key shift along q's direction... a shared shift of every key by a
+    # vector u moves row i's scores by scale * q_i . u, a per-row constant:
+    u = rng.standard_normal(d)
+    dq2, dk2, dv2 = attention_backward(q, k + u, v, do, 0.6)
+    _close(dv2, dv, 1e-12, "dV under a shared key shift")
+    _close(dk2, dk, 1e-12, "dK under a shared key shift")
+
+
 INDEPENDENT_PINS = [
     pin_uniform_closed_form,
     pin_identity_closed_form,
@@ -424,9 +493,12 @@ INDEPENDENT_PINS = [
     pin_key_shard_merge,
     pin_padding_prefix_uniform,
     pin_block_sparse,
+    pin_backward_finite_differences,
+    pin_backward_invariants,
 ]
 
 ALL_PINS = INDEPENDENT_PINS + [
+    pin_backward_torch_autograd,
     pin_torch_sdpa_float64,
     pin_materialised_brute_force,
     pin_fsum_variant,

@@ -67,3 +67,31 @@ def test_independent_pins_catch_mutant(name, monkeypatch):
         except (AssertionError, ValueError, FloatingPointError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every independent pin"
+
+
+# mistakes in the gradient steps (oracle.backward)
+BACKWARD_MUTANTS = {
+    "dv_not_transposed": ("_dv", lambda p, do: p @ do),
+    "dp_uses_values_untransposed": ("_dp", lambda do, v: do @ v[::-1].T),
+    "delta_sums_dp_only": ("_delta", lambda p, dp: dp.sum(axis=1)),
+    "delta_dropped": ("_delta", lambda p, dp: np.zeros(p.shape[0])),
+    "ds_sign_flipped": ("_ds", lambda p, dp, delta: p * (delta[:, None] - dp)),
+    "ds_without_p": ("_ds", lambda p, dp, delta: dp - delta[:, None]),
+    "dq_scale_dropped": ("_dq", lambda ds, k, scale: ds @ k),
+    "dk_not_transposed": ("_dk", lambda ds, q, scale: scale * (ds @ q)),
+    "dk_scale_squared": ("_dk", lambda ds, q, scale: scale * scale * (ds.T @ q)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_independent_pins_catch_backward_mutant(name, monkeypatch):
+    from oracle import backward as OB
+    attr, fn = BACKWARD_MUTANTS[name]
+    monkeypatch.setattr(OB, attr, fn)
+    caught = []
+    for pin in INDEPENDENT_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every independent pin"
