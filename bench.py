@@ -382,6 +382,49 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     return line
 
 
+def bench_backward(w, steps, warmup):
+    """attn_bwd (three kernels: D, dK/dV, dQ) on the workload, inputs and
+    the forward's O, LSE resident.  FLOPs: the algorithmic 10*B*H*N^2*d of
+    the recomputing backward pass (recompute S, then dV, dP, dQ, dK: five
+    N x N x d products), halved when causal; this implementation recomputes S
+    and dP in both the key-parallel and the query-parallel kernel (14*N^2*d
+    executed)."""
+    import torch
+    import exact_attention_29_amd as ea
+    from workloads import make_inputs, Workload
+
+    dev = "cuda:0"
+    B, H, N, d = w.shape
+    q, k, v = (t.to(dev) for t in make_inputs(w))
+    do = make_inputs(Workload("do", B, H, N, d, "bf16", 1.0, w.scale, w.causal, w.seed + 50, ""))[0].to(dev)
+    o, lse = ea.forward(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def step():
+        ea.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, w.scale,
+                    w.causal, sh)
+
+    wall, kern, per = time_gpu(step, steps, warmup, stream)
+    flops = 10.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
+    return {
+        "metric": "attention backward (dQ, dK, dV) TFLOP/s",
+        "value": round(flops / wall / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.what}", "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "scale": w.scale, "flops_counted": "10*B*H*N^2*d (x0.5 causal)"},
+        "pct_of_bf16_peak": round(100.0 * flops / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "timing": {"ms_mean": round(kern * 1e3, 4), "ms_median": round(median(per) * 1e3, 4),
+                   "ms_min": round(min(per) * 1e3, 4),
+                   "note": "the three kernels of one call, between events on the launch stream"},
+        "workspace": {"delta_bytes": B * H * N * 4, "note": "caller-owned [B,H,N] fp32 scratch for D"},
+    }
+
+
 def workspace_sweep():
     """Device memory one call needs beyond its outputs, over the patch counts
     of the 0.5-8 MP workloads, with the two fits: extra = c*P + d and
@@ -442,6 +485,8 @@ def main():
     ap.add_argument("--cold", type=int, default=30,
                     help="launches timed with flushed caches after the warm steps (0: skip)")
     ap.add_argument("--no-clock", action="store_true", help="do not sample the clock with amd-smi")
+    ap.add_argument("--backward", action="store_true",
+                    help="time attn_bwd (dQ, dK, dV) instead of the forward pass")
     ap.add_argument("--block-density", type=float, default=None,
                     help="time attn_fwd_block_sparse with this fraction of random blocks set")
     ap.add_argument("--layout", choices=["contiguous", "packed"], default="contiguous",
@@ -478,6 +523,16 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 3}))
+        return
+
+    if args.backward:
+        w = WORKLOADS[args.workload]
+        if args.n:
+            w = w.with_n(args.n)
+        if args.causal:
+            from dataclasses import replace
+            w = replace(w, causal=args.causal == "yes")
+        print(json.dumps(bench_backward(w, args.steps, args.warmup)), flush=True)
         return
 
     if args.workspace_sweep:

@@ -6,7 +6,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 
@@ -30,9 +30,9 @@ def hipcc():
 
 
 def build(verbose=False, extra_flags=()):
-    """Compile csrc/attn_fwd.hip into exact_attention_29_amd/libattn.so."""
+    """Compile csrc/attn_fwd.hip and csrc/attn_bwd.hip into exact_attention_29_amd/libattn.so."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE] + SRCS + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

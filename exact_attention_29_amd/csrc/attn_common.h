@@ -1,0 +1,80 @@
+// Pieces shared by the forward and backward attention kernels on gfx950:
+// vector types, the swizzled LDS layout of 64-row x 64-feature bf16 tiles
+// and their two read patterns, lane-half exchanges, the XCD-aware block
+// remap, and host-side checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "attn.h"
+
+namespace attn_detail {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kD = 64;     // head size
+constexpr int kRow = 128;  // bytes per tile row (64 bf16)
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// max(x[lane], x[lane ^ 32]) in every lane, via v_permlane32_swap (which
+// exchanges the upper half of one register with the lower half of another).
+__device__ __forceinline__ float half_swap_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// XCD-aware block remap.  Workgroups are dealt round-robin to the 8 XCDs; this
+// makes the workgroups that land on one XCD take consecutive logical tiles, so
+// the query tiles of one head share that XCD's L2 while they stream its K/V.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int per = total >> 3, rem = total & 7;
+  const int x = w & 7, i = w >> 3;
+  return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+// 16-byte chunk c of tile row r lives at chunk position c ^ swz(r) of that
+// row: the row-operand reads (16 rows, one chunk) and the transpose reads (4
+// rows, 4 chunks per half wave) then hit 64 distinct banks.
+__device__ __forceinline__ int swz(int row) {
+  const int x = (row >> 1) & 7;
+  return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+}
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * kRow + ((chunk ^ swz(row)) << 4); }
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
+  return *(const bf16x8*)(base + off);
+}
+
+// Two ds_read_b64_tr_b16: the transposed operand (8 rows of one column per
+// lane) of an MFMA from a row-major tile.
+__device__ __forceinline__ bf16x8 lds_read_vt(const char* p0, const char* p1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Host side: ATTN_OK when the current device is a gfx950 (cached per device).
+__attribute__((visibility("hidden"))) attn_status check_device();
+
+inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+}  // namespace attn_detail

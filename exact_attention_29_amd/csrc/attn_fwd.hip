@@ -51,20 +51,12 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "attn_common.h"
 
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(8))) short i16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+using namespace attn_detail;
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr int kD = 64;                       // head size
 constexpr int kBc = 64;                      // keys per K/V tile (two half tiles)
 // Waves per workgroup (each owns 32 query rows): 8 (256 rows, one workgroup
 // per CU) without a mask, 4 (128 rows, two workgroups per CU) when causal,
@@ -77,7 +69,6 @@ constexpr int kWavesCausal = 4;
 constexpr int kSparseBlockQ = 128;
 constexpr int kSparseBlockK = 64;
 constexpr int kMaxSparseTiles = 4096;
-constexpr int kRow = 128;                    // bytes per K or V row (64 bf16)
 constexpr int kTileBytes = kBc * kRow;       // 8192
 constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile: 16384
 // Prefetch distance: after the barrier that ends tile t, tile t+kLead+1 is
@@ -97,8 +88,6 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS ring exceeds the 160 KiB of a gfx950
 // Fourth word of a gfx950 buffer resource: 32-bit data format, no swizzle.
 constexpr int kBufferWord3 = 0x00020000;
 
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kTau = 8.0f;                 // slack when the reference max is set
 constexpr unsigned kRedoBits = 0x4f800000u;  // bit pattern of 2^32: a partial
                                              // row sum above it means the
@@ -161,48 +150,6 @@ struct Unroll {
     }
   }
 };
-
-// max(x[lane], x[lane ^ 32]) in every lane, via v_permlane32_swap (which
-// exchanges the upper half of one register with the lower half of another).
-__device__ __forceinline__ float half_swap_max(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
-}
-
-__device__ __forceinline__ float half_swap_sum(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-// XCD-aware block remap.  Workgroups are dealt round-robin to the 8 XCDs; this
-// makes the workgroups that land on one XCD take consecutive logical tiles, so
-// the query tiles of one head share that XCD's L2 while they stream its K/V.
-__device__ __forceinline__ int xcd_remap(int w, int total) {
-  const int per = total >> 3, rem = total & 7;
-  const int x = w & 7, i = w >> 3;
-  return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
-}
-
-// 16-byte chunk c of tile row r lives at chunk position c ^ swz(r) of that
-// row: the K reads (16 rows, one chunk) and the V^T transpose reads (4 rows,
-// 4 chunks per half wave) then hit 64 distinct banks.
-__device__ __forceinline__ int swz(int row) {
-  const int x = (row >> 1) & 7;
-  return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
-}
-__device__ __forceinline__ int tile_off(int row, int chunk) { return row * kRow + ((chunk ^ swz(row)) << 4); }
-
-__device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
-  return *(const bf16x8*)(base + off);
-}
-
-__device__ __forceinline__ bf16x8 lds_read_vt(const char* p0, const char* p1) {
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
 
 template <bool kCausal, int kWaves, bool kKeyMask, bool kSparse>
 __global__ void __launch_bounds__(kWaves * 64)
@@ -909,6 +856,10 @@ __global__ void __launch_bounds__(256) attn_pack_key_mask_kernel(const uint8_t* 
 
 // ---------------------------------------------------------------- host side
 
+}  // namespace
+
+namespace attn_detail {
+
 constexpr int kMaxDevices = 64;
 // 0 = not checked, 1 = gfx950, 2 = other architecture
 int g_arch_state[kMaxDevices];
@@ -932,7 +883,9 @@ attn_status check_device() {
   return state == 1 ? ATTN_OK : ATTN_E_DEVICE;
 }
 
-bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+}  // namespace attn_detail
+
+namespace {
 
 attn_status validate(const void* q, const void* k, const void* v, const void* o, const void* lse,
                      int B, int H, int N, int d, float scale) {

@@ -200,6 +200,30 @@ attn_status attn_pack_key_mask(const unsigned char *key_valid,
                                unsigned *key_bits, int B, int N,
                                void *stream);
 
+/*
+ * attn_bwd: gradients of attn_fwd (bf16, contiguous [B][H][N][d], optional
+ * causal mask) by recomputation, as on the FlashAttention reading notes
+ * page, section "recomputation": from Q, K, V, the forward output O and its
+ * LSE, and the upstream gradient dO = dL/dO, the probabilities are rebuilt
+ * tile by tile (never stored) and
+ *     dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q.
+ *   q, k, v, o, dout : const bf16 [B][H][N][d] (o and lse as attn_fwd wrote
+ *                      them for the same q, k, v, scale and causal)
+ *   lse              : const float [B][H][N]
+ *   dq, dk, dv       : bf16 [B][H][N][d], written in full (rounded to
+ *                      nearest-even from fp32 accumulators)
+ *   delta            : float [B][H][N] scratch owned by the caller (D is
+ *                      written there, then read); 4-byte aligned.
+ * Three kernels are enqueued on `stream` (D, then dK and dV, then dQ); no
+ * atomics, so the result is deterministic.  Errors as attn_fwd (every bf16
+ * pointer 16-byte aligned, lse and delta 4-byte aligned).
+ */
+attn_status attn_bwd(const void *q, const void *k, const void *v,
+                     const void *o, const float *lse, const void *dout,
+                     void *dq, void *dk, void *dv, float *delta, int B, int H,
+                     int N, int d, float scale, int causal, void *stream);
+
 /* Static, human-readable text for a status code; never NULL. */
 const char *attn_strerror(attn_status status);
 

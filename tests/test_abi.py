@@ -114,6 +114,23 @@ def test_block_sparse_validation():
         assert f() == ea.ATTN_E_DEVICE
 
 
+def test_backward_validation():
+    lib = ea.load_library()
+
+    def bwd(**kw):
+        ptrs = [kw.get(n, ALIGNED) for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")]
+        return lib.attn_bwd(*ptrs, kw.get("B", 1), 1, kw.get("N", 100), kw.get("d", 64), 0.125, 0, None)
+    assert bwd(delta=None) == ea.ATTN_E_INVALID
+    assert bwd(dq=None) == ea.ATTN_E_INVALID
+    assert bwd(d=32) == ea.ATTN_E_INVALID
+    assert bwd(N=0) == ea.ATTN_E_INVALID
+    assert bwd(dout=ALIGNED + 8) == ea.ATTN_E_ALIGN
+    assert bwd(delta=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd(lse=ALIGNED + 4) == ea.ATTN_E_DEVICE
+
+
 def test_pack_key_mask_validation():
     lib = ea.load_library()
     assert lib.attn_pack_key_mask(None, ALIGNED, 1, 8, None) == ea.ATTN_E_INVALID

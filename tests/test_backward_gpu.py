@@ -1,0 +1,92 @@
+"""Backward pass on the GPU (attn_bwd) against the fp64 oracle's gradients.
+
+The GPU path gets O and LSE from its own forward pass (as a training step
+would), so D = rowsum(dO * O) uses the bf16-rounded O; the oracle computes
+the exact gradients of the definition from Q, K, V and dO.
+
+Bar (derived from the arithmetic): P and dS are rounded to bf16 (relative
+2^-9) before the products, O is bf16 (2^-9) where it enters D, and the
+results are rounded to bf16 (2^-9); with fp32 accumulation these give a
+relative Frobenius error of a few 1e-3 for random data (measured: about
+2.4e-3 on every gradient, elements within 5.3e-3 of max|ref|).  Each gradient
+must stay within 1e-2 relative Frobenius error and within 2e-2 * max|ref|
+at every element (about four times the measured error).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_29_amd as ea
+from oracle import attention_backward
+from workloads import WORKLOADS, Workload, make_inputs, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+REL_FRO = 1e-2
+REL_MAX = 2e-2
+
+
+def grads_gpu(q, k, v, do, scale, causal):
+    q, k, v, do = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = ea.forward(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = ea.backward(q, k, v, o, lse, do, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check(name, got, ref):
+    got = to_f64(got)
+    err = got - ref
+    fro = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300))
+    mx = float(np.abs(err).max() / max(np.abs(ref).max(), 1e-300))
+    print(f"[bwd] {name}: rel_fro {fro:.2e}  max/maxref {mx:.2e}", flush=True)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    assert fro <= REL_FRO, f"{name}: relative Frobenius error {fro:.3e} > {REL_FRO}"
+    assert mx <= REL_MAX, f"{name}: max error {mx:.3e} of max|ref| > {REL_MAX}"
+
+
+def inputs(B, H, N, seed, sigma=1.0):
+    w = Workload("bwd", B, H, N, 64, "bf16", sigma, 0.125, False, seed, "")
+    q, k, v = make_inputs(w)
+    do = make_inputs(Workload("bwd_do", B, H, N, 64, "bf16", 1.0, 0.125, False, seed + 1, ""))[0]
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("n", [1, 17, 64, 65, 200, 513])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_sizes(n, causal):
+    q, k, v, do = inputs(1, 2, n, seed=1100 + n)
+    dq, dk, dv = grads_gpu(q, k, v, do, 0.125, causal)
+    rq, rk, rv = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), 0.125, causal=causal)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(f"{name} n={n} causal={causal}", g, r)
+
+
+@pytest.mark.parametrize("name", ["bert_large", "gpt2_small_causal"])
+def test_backward_workload_shapes(name):
+    """The BERT-large and GPT-2 shapes of the pages' training runs, on two of
+    their batch entries (the oracle is quadratic per head)."""
+    w = WORKLOADS[name]
+    q, k, v = (t[:2] for t in make_inputs(w))
+    do = make_inputs(Workload("do", 2, w.H, w.N, 64, "bf16", 1.0, w.scale, w.causal, w.seed + 50, ""))[0]
+    dq, dk, dv = grads_gpu(q, k, v, do, w.scale, w.causal)
+    rq, rk, rv = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), w.scale, causal=w.causal)
+    for nm, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(f"{nm} {name}", g, r)
+
+
+def test_backward_deterministic():
+    q, k, v, do = inputs(2, 2, 300, seed=1200)
+    a = grads_gpu(q, k, v, do, 0.125, True)
+    b = grads_gpu(q, k, v, do, 0.125, True)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_backward_scale_sign():
+    """A negative scale flips every score: the gradients of the definition."""
+    q, k, v, do = inputs(1, 2, 150, seed=1300)
+    dq, dk, dv = grads_gpu(q, k, v, do, -0.2, False)
+    rq, rk, rv = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), -0.2)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(f"{name} scale=-0.2", g, r)
