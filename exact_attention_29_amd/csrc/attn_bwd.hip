@@ -119,6 +119,7 @@ struct TrOffsets {
 
 // ------------------------------------------------------------------ dK, dV
 
+template <bool kCausal>
 __global__ void __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkdv_kernel(BwdArgs a) {
   // double-buffered tiles: Q, dO (64 rows each, swizzled), LSE*log2(e), D
@@ -155,7 +156,7 @@ bwd_dkdv_kernel(BwdArgs a) {
 
   // query tiles: all of them, or (causal) from the one holding this
   // workgroup's first key
-  const int t_begin = a.causal ? (kb * kBwdRows) / kBwdTile : 0;
+  const int t_begin = kCausal ? (kb * kBwdRows) / kBwdTile : 0;
   const int t_end = (n + kBwdTile - 1) / kBwdTile;
 
   // staging: thread tid moves chunks tid and tid + 256 of the Q and dO tiles
@@ -208,6 +209,11 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {  // 32-query halves of the tile
       const int q0 = t * kBwdTile + 32 * j;
+      // causal: a half tile of queries before this wave's keys adds nothing
+      // (every key is hidden from every query); the one that starts at the
+      // wave's first key is the diagonal, the only one masked per element
+      if (kCausal && q0 < key0) continue;
+      const bool diag = kCausal && q0 == key0;
       // S = Q K^T and dP = dO V^T: lane = key, register r = query
       // q0 + 8*(r/4) + 4*hi + r%4
       f32x16 s = zero16, dp = zero16;
@@ -218,23 +224,31 @@ bwd_dkdv_kernel(BwdArgs a) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(dt, off), vop[ks], dp, 0, 0, 0);
       }
       // P = exp2(c s - LSE log2 e), dS = P (dP - D)
-      bf16x8 pb[2], dsb[2];
+      float p[16], dd[16];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qr = 32 * j + 8 * g4 + 4 * hi;  // tile row of register 4*g4
         const float4 l4 = *(const float4*)&ls[buf][qr];
         const float4 d4 = *(const float4*)&ds_[buf][qr];
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        dd[4 * g4] = d4.x, dd[4 * g4 + 1] = d4.y, dd[4 * g4 + 2] = d4.z, dd[4 * g4 + 3] = d4.w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
-          if (a.causal && key > t * kBwdTile + qr + e) p = 0.f;
-          const float dsv = p * (dp[r] - dd[e]);
-          pb[r >> 3][r & 7] = (__bf16)p;
-          dsb[r >> 3][r & 7] = (__bf16)dsv;
-        }
+        for (int e = 0; e < 4; ++e) p[4 * g4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g4 + e], c, -lv[e]));
+      }
+      if (diag) {  // wave-uniform: key > query hidden
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (l32 > 8 * (r >> 2) + 4 * hi + (r & 3)) p[r] = 0.f;
+      }
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const bf16x2 pp = {(__bf16)p[r], (__bf16)p[r + 1]};
+        const bf16x2 dq2 = {(__bf16)(p[r] * (dp[r] - dd[r])), (__bf16)(p[r + 1] * (dp[r + 1] - dd[r + 1]))};
+        pb[r >> 3][r & 7] = pp[0];
+        pb[r >> 3][(r & 7) + 1] = pp[1];
+        dsb[r >> 3][r & 7] = dq2[0];
+        dsb[r >> 3][(r & 7) + 1] = dq2[1];
       }
       // dV^T += dO^T P, dK^T += Q^T dS (k index i of half tt <-> query
       // q0 + 16*tt + 8*(i/4) + 4*hi + i%4, matched by the transposed reads)
@@ -275,6 +289,7 @@ bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------- dQ
 
+template <bool kCausal>
 __global__ void __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char ks_[2][kBwdTileBytes];
@@ -284,7 +299,7 @@ bwd_dq_kernel(BwdArgs a) {
   const int logical = xcd_remap(blockIdx.x, a.total);
   const int bh = logical / a.blocks;
   int qb = logical - bh * a.blocks;
-  if (a.causal) qb = a.blocks - 1 - qb;  // longest rows first
+  if (kCausal) qb = a.blocks - 1 - qb;  // longest rows first
   const size_t head = (size_t)bh * n * kD;
   const uint16_t* qg = a.q + head;
   const uint16_t* kg = a.k + head;
@@ -293,7 +308,8 @@ bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int qi = qb * kBwdRows + wave * 32 + l32;  // this lane's query
+  const int q0w = qb * kBwdRows + wave * 32;  // this wave's first query
+  const int qi = q0w + l32;                    // this lane's query
 
   // Q^T and dO^T operands (B operands of S^T = K Q^T and dP^T = V dO^T)
   bf16x8 qop[4], dop[4];
@@ -307,7 +323,7 @@ bwd_dq_kernel(BwdArgs a) {
   const TrOffsets tr(lane);
 
   const int q_last = min(n - 1, qb * kBwdRows + kBwdRows - 1);
-  const int kv_end = a.causal ? q_last + 1 : n;
+  const int kv_end = kCausal ? q_last + 1 : n;
   const int t_end = (kv_end + kBwdTile - 1) / kBwdTile;
 
   u32x4 stk[2], stv[2];
@@ -348,8 +364,15 @@ bwd_dq_kernel(BwdArgs a) {
     const char* vt = vs_[buf];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {  // 32-key halves of the tile
+      const int k0 = t * kBwdTile + 32 * j;
+      // causal: keys past this wave's last query add nothing; the half tile
+      // that starts at the wave's first query is the diagonal.  Only the
+      // diagonal and the ragged last half tile are masked per element.
+      if (kCausal && k0 > q0w) continue;
+      const bool diag = kCausal && k0 == q0w;
+      const bool ragged = k0 + 32 > n;
       // S^T = K Q^T, dP^T = V dO^T: lane = query, register r = key
-      // t*64 + 32*j + 8*(r/4) + 4*hi + r%4
+      // k0 + 8*(r/4) + 4*hi + r%4
       f32x16 s = zero16, dp = zero16;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -357,13 +380,22 @@ bwd_dq_kernel(BwdArgs a) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kt, off), qop[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(vt, off), dop[ks], dp, 0, 0, 0);
       }
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+      if (diag || ragged) {  // wave-uniform: only these half tiles pay for masks
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);  // key - k0
+          if ((diag && kr > l32) || k0 + kr >= n) p[r] = 0.f;
+        }
+      }
       bf16x8 dsb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = t * kBwdTile + 32 * j + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-        if (kk >= n || (a.causal && kk > qi)) p = 0.f;
-        dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dlt));
+      for (int r = 0; r < 16; r += 2) {
+        const bf16x2 pr = {(__bf16)(p[r] * (dp[r] - dlt)), (__bf16)(p[r + 1] * (dp[r + 1] - dlt))};
+        dsb[r >> 3][r & 7] = pr[0];
+        dsb[r >> 3][(r & 7) + 1] = pr[1];
       }
       // dQ^T += K^T dS^T
 #pragma unroll
@@ -435,10 +467,12 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
                                  dim3((unsigned)((rows + 255) / 256)), dim3(256), dargs, 0, s);
   if (e != hipSuccess) return ATTN_E_LAUNCH;
   void* args[] = {&a};
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel), dim3(a.total), dim3(kBwdWaves * 64),
-                      args, 0, s);
+  const void* dkdv = causal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<true>)
+                            : reinterpret_cast<const void*>(&bwd_dkdv_kernel<false>);
+  const void* dqk = causal ? reinterpret_cast<const void*>(&bwd_dq_kernel<true>)
+                           : reinterpret_cast<const void*>(&bwd_dq_kernel<false>);
+  e = hipLaunchKernel(dkdv, dim3(a.total), dim3(kBwdWaves * 64), args, 0, s);
   if (e != hipSuccess) return ATTN_E_LAUNCH;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel), dim3(a.total), dim3(kBwdWaves * 64),
-                      args, 0, s);
+  e = hipLaunchKernel(dqk, dim3(a.total), dim3(kBwdWaves * 64), args, 0, s);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
