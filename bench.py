@@ -399,13 +399,13 @@ def bench_backward(w, steps, warmup):
     do = make_inputs(Workload("do", B, H, N, d, "bf16", 1.0, w.scale, w.causal, w.seed + 50, ""))[0].to(dev)
     o, lse = ea.forward(q, k, v, scale=w.scale, causal=w.causal)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(ea.attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
     def step():
         ea.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, w.scale,
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, N, d, w.scale,
                     w.causal, sh)
 
     wall, kern, per = time_gpu(step, steps, warmup, stream)
@@ -421,7 +421,8 @@ def bench_backward(w, steps, warmup):
         "timing": {"ms_mean": round(kern * 1e3, 4), "ms_median": round(median(per) * 1e3, 4),
                    "ms_min": round(min(per) * 1e3, 4),
                    "note": "the three kernels of one call, between events on the launch stream"},
-        "workspace": {"delta_bytes": B * H * N * 4, "note": "caller-owned [B,H,N] fp32 scratch for D"},
+        "workspace": {"bytes": int(ws.numel()),
+                      "note": "caller-owned attn_bwd_workspace_size(B, H, N): LSE*log2(e) and -D per padded row"},
     }
 
 

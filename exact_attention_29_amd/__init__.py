@@ -2,7 +2,8 @@
 
 The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
 ``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_fwd_block_sparse``,
-``attn_bwd``, ``attn_pack_key_mask`` and ``attn_strerror`` carry the names and
+``attn_bwd``, ``attn_bwd_workspace_size``, ``attn_pack_key_mask`` and
+``attn_strerror`` carry the names and
 arguments
 of the C entry points declared in include/attn.h and only marshal arguments;
 every step of the computation runs in the HIP kernels.
@@ -17,7 +18,8 @@ import os
 import torch  # imported first: the library then binds to torch's HIP runtime
 
 __all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-           "attn_fwd_strided", "attn_fwd_block_sparse", "attn_bwd", "attn_pack_key_mask", "AttnLayout",
+           "attn_fwd_strided", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_workspace_size",
+           "attn_pack_key_mask", "AttnLayout",
            "backward", "attn_strerror", "forward", "pack_key_mask", "AttnError",
            "library_path", "load_library"]
 
@@ -26,7 +28,7 @@ _LIB_PATH = os.path.join(_PKG, "libattn.so")
 _lib = None
 
 ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH = range(5)
-EXPORTED = ("attn_bwd", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
+EXPORTED = ("attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
             "attn_fwd_strided", "attn_fwd_block_sparse", "attn_pack_key_mask", "attn_strerror")
 SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 128, 64
 
@@ -75,6 +77,8 @@ def load_library():
     lib.attn_fwd_block_sparse.restype = i32
     lib.attn_bwd.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_pack_key_mask.argtypes = [ptr, ptr, i32, i32, ptr]
     lib.attn_pack_key_mask.restype = i32
     lib.attn_strerror.argtypes = [i32]
@@ -129,16 +133,21 @@ def attn_fwd_block_sparse(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask
                                                 block_mask, stream))
 
 
-def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream):
-    """C entry point attn_bwd: raw addresses of the ten tensors."""
-    _check(load_library().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, float(scale),
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, stream):
+    """C entry point attn_bwd: raw addresses of the nine tensors and the workspace."""
+    _check(load_library().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, float(scale),
                                    int(bool(causal)), stream))
+
+
+def attn_bwd_workspace_size(B, H, N):
+    """C entry point attn_bwd_workspace_size: bytes of workspace attn_bwd needs."""
+    return int(load_library().attn_bwd_workspace_size(B, H, N))
 
 
 def backward(q, k, v, o, lse, dout, scale=None, causal=False):
     """dQ, dK, dV (bf16 [B, H, N, d]) of attention for upstream gradient dout,
     from forward's o and lse (same q, k, v, scale, causal).  Contiguous bf16
-    tensors on one GPU; the [B, H, N] fp32 scratch for D = rowsum(dO * O) is
+    tensors on one GPU; the workspace (attn_bwd_workspace_size bytes) is
     allocated here.  Launches on torch's current stream."""
     ts = (q, k, v, o, dout)
     if any(t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous() or t.device != q.device
@@ -150,10 +159,10 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False):
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale, causal,
+                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, N, d, scale, causal,
                  _stream_handle(q.device))
     return dq, dk, dv
 

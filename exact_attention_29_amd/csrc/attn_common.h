@@ -1,12 +1,13 @@
 // Pieces shared by the forward and backward attention kernels on gfx950:
 // vector types, the swizzled LDS layout of 64-row x 64-feature bf16 tiles
 // and their two read patterns, lane-half exchanges, the XCD-aware block
-// remap, and host-side checks.
+// remap, the wait-and-barrier used with LDS DMA, and host-side checks.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -71,6 +72,43 @@ __device__ __forceinline__ bf16x8 lds_read_vt(const char* p0, const char* p1) {
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+
+// Fourth word of a gfx950 buffer resource: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+
+// s_waitcnt vmcnt(N) followed by s_barrier.  A plain s_barrier: the
+// compiler's __syncthreads() would also wait for every newer DMA.  The memory
+// clobber keeps the compiler from moving memory operations across it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// Calls vm_wait_barrier<kPer * c>() for a wave-uniform c in [0, kMax]: c
+// tiles of kPer DMAs each may stay in flight.
+template <int kPer, int kMax>
+__device__ __forceinline__ void vm_wait_barrier_tiles(int c) {
+  if constexpr (kMax > 0) {
+    if (c >= kMax) {
+      vm_wait_barrier<kPer * kMax>();
+      return;
+    }
+    vm_wait_barrier_tiles<kPer, kMax - 1>(c);
+  } else {
+    vm_wait_barrier<0>();
+  }
+}
+
+// Calls f(std::integral_constant<int, I>()) for I = kFirst .. kEnd-1.
+template <int kFirst, int kEnd>
+struct Unroll {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    if constexpr (kFirst < kEnd) {
+      f(std::integral_constant<int, kFirst>());
+      Unroll<kFirst + 1, kEnd>::run(f);
+    }
+  }
+};
 
 // Host side: ATTN_OK when the current device is a gfx950 (cached per device).
 __attribute__((visibility("hidden"))) attn_status check_device();

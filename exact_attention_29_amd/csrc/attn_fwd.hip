@@ -85,9 +85,6 @@ constexpr int kLdsBytes = kStages * kStageBytes;  // 80 KiB at the default lead:
 static_assert(kLead >= 2 && kStages <= 8, "prefetch distance out of range");
 static_assert(kLdsBytes <= 160 * 1024, "LDS ring exceeds the 160 KiB of a gfx950 CU");
 
-// Fourth word of a gfx950 buffer resource: 32-bit data format, no swizzle.
-constexpr int kBufferWord3 = 0x00020000;
-
 constexpr float kTau = 8.0f;                 // slack when the reference max is set
 constexpr unsigned kRedoBits = 0x4f800000u;  // bit pattern of 2^32: a partial
                                              // row sum above it means the
@@ -115,40 +112,6 @@ struct Bf16Args {
   const int* key_len;         // [B] or null: keys j >= key_len[b] are hidden
   const uint32_t* key_bits;   // [B][ceil(N/32)] or null: bit j%32 of word j/32
                               // clear hides key j of entry b
-};
-
-// s_waitcnt vmcnt(N) followed by s_barrier.  A plain s_barrier: the
-// compiler's __syncthreads() would also wait for every newer DMA.  The memory
-// clobber keeps the compiler from moving memory operations across it.
-template <int N>
-__device__ __forceinline__ void vm_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-// Calls vm_wait_barrier<kPer * c>() for a wave-uniform c in [0, kMax]: c
-// tiles of kPer DMAs each may stay in flight.
-template <int kPer, int kMax>
-__device__ __forceinline__ void vm_wait_barrier_tiles(int c) {
-  if constexpr (kMax > 0) {
-    if (c >= kMax) {
-      vm_wait_barrier<kPer * kMax>();
-      return;
-    }
-    vm_wait_barrier_tiles<kPer, kMax - 1>(c);
-  } else {
-    vm_wait_barrier<0>();
-  }
-}
-
-// Calls f(std::integral_constant<int, I>()) for I = kFirst .. kEnd-1.
-template <int kFirst, int kEnd>
-struct Unroll {
-  template <class F>
-  __device__ __forceinline__ static void run(F&& f) {
-    if constexpr (kFirst < kEnd) {
-      f(std::integral_constant<int, kFirst>());
-      Unroll<kFirst + 1, kEnd>::run(f);
-    }
-  }
 };
 
 template <bool kCausal, int kWaves, bool kKeyMask, bool kSparse>

@@ -43,6 +43,8 @@
 #ifndef EXACT_ATTENTION_29_AMD_ATTN_H
 #define EXACT_ATTENTION_29_AMD_ATTN_H
 
+#include <stddef.h> /* size_t */
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -213,16 +215,26 @@ attn_status attn_pack_key_mask(const unsigned char *key_valid,
  *   lse              : const float [B][H][N]
  *   dq, dk, dv       : bf16 [B][H][N][d], written in full (rounded to
  *                      nearest-even from fp32 accumulators)
- *   delta            : float [B][H][N] scratch owned by the caller (D is
- *                      written there, then read); 4-byte aligned.
- * Three kernels are enqueued on `stream` (D, then dK and dV, then dQ); no
- * atomics, so the result is deterministic.  Errors as attn_fwd (every bf16
- * pointer 16-byte aligned, lse and delta 4-byte aligned).
+ *   workspace        : scratch owned by the caller, at least
+ *                      attn_bwd_workspace_size(B, H, N) bytes, 16-byte
+ *                      aligned; overwritten (it holds LSE * log2(e) and -D
+ *                      per row, rows padded to a multiple of 256), so calls
+ *                      that overlap in time need separate workspaces.
+ * Three kernels are enqueued on `stream` (the per-row terms, then dK and dV,
+ * then dQ); no atomics, so the result is deterministic.  Errors as attn_fwd
+ * (every bf16 pointer and workspace 16-byte aligned, lse 4-byte aligned).
  */
 attn_status attn_bwd(const void *q, const void *k, const void *v,
                      const void *o, const float *lse, const void *dout,
-                     void *dq, void *dk, void *dv, float *delta, int B, int H,
-                     int N, int d, float scale, int causal, void *stream);
+                     void *dq, void *dk, void *dv, void *workspace, int B,
+                     int H, int N, int d, float scale, int causal,
+                     void *stream);
+
+/*
+ * Bytes of workspace attn_bwd needs: 8 * B * H * ceil(N / 256) * 256 (two
+ * fp32 values per padded row of every head); 0 when B, H or N is below 1.
+ */
+size_t attn_bwd_workspace_size(int B, int H, int N);
 
 /* Static, human-readable text for a status code; never NULL. */
 const char *attn_strerror(attn_status status);

@@ -118,17 +118,28 @@ def test_backward_validation():
     lib = ea.load_library()
 
     def bwd(**kw):
-        ptrs = [kw.get(n, ALIGNED) for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")]
+        ptrs = [kw.get(n, ALIGNED) for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws")]
         return lib.attn_bwd(*ptrs, kw.get("B", 1), 1, kw.get("N", 100), kw.get("d", 64), 0.125, 0, None)
-    assert bwd(delta=None) == ea.ATTN_E_INVALID
+    assert bwd(ws=None) == ea.ATTN_E_INVALID
     assert bwd(dq=None) == ea.ATTN_E_INVALID
     assert bwd(d=32) == ea.ATTN_E_INVALID
     assert bwd(N=0) == ea.ATTN_E_INVALID
     assert bwd(dout=ALIGNED + 8) == ea.ATTN_E_ALIGN
-    assert bwd(delta=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    assert bwd(ws=ALIGNED + 4) == ea.ATTN_E_ALIGN
     import torch
     if not torch.cuda.is_available():
         assert bwd(lse=ALIGNED + 4) == ea.ATTN_E_DEVICE
+
+
+def test_backward_workspace_size():
+    # two fp32 values per row of every head, rows padded to a multiple of 256
+    size = ea.attn_bwd_workspace_size
+    assert size(1, 1, 1) == 2 * 256 * 4
+    assert size(1, 1, 256) == 2 * 256 * 4
+    assert size(1, 1, 257) == 2 * 512 * 4
+    assert size(8, 12, 1024) == 2 * 8 * 12 * 1024 * 4
+    assert size(1, 16, 11616) == 2 * 16 * 11776 * 4
+    assert size(0, 1, 1) == 0 and size(1, 0, 1) == 0 and size(1, 1, 0) == 0
 
 
 def test_pack_key_mask_validation():
