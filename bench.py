@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_29_amd", "csrc", "attn_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_29_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak at H=16,d=64,P=11616"
 
@@ -45,8 +45,13 @@ def log(*a):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernel's sources (the traffic counters are only
+    reported for the source they were taken on)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(workload_name):
