@@ -613,7 +613,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   }
   int t = 1;
   // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
-  if (t + kStagesK - 1 < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
+  if (t < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
   for (; t + kStagesK - 1 < t_fast_end; t += kStagesK) {
     // tiles t .. t+kStagesK-1 sit in stages 1, 2, .., kStagesK-1, 0
     Unroll<0, kStagesK>::run([&](auto i) {
@@ -621,7 +621,18 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       tile_fast(t + I, std::integral_constant<int, (I + 1) % kStagesK>());
     });
   }
-  for (; t < n_tiles; ++t) tile_general(t);
+  // A last, partial turn of the ring (short rows: most of a causal or short
+  // sequence's tiles are here), in a copy of its own so that the loop above
+  // stays branch-free.  Each wave handles every tile exactly once, fast
+  // below its t_fast_end and general from there on, so all waves meet the
+  // same barriers.
+  if (t < t_fast_end) {
+    Unroll<0, kStagesK - 1>::run([&](auto i) {
+      constexpr int I = decltype(i)::value;
+      if (t + I < t_fast_end) tile_fast(t + I, std::integral_constant<int, (I + 1) % kStagesK>());
+    });
+  }
+  for (t = t_fast_end; t < n_tiles; ++t) tile_general(t);
   // the last half tile's PV
   if (n_half >= 1 && n_half - 1 <= last_h) {
     if ((n_half - 1) & 1) compute_pv(stage_base(n_half - 1), 1, pB);
