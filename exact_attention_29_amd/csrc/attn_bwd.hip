@@ -309,8 +309,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int jf = kCausal ? key0 / 32 : 0;
   // Tiles t0 .. t0+kHead-1 run on the general path; then tiles whose two
   // steps are fast in every wave (2t > the last wave's first half, 2t+1 <
-  // jl) run pipelined, in whole turns of the ring; the rest on the general
-  // path again.
+  // jl) run pipelined, in whole turns of the ring and a last partial one;
+  // the rest on the general path again.
   constexpr int kHead = kCausal ? (kWaves + 1) / 2 : 1;
   const int t_fast_end = jl >= 2 ? (jl - 2) / 2 + 1 : 0;
   const Dma dma(qg, dog, n, wave, lane, a.ws, 2 * a.bh_count * a.n_pad, bh, a.n_pad, a.bh_count);
@@ -523,9 +523,16 @@ bwd_dkdv_kernel(BwdArgs a) {
     Unroll<0, kStages>::run([&](auto i) {
       tile(t + decltype(i)::value, std::integral_constant<int, (kHead + decltype(i)::value) % kStages>(), kFast());
     });
+  // the last, partial turn of fast tiles (short sequences), then the rest on
+  // the general path from the same turn on (skipping what ran fast)
+  if (t < t_fast_end)
+    Unroll<0, kStages - 1>::run([&](auto i) {
+      if (t + decltype(i)::value < t_fast_end)
+        tile(t + decltype(i)::value, std::integral_constant<int, (kHead + decltype(i)::value) % kStages>(), kFast());
+    });
   for (; t < t_end; t += kStages)
     Unroll<0, kStages>::run([&](auto i) {
-      if (t + decltype(i)::value < t_end)
+      if (t + decltype(i)::value >= t_fast_end && t + decltype(i)::value < t_end)
         tile(t + decltype(i)::value, std::integral_constant<int, (kHead + decltype(i)::value) % kStages>(),
              kGeneral());
     });
@@ -783,9 +790,14 @@ bwd_dq_kernel(BwdArgs a) {
     Unroll<0, kStages>::run([&](auto i) {
       tile(t + decltype(i)::value, std::integral_constant<int, (kHead + decltype(i)::value) % kStages>(), kFast());
     });
+  if (t < t_fast_end)
+    Unroll<0, kStages - 1>::run([&](auto i) {
+      if (t + decltype(i)::value < t_fast_end)
+        tile(t + decltype(i)::value, std::integral_constant<int, (kHead + decltype(i)::value) % kStages>(), kFast());
+    });
   for (; t < t_end; t += kStages)
     Unroll<0, kStages>::run([&](auto i) {
-      if (t + decltype(i)::value < t_end)
+      if (t + decltype(i)::value >= t_fast_end && t + decltype(i)::value < t_end)
         tile(t + decltype(i)::value, std::integral_constant<int, (kHead + decltype(i)::value) % kStages>(),
              kGeneral());
     });
