@@ -261,7 +261,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, k_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t v_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, v_bytes, kBufferWord3);
-  auto dma_tile = [&](int pos, char* stage_base) {
+  auto dma_tile = [&](int pos, char* stage_base) __attribute__((always_inline)) {
     const int kt = kt_of(pos);
     char* kd = stage_base + wave_s * 1024;
     if ((kt + 1) * kBc <= n) {
@@ -296,7 +296,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // those of tiles t+3 .. t+kLeadK (the ones that exist) may still fly.  Every
   // LDS read of the stage the next DMA overwrites has already fed an MFMA, so
   // the barrier needs no LDS wait.
-  auto dma_barrier = [&](int t) {
+  auto dma_barrier = [&](int t) __attribute__((always_inline)) {
     vm_wait_barrier_tiles<kDmaPerTile, kLeadK - 2>(min(kLeadK - 2, max(0, n_tiles - 3 - t)));
   };
 
@@ -335,7 +335,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // covers keys 32*j .. 32*j+31: tile j/2 (LDS stage (j/2) % 4), rows 32*(j%2)..
   //
   // S^T = K Q^T: s holds keys 32*j + 8*(r/4) + 4*hi + r%4 of query qi.
-  auto compute_s = [&](const char* stage_base, int h, f32x16& s) {
+  auto compute_s = [&](const char* stage_base, int h, f32x16& s) __attribute__((always_inline)) {
     const char* kb = stage_base + 32 * h * kRow;
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kb, k_off[0]), qop[0], zero16, 0, 0, 0);
 #pragma unroll
@@ -343,7 +343,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kb, k_off[ks]), qop[ks], s, 0, 0, 0);
   };
   // O^T += V^T P^T over one half tile; pop[tt] covers its keys 16*tt .. +15.
-  auto compute_pv = [&](const char* stage_base, int h, const bf16x8 (&pop)[2]) {
+  auto compute_pv = [&](const char* stage_base, int h, const bf16x8 (&pop)[2]) __attribute__((always_inline)) {
     const char* vb = stage_base + 32 * h * kRow;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -366,7 +366,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // One mask word covers a half tile's 32 keys, the same for every lane (a
   // scalar load).  Register r holds key 8*(r/4) + 4*hi + r%4: its 64-lane
   // condition is built on the scalar unit and selects with one v_cndmask.
-  auto apply_bits = [&](uint32_t vis, f32x16& s) {
+  auto apply_bits = [&](uint32_t vis, f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int k0 = 8 * (r >> 2) + (r & 3);
@@ -375,7 +375,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       s[r] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? s[r] : -INFINITY;
     }
   };
-  auto apply_mask = [&](int j, f32x16& s) {
+  auto apply_mask = [&](int j, f32x16& s) __attribute__((always_inline)) {
     if (kKeyMask) apply_bits(mask_row[j], s);  // j < n_half <= ceil(N/32)
     if (!kKeyMask || needs_lim(j)) {
       const int lim = kCausal ? min(qi, n_k - 1) : n_k - 1;  // last visible key
@@ -390,7 +390,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 
   // exp2(c*s - m) for the 16 scores, packed into the two bf16 P operands;
   // returns this lane's fp32 partial row sum.
-  auto exp_pack = [&](const f32x16& s, float m, bf16x8 (&pop)[2]) -> float {
+  auto exp_pack = [&](const f32x16& s, float m, bf16x8 (&pop)[2]) -> float __attribute__((always_inline)) {
     float lsum = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -415,7 +415,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // probabilities are taken against; it is raised only when some row's max
   // exceeds it by more than kTau.  Any reference gives the same O and LSE.
   // Returns the factor acc must be scaled by (1 when unchanged).
-  auto softmax_exact = [&](const f32x16& s, bf16x8 (&pop)[2], bool& raised) -> float {
+  auto softmax_exact = [&](const f32x16& s, bf16x8 (&pop)[2], bool& raised) -> float __attribute__((always_inline)) {
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
@@ -438,7 +438,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // General step (any j): j is the half tile being softmaxed; s_cur/p_cur its
   // buffers, s_nxt receives S(j+1), p_prv holds P(j-1).
   auto step_general = [&](int j, f32x16& s_cur, bf16x8 (&p_cur)[2], f32x16& s_nxt,
-                          const bf16x8 (&p_prv)[2]) {
+                          const bf16x8 (&p_prv)[2]) __attribute__((always_inline)) {
     if (j >= 1 && j - 1 <= last_h) compute_pv(stage_base(j - 1), (j - 1) & 1, p_prv);
     if (j + 1 < n_half && j + 1 <= last_h) compute_s(stage_base(j + 1), (j + 1) & 1, s_nxt);
     if (j <= last_h) {
@@ -454,7 +454,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     bf16x8 v[2][2];
     bf16x8 k[4];
   };
-  auto load_ops = [&](const char* pv_base, int pv_h, const char* s_base, int s_h, Ops& o) {
+  auto load_ops = [&](const char* pv_base, int pv_h, const char* s_base, int s_h, Ops& o) __attribute__((always_inline)) {
     const char* vb = pv_base + 32 * pv_h * kRow;
     const char* kb = s_base + 32 * s_h * kRow;
 #pragma unroll
@@ -476,7 +476,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // with their FMA, sum and bf16 packing).
   auto step_fast = [&](const Ops& cur, Ops& nxt, const char* npv_base, int npv_h,
                        const char* ns_base, int ns_h, f32x16& s_cur, bf16x8 (&p_cur)[2],
-                       f32x16& s_nxt, const bf16x8 (&p_prv)[2], uint32_t vis) {
+                       f32x16& s_nxt, const bf16x8 (&p_prv)[2], uint32_t vis) __attribute__((always_inline)) {
     // with a key mask, hide the masked keys of this half tile first (nothing
     // to do, and no instruction spent, when all 32 keys take part)
     if (kKeyMask && vis != 0xffffffffu) apply_bits(vis, s_cur);
@@ -543,7 +543,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   bf16x8 pA[2], pB[2];
 
   // one tile t (half tiles 2t, 2t+1) on the general path
-  auto tile_general = [&](int t) {
+  auto tile_general = [&](int t) __attribute__((always_inline)) {
     step_general(2 * t, sA, pA, sB, pB);
     if (2 * t + 1 < n_half) step_general(2 * t + 1, sB, pB, sA, pA);
     dma_barrier(t);
@@ -554,7 +554,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // first half, S(2t+2) from the next tile's first half); step 2t+1 reads A
   // for step 2t+2 (PV(2t+1), S(2t+3): second halves).
   Ops opA, opB;
-  auto tile_fast = [&](int t, auto stage_tag) {
+  auto tile_fast = [&](int t, auto stage_tag) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_tag)::value;
     char* const b_cur = stage_ptr(st);
     char* const b_next = stage_ptr((st + 1) % kStagesK);
