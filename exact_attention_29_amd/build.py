@@ -1,6 +1,7 @@
 """Compile the HIP library in-tree for gfx950 (cross-compiles without a GPU)."""
 
 import os
+import re
 import subprocess
 import sys
 
@@ -9,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
+# The compiler's per-kernel resource report of the last build (registers,
+# stack, occupancy, LDS), one "kernel: key=value ..." line per kernel.
+RESOURCES = os.path.join(PKG, "libattn.resources.txt")
 
 # Packed fp32 ops are disabled on purpose: hipcc would otherwise emit
 # v_pk_{add,mul,fma}_f32 from ordinary float code.
@@ -22,7 +26,27 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Xarch_device", "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+_REMARK = re.compile(r"remark:\s+(.*?)\s*\[-Rpass-analysis=kernel-resource-usage\]")
+
+
+def resource_report(output):
+    """Collect the kernel-resource-usage remarks of a compile into
+    {mangled kernel name: {field: value}} (values as the compiler prints them)."""
+    kernels, cur = {}, None
+    for line in output.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        text = m.group(1)
+        if text.startswith("Function Name:"):
+            cur = kernels.setdefault(text.split(":", 1)[1].strip(), {})
+        elif cur is not None and ":" in text:
+            key, val = text.rsplit(":", 1)
+            cur[key.strip()] = val.strip()
+    return kernels
 
 
 def hipcc():
@@ -36,8 +60,10 @@ def build(verbose=False, extra_flags=()):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    kernels = resource_report(proc.stdout)
     out = "\n".join(line for line in proc.stdout.splitlines()
-                    if "packed-fp32-ops' is not a recognized feature" not in line)
+                    if "packed-fp32-ops' is not a recognized feature" not in line
+                    and "kernel-resource-usage" not in line and not line.startswith(" "))
     if proc.returncode != 0:
         if os.path.exists(tmp):
             os.remove(tmp)
@@ -45,6 +71,10 @@ def build(verbose=False, extra_flags=()):
     if verbose and out.strip():
         print(out, flush=True)
     os.replace(tmp, LIB)
+    with open(RESOURCES, "w") as f:
+        for name in sorted(kernels):
+            f.write(name + ": " + " ".join("%s=%s" % (k.replace(" ", "_"), v)
+                                            for k, v in kernels[name].items()) + "\n")
     return LIB
 
 
