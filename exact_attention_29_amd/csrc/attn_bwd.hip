@@ -62,7 +62,7 @@ struct BwdArgs {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;
-  float* ws;  // [B*H][n_pad] L2 = LSE*log2(e), then [B*H][n_pad] -D
+  float* ws;  // per head bh, at bh * 2 * n_pad: L2[n_pad] = LSE*log2(e), then -D[n_pad]
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -103,8 +103,9 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a, long long rows
     l2 = a.lse[g] * kLog2e;
     nd = -acc;
   }
-  a.ws[r] = l2;
-  a.ws[rows + r] = nd;
+  float* const hs = a.ws + (size_t)bh * 2 * a.n_pad;  // this head's L2, then -D
+  hs[row] = l2;
+  hs[a.n_pad + row] = nd;
 }
 
 // 16-byte chunk `ch` of row `row` of a [n][64] bf16 matrix, zero past row n.
@@ -176,10 +177,11 @@ struct TileDma {
   __amdgpu_buffer_rsrc_t r0, r1, rs;
   const uint16_t* g0;
   const uint16_t* g1;
-  int n, lane, row_in, chunk, lane_off, wave_s, stat_voff, stat_row0;
+  int n, lane, row_in, chunk, lane_off, wave_s, stat_voff;
 
-  __device__ TileDma(const uint16_t* m0, const uint16_t* m1, int n_, int wave, int lane_, float* ws,
-                     int ws_floats, int bh, int n_pad, int bh_count)
+  // stats: this head's L2[n_pad], then -D[n_pad] (dK/dV only)
+  __device__ TileDma(const uint16_t* m0, const uint16_t* m1, int n_, int wave, int lane_, const float* stats,
+                     int n_pad)
       : g0(m0), g1(m1), n(n_), lane(lane_) {
     row_in = 8 * wave + (lane >> 3);
     chunk = (lane & 7) ^ swz(row_in);
@@ -187,13 +189,12 @@ struct TileDma {
     wave_s = __builtin_amdgcn_readfirstlane(wave);
     r0 = __builtin_amdgcn_make_buffer_rsrc((void*)m0, (short)0, n * kRow, kBufferWord3);
     r1 = __builtin_amdgcn_make_buffer_rsrc((void*)m1, (short)0, n * kRow, kBufferWord3);
-    stat_voff = stat_row0 = 0;
+    stat_voff = 0;
     if constexpr (kStats) {
       // chunk ci of a tile's stats: L2 in chunks 0-15, -D in chunks 16-31
       const int ci = kStatLanes * wave + lane;
-      stat_voff = ci < 16 ? 16 * ci : bh_count * n_pad * 4 + 16 * (ci - 16);
-      stat_row0 = bh * n_pad;
-      rs = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, ws_floats * 4, kBufferWord3);
+      stat_voff = ci < 16 ? 16 * ci : n_pad * 4 + 16 * (ci - 16);
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)stats, (short)0, n_pad * 8, kBufferWord3);
     }
   }
 
@@ -223,7 +224,7 @@ struct TileDma {
     if constexpr (kStats) {
       if (lane < kStatLanes)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sb + 2 * kTileBytes + wave_s * kStatLanes * 16),
-                                                 16, stat_voff, (stat_row0 + t * kBwdTile) * 4, 0, 0);
+                                                 16, stat_voff, t * kBwdTile * 4, 0, 0);
     }
   }
 };
@@ -313,7 +314,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   // the rest on the general path again.
   constexpr int kHead = kCausal ? (kWaves + 1) / 2 : 1;
   const int t_fast_end = jl >= 2 ? (jl - 2) / 2 + 1 : 0;
-  const Dma dma(qg, dog, n, wave, lane, a.ws, 2 * a.bh_count * a.n_pad, bh, a.n_pad, a.bh_count);
+  const Dma dma(qg, dog, n, wave, lane, a.ws + (size_t)bh * 2 * a.n_pad, a.n_pad);
 
   // a step is fast (pipelined, unmasked) when it has a step on each side
   auto fast = [&](int j) { return j >= jf + 1 && j <= jl - 1; };
@@ -601,9 +602,9 @@ bwd_dq_kernel(BwdArgs a) {
     qop[ks] = row_operand(qg, qi, ks, hi, n);
     dop[ks] = row_operand(dog, qi, ks, hi, n);
   }
-  const size_t ws_row = (size_t)bh * a.n_pad + qi;
-  const float lse2 = a.ws[ws_row];
-  const float ndl = a.ws[(size_t)a.bh_count * a.n_pad + ws_row];
+  const float* const hs = a.ws + (size_t)bh * 2 * a.n_pad;  // this head's L2, then -D
+  const float lse2 = hs[qi];
+  const float ndl = hs[a.n_pad + qi];
   f32x16 nd16;  // -D of this lane's query in every register: dP^T starts there
 #pragma unroll
   for (int r = 0; r < 16; ++r) nd16[r] = ndl;
@@ -627,7 +628,7 @@ bwd_dq_kernel(BwdArgs a) {
   constexpr int kHead = 1;
   const int jl_min = kCausal ? min(qb * kWaves, 2 * t_end - 1) : 2 * t_end - 1;
   const int t_fast_end = jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
-  const Dma dma(kg, vg, n, wave, lane, nullptr, 0, bh, a.n_pad, a.bh_count);
+  const Dma dma(kg, vg, n, wave, lane, nullptr, 0);
 
   auto fast = [&](int j) { return j >= 1 && j <= jl - 1; };
   auto half_stage = [&](int j) { return stage((j / 2) % kStages); };
@@ -867,7 +868,7 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
                                 int N, int d, float scale, int causal, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_E_INVALID;
   if (B < 1 || H < 1 || N < 1 || d != kD || !std::isfinite(scale)) return ATTN_E_INVALID;
-  if ((long long)B * H * N * d >= (1LL << 31)) return ATTN_E_INVALID;
+  if (!sizes_fit(B, H, N)) return ATTN_E_INVALID;
   const void* vec[] = {q, k, v, o, dout, dq, dk, dv, workspace};
   for (const void* p : vec)
     if (misaligned(p, 16)) return ATTN_E_ALIGN;

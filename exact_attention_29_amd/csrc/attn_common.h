@@ -115,4 +115,12 @@ __attribute__((visibility("hidden"))) attn_status check_device();
 
 inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
+// Sizes every kernel handles: tile, row-block and workgroup counts are ints
+// (B*H*ceil(N/32) bounds them all), and one head's rows are addressed with
+// 32-bit byte offsets (N rows of 128 bytes).  Offsets between heads and
+// batch entries are 64-bit, so a tensor may exceed 2^31 elements.
+inline bool sizes_fit(int B, int H, int N) {
+  return (long long)B * H * ((N + 31LL) / 32) < (1LL << 31) && N < (1 << 24);
+}
+
 }  // namespace attn_detail

@@ -865,7 +865,7 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
                      int B, int H, int N, int d, float scale) {
   if (!q || !k || !v || !o || !lse) return ATTN_E_INVALID;
   if (B < 1 || H < 1 || N < 1 || d != kD || !std::isfinite(scale)) return ATTN_E_INVALID;
-  if ((long long)B * H * N * d >= (1LL << 31)) return ATTN_E_INVALID;
+  if (!sizes_fit(B, H, N)) return ATTN_E_INVALID;
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
       misaligned(lse, 4))
     return ATTN_E_ALIGN;
@@ -1039,7 +1039,7 @@ extern "C" attn_status attn_fwd_block_sparse(const void* q, const void* k, const
 extern "C" attn_status attn_pack_key_mask(const unsigned char* key_valid, unsigned* key_bits,
                                           int B, int N, void* stream) {
   if (!key_valid || !key_bits || B < 1 || N < 1) return ATTN_E_INVALID;
-  if ((long long)B * N >= (1LL << 31)) return ATTN_E_INVALID;
+  if (!sizes_fit(B, 1, N)) return ATTN_E_INVALID;
   if (misaligned(key_bits, 4)) return ATTN_E_ALIGN;
   const attn_status st = check_device();
   if (st != ATTN_OK) return st;

@@ -52,7 +52,9 @@ extern "C" {
 typedef enum attn_status {
     ATTN_OK = 0,
     /* A null pointer; B, H or N below 1; d other than 64; a non-finite
-     * scale; or B*H*N*d at or above 2^31 elements. */
+     * scale; N at or above 2^24 (16,777,216); or B*H*ceil(N/32) at or above
+     * 2^31.  (The tensors themselves may hold more than 2^31 elements:
+     * offsets between heads and batch entries are 64-bit.) */
     ATTN_E_INVALID = 1,
     /* q, k, v or o not 16-byte aligned (the kernels move 128-bit vectors;
      * rows of 64 features keep every row aligned), or lse not 4-byte
@@ -194,7 +196,8 @@ attn_status attn_fwd_block_sparse(const void *q, const void *k, const void *v,
  * the key takes part); key_bits: unsigned [B][ceil(N/32)] device array,
  * 4-byte aligned, written in full (bits past N are 0).  Enqueued on
  * `stream` like the attention calls; the caller owns both buffers.
- * ATTN_E_INVALID for a null pointer, B or N below 1 or B*N >= 2^31;
+ * ATTN_E_INVALID for a null pointer, B or N below 1, N >= 2^24 or
+ * B*ceil(N/32) >= 2^31;
  * ATTN_E_ALIGN for a misaligned key_bits; ATTN_E_DEVICE, ATTN_E_LAUNCH as
  * attn_fwd.
  */

@@ -35,3 +35,47 @@ def assert_within(err, bar, what=""):
     assert err["finite"], f"{what}: non-finite output"
     for key, lim in bar.items():
         assert err[key] <= lim, f"{what}: {key} = {err[key]:.3e} > {lim:.1e} ({err})"
+
+
+# Gradients (bf16 I/O): P and dS are rounded to bf16 before their products,
+# O enters D = rowsum(dO * O) as bf16, and the results are rounded to bf16;
+# each gradient stays within 1e-2 relative Frobenius error and within 2e-2
+# of max|ref| at every element.  dS = P * (dP - D) cancels where the exact
+# gradient is (nearly) zero, so the denominators are max(|ref|, 0.05 |mag|),
+# mag being the same gradient with every cancelling difference replaced by
+# its magnitude (grad_magnitudes).
+GRAD = dict(rel_fro=1e-2, rel_max=2e-2)
+
+
+def grad_magnitudes(q, k, v, do, scale, causal):
+    """The gradients with every cancelling difference replaced by its
+    magnitude: dS -> P * (|dP| + |D|), dO -> |dO| (float64, from the oracle's
+    own steps)."""
+    from oracle import backward as ob
+    from workloads import to_f64
+    q, k, v, do = (to_f64(t) for t in (q, k, v, do))
+    B, H, N, d = q.shape
+    mq, mk, mv = (np.zeros((B, H, N, d)) for _ in range(3))
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            p = ob._probabilities(q[b, h], k[b, h], scale, causal, rows)
+            dp = ob._dp(do[b, h], v[b, h])
+            delta = ob._delta(p, dp)
+            mds = p * (np.abs(dp) + np.abs(delta)[:, None])
+            mq[b, h] = abs(scale) * (mds @ np.abs(k[b, h]))
+            mk[b, h] = abs(scale) * (mds.T @ np.abs(q[b, h]))
+            mv[b, h] = p.T @ np.abs(do[b, h])
+    return mq, mk, mv
+
+
+def assert_grad_within(name, got, ref, mag):
+    from workloads import to_f64
+    got = to_f64(got)
+    err = got - ref
+    fro = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 0.05 * np.linalg.norm(mag), 1e-300))
+    mx = float(np.abs(err).max() / max(np.abs(ref).max(), 0.05 * np.abs(mag).max(), 1e-300))
+    print(f"[bwd] {name}: rel_fro {fro:.2e}  max/maxref {mx:.2e}", flush=True)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    assert fro <= GRAD["rel_fro"], f"{name}: relative Frobenius error {fro:.3e} > {GRAD['rel_fro']}"
+    assert mx <= GRAD["rel_max"], f"{name}: max error {mx:.3e} of max|ref| > {GRAD['rel_max']}"

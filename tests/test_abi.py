@@ -124,11 +124,14 @@ def test_backward_validation():
     assert bwd(dq=None) == ea.ATTN_E_INVALID
     assert bwd(d=32) == ea.ATTN_E_INVALID
     assert bwd(N=0) == ea.ATTN_E_INVALID
+    assert bwd(N=1 << 24) == ea.ATTN_E_INVALID
+    assert bwd(B=1 << 26, N=1024) == ea.ATTN_E_INVALID
     assert bwd(dout=ALIGNED + 8) == ea.ATTN_E_ALIGN
     assert bwd(ws=ALIGNED + 4) == ea.ATTN_E_ALIGN
     import torch
     if not torch.cuda.is_available():
         assert bwd(lse=ALIGNED + 4) == ea.ATTN_E_DEVICE
+        assert bwd(B=1 << 20, N=64) == ea.ATTN_E_DEVICE   # 2^32 elements per tensor
 
 
 def test_backward_workspace_size():
@@ -148,11 +151,13 @@ def test_pack_key_mask_validation():
     assert lib.attn_pack_key_mask(ALIGNED, None, 1, 8, None) == ea.ATTN_E_INVALID
     assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 0, 8, None) == ea.ATTN_E_INVALID
     assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 1, 0, None) == ea.ATTN_E_INVALID
-    assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 1 << 16, 1 << 15, None) == ea.ATTN_E_INVALID
+    assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 1 << 30, 64, None) == ea.ATTN_E_INVALID
+    assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 1, 1 << 24, None) == ea.ATTN_E_INVALID
     assert lib.attn_pack_key_mask(ALIGNED + 1, ALIGNED + 2, 1, 8, None) == ea.ATTN_E_ALIGN
     import torch
     if not torch.cuda.is_available():
         assert lib.attn_pack_key_mask(ALIGNED + 1, ALIGNED, 2, 33, None) == ea.ATTN_E_DEVICE
+        assert lib.attn_pack_key_mask(ALIGNED, ALIGNED, 1 << 16, 1 << 15, None) == ea.ATTN_E_DEVICE
 
 
 @pytest.mark.parametrize("fn", ALL_FWD)
@@ -166,7 +171,9 @@ def test_pack_key_mask_validation():
     (dict(d=32), ea.ATTN_E_INVALID),
     (dict(scale=float("nan")), ea.ATTN_E_INVALID),
     (dict(scale=float("inf")), ea.ATTN_E_INVALID),
-    (dict(B=1 << 12, H=1 << 12, N=2), ea.ATTN_E_INVALID),   # 2^31 elements
+    (dict(B=1 << 16, H=1 << 15, N=2), ea.ATTN_E_INVALID),   # 2^31 workgroup-sized row blocks
+    (dict(B=1 << 8, H=1 << 8, N=1 << 20), ea.ATTN_E_INVALID),  # B*H*ceil(N/32) = 2^31
+    (dict(N=1 << 24), ea.ATTN_E_INVALID),                   # a head's rows past 32-bit byte offsets
     (dict(q=ALIGNED + 8), ea.ATTN_E_ALIGN),
     (dict(v=ALIGNED + 2), ea.ATTN_E_ALIGN),
     (dict(o=ALIGNED + 4), ea.ATTN_E_ALIGN),
@@ -183,6 +190,10 @@ def test_valid_arguments_without_a_gpu_report_no_device(fn):
         pytest.skip("a GPU is present")
     assert call(fn) == ea.ATTN_E_DEVICE
     assert call(fn, lse=ALIGNED + 4, causal=1, scale=-0.5, N=1) == ea.ATTN_E_DEVICE
+    # tensors past 2^31 elements pass validation (64-bit offsets between heads)
+    assert call(fn, B=1 << 12, H=1 << 12, N=2) == ea.ATTN_E_DEVICE
+    assert call(fn, B=2, H=8200, N=2048) == ea.ATTN_E_DEVICE
+    assert call(fn, N=(1 << 24) - 1) == ea.ATTN_E_DEVICE
     if fn in MASKED:
         assert call(fn, key_len=ALIGNED + 4, key_bits=ALIGNED + 8) == ea.ATTN_E_DEVICE
 

@@ -21,19 +21,16 @@ replaced by P * (|dP| + |D|) (and dO by |dO| for dV); for random data |ref|
 is the larger one and the bar above is unchanged.
 """
 
-import numpy as np
 import pytest
 import torch
 
 import exact_attention_29_amd as ea
 from oracle import attention_backward
-from oracle import backward as ob
+from tests.parity import assert_grad_within, grad_magnitudes
 from workloads import WORKLOADS, Workload, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-REL_FRO = 1e-2
-REL_MAX = 2e-2
 
 
 def grads_gpu(q, k, v, do, scale, causal):
@@ -42,36 +39,6 @@ def grads_gpu(q, k, v, do, scale, causal):
     dq, dk, dv = ea.backward(q, k, v, o, lse, do, scale=scale, causal=causal)
     torch.cuda.synchronize()
     return dq, dk, dv
-
-
-def magnitudes(q, k, v, do, scale, causal):
-    """The gradients with every cancelling difference replaced by its
-    magnitude: dS -> P * (|dP| + |D|), dO -> |dO| (float64, as the oracle)."""
-    q, k, v, do = (to_f64(t) for t in (q, k, v, do))
-    B, H, N, d = q.shape
-    mq, mk, mv = (np.zeros((B, H, N, d)) for _ in range(3))
-    rows = np.arange(N)
-    for b in range(B):
-        for h in range(H):
-            p = ob._probabilities(q[b, h], k[b, h], scale, causal, rows)
-            dp = ob._dp(do[b, h], v[b, h])
-            delta = ob._delta(p, dp)
-            mds = p * (np.abs(dp) + np.abs(delta)[:, None])
-            mq[b, h] = abs(scale) * (mds @ np.abs(k[b, h]))
-            mk[b, h] = abs(scale) * (mds.T @ np.abs(q[b, h]))
-            mv[b, h] = p.T @ np.abs(do[b, h])
-    return mq, mk, mv
-
-
-def check(name, got, ref, mag):
-    got = to_f64(got)
-    err = got - ref
-    fro = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 0.05 * np.linalg.norm(mag), 1e-300))
-    mx = float(np.abs(err).max() / max(np.abs(ref).max(), 0.05 * np.abs(mag).max(), 1e-300))
-    print(f"[bwd] {name}: rel_fro {fro:.2e}  max/maxref {mx:.2e}", flush=True)
-    assert np.all(np.isfinite(got)), f"{name}: non-finite"
-    assert fro <= REL_FRO, f"{name}: relative Frobenius error {fro:.3e} > {REL_FRO}"
-    assert mx <= REL_MAX, f"{name}: max error {mx:.3e} of max|ref| > {REL_MAX}"
 
 
 def inputs(B, H, N, seed, sigma=1.0):
@@ -87,9 +54,9 @@ def test_backward_sizes(n, causal):
     q, k, v, do = inputs(1, 2, n, seed=1100 + n)
     dq, dk, dv = grads_gpu(q, k, v, do, 0.125, causal)
     rq, rk, rv = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), 0.125, causal=causal)
-    mags = magnitudes(q, k, v, do, 0.125, causal)
+    mags = grad_magnitudes(q, k, v, do, 0.125, causal)
     for name, g, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv), mags):
-        check(f"{name} n={n} causal={causal}", g, r, m)
+        assert_grad_within(f"{name} n={n} causal={causal}", g, r, m)
 
 
 @pytest.mark.parametrize("n", [700, 1337, 2100])
@@ -101,9 +68,9 @@ def test_backward_pipeline_lengths(n, causal):
     q, k, v, do = inputs(1, 1, n, seed=1400 + n)
     dq, dk, dv = grads_gpu(q, k, v, do, 0.125, causal)
     rq, rk, rv = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), 0.125, causal=causal)
-    mags = magnitudes(q, k, v, do, 0.125, causal)
+    mags = grad_magnitudes(q, k, v, do, 0.125, causal)
     for name, g, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv), mags):
-        check(f"{name} n={n} causal={causal}", g, r, m)
+        assert_grad_within(f"{name} n={n} causal={causal}", g, r, m)
 
 
 @pytest.mark.parametrize("name", ["bert_large", "gpt2_small_causal"])
@@ -115,9 +82,9 @@ def test_backward_workload_shapes(name):
     do = make_inputs(Workload("do", 2, w.H, w.N, 64, "bf16", 1.0, w.scale, w.causal, w.seed + 50, ""))[0]
     dq, dk, dv = grads_gpu(q, k, v, do, w.scale, w.causal)
     rq, rk, rv = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), w.scale, causal=w.causal)
-    mags = magnitudes(q, k, v, do, w.scale, w.causal)
+    mags = grad_magnitudes(q, k, v, do, w.scale, w.causal)
     for nm, g, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv), mags):
-        check(f"{nm} {name}", g, r, m)
+        assert_grad_within(f"{nm} {name}", g, r, m)
 
 
 def test_backward_deterministic():
@@ -132,6 +99,6 @@ def test_backward_scale_sign():
     q, k, v, do = inputs(1, 2, 150, seed=1300)
     dq, dk, dv = grads_gpu(q, k, v, do, -0.2, False)
     rq, rk, rv = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), -0.2)
-    mags = magnitudes(q, k, v, do, -0.2, False)
+    mags = grad_magnitudes(q, k, v, do, -0.2, False)
     for name, g, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv), mags):
-        check(f"{name} scale=-0.2", g, r, m)
+        assert_grad_within(f"{name} scale=-0.2", g, r, m)

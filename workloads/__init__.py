@@ -103,3 +103,24 @@ def sample_rows(n, count, seed=12345):
     rest = max(count - len(fixed), 0)
     fixed |= set(rng.integers(0, n, size=rest).tolist())
     return np.array(sorted(i for i in fixed if 0 <= i < n), dtype=np.int64)
+
+
+def make_device_normal(shape, seed, device, dtype="bf16", sigma=1.0):
+    """A seeded i.i.d. normal tensor drawn on `device` itself, for tensors too
+    large to draw on the host and copy (several GiB).  Recipe:
+    torch.Generator(device).manual_seed(seed), torch.randn(shape) in float32
+    one slice of dim 1 at a time (bounded temporary memory), times sigma,
+    rounded to dtype (round-to-nearest-even for bf16).  Checks copy the
+    slices they compare back to the host, so both sides see the same values."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=TORCH_DTYPE[dtype], device=device)
+    step = max(1, (1 << 26) // max(1, int(np.prod(shape[2:])) * shape[0]))
+    for h0 in range(0, shape[1], step):
+        h1 = min(shape[1], h0 + step)
+        x = torch.randn((shape[0], h1 - h0) + tuple(shape[2:]), generator=g, device=device,
+                        dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        out[:, h0:h1].copy_(x)
+    return out
