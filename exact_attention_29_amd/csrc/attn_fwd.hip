@@ -77,11 +77,22 @@ constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile: 16384
 #ifndef ATTN_LEAD
 #define ATTN_LEAD 3
 #endif
+// Paired barriers for 8-wave workgroups (one per CU, so the LDS has room for
+// a sixth stage): only odd tiles end in a wait and a barrier, which publish
+// the next two tiles at once and request the two after them.  Every tile
+// still gets two tiles' time to arrive; the workgroup meets half as often.
+#ifndef ATTN_PAIR
+#define ATTN_PAIR 1
+#endif
+#if ATTN_PAIR && ATTN_LEAD + 2 < 6
+#define ATTN_STAGES 6
+#else
 #define ATTN_STAGES (ATTN_LEAD + 2)
+#endif
 constexpr int kLead = ATTN_LEAD;
 constexpr int kStages = ATTN_STAGES;         // LDS ring of K/V tiles
-constexpr int kLdsBytes = kStages * kStageBytes;  // 80 KiB at the default lead:
-                                                  // two 4-wave workgroups fit a CU
+constexpr int kLdsBytes = kStages * kStageBytes;  // the largest ring (96 KiB paired);
+                                                  // 4-wave workgroups use 80 KiB, two per CU
 static_assert(kLead >= 2 && kStages <= 8, "prefetch distance out of range");
 static_assert(kLdsBytes <= 160 * 1024, "LDS ring exceeds the 160 KiB of a gfx950 CU");
 
@@ -124,8 +135,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
   static_assert(!kSparse || (kWaves * 32 == kSparseBlockQ && !kKeyMask),
                 "a block-sparse workgroup owns one query block; no key mask on that path");
-  constexpr int kLeadK = kSparse ? 2 : kLead;  // prefetch distance
-  constexpr int kStagesK = kLeadK + 2;         // LDS ring stages
+  constexpr int kLeadK = kSparse ? 2 : kLead;  // prefetch distance (unpaired ring)
+  constexpr bool kPair = ATTN_PAIR && kWaves == 8 && !kSparse;
+  constexpr int kStagesK = kPair ? 6 : kLeadK + 2;  // LDS ring stages; tile t in stage t % kStagesK
   static_assert(kLeadK >= 2 && kStagesK <= ATTN_STAGES, "ring deeper than the declared stages");
   // One LDS object per ring stage: with the stage known at compile time (the
   // steady state), the compiler can tell a stage being filled by DMA from the
@@ -298,6 +310,25 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // the barrier needs no LDS wait.
   auto dma_barrier = [&](int t) __attribute__((always_inline)) {
     vm_wait_barrier_tiles<kDmaPerTile, kLeadK - 2>(min(kLeadK - 2, max(0, n_tiles - 3 - t)));
+  };
+  // End of tile t (in stage st).  Unpaired ring: the barrier above, then
+  // tile t+1+kLeadK is requested into the stage of tile t-1.  Paired ring:
+  // nothing after an even tile; after an odd tile, every request is waited
+  // for (tiles t+2 and t+3, requested two tiles ago), the barrier publishes
+  // them, and tiles t+4 and t+5 are requested into the stages of tiles t-2
+  // and t-1, whose last reads fed MFMAs of tile t at the latest.  A tile's
+  // parity is its stage's (the ring has an even number of stages).
+  auto end_tile = [&](int t, int st) __attribute__((always_inline)) {
+    if constexpr (kPair) {
+      if (st & 1) {
+        vm_wait_barrier<0>();
+        if (t + 4 < n_tiles) dma_tile(t + 4, stage_ptr((st + 4) % kStagesK));
+        if (t + 5 < n_tiles) dma_tile(t + 5, stage_ptr((st + 5) % kStagesK));
+      }
+    } else {
+      dma_barrier(t);
+      if (t + 1 + kLeadK < n_tiles) dma_tile(t + 1 + kLeadK, stage_ptr((st + 1 + kLeadK) % kStagesK));
+    }
   };
 
 
@@ -546,8 +577,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   auto tile_general = [&](int t) __attribute__((always_inline)) {
     step_general(2 * t, sA, pA, sB, pB);
     if (2 * t + 1 < n_half) step_general(2 * t + 1, sB, pB, sA, pA);
-    dma_barrier(t);
-    if (t + 1 + kLeadK < n_tiles) dma_tile(t + 1 + kLeadK, stage_ptr((t + 1 + kLeadK) % kStagesK));
+    end_tile(t, t % kStagesK);
   };
   // one tile t whose stage is known at compile time, both steps fast.  Step
   // 2t uses operands A and reads B for step 2t+1 (PV(2t) from this tile's
@@ -562,19 +592,20 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     const uint32_t vis1 = kKeyMask ? mask_row[real_half(2 * t + 1)] : 0xffffffffu;
     step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0);  // j = 2t
     step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1);  // j = 2t + 1
-    dma_barrier(t);
-    if (t + 1 + kLeadK < n_tiles) dma_tile(t + 1 + kLeadK, stage_ptr((st + 1 + kLeadK) % kStagesK));
+    end_tile(t, st);
   };
 
-  // ---- prologue: tiles 0 and 1 into LDS, tile 2 in flight, S(0)
-  // tiles 0 .. kLeadK in flight; tiles 0 and 1 must land before the first
-  // barrier (tile t+kLeadK is issued right after the barrier ending tile t-1)
+  // ---- prologue: tiles 0 .. kFirst requested; the first kReady must land
+  // before the first barrier.  Unpaired: tiles 0 and 1 (tile t+kLeadK is
+  // requested right after the barrier ending tile t-1).  Paired: tiles 0, 1
+  // and 2 (tile 2 is read during tile 1, whose barrier publishes 3 and 4).
+  constexpr int kFirst = kPair ? 4 : kLeadK;
+  constexpr int kReady = kPair ? 3 : 2;
 #pragma unroll
-  for (int tl = 0; tl <= kLeadK; ++tl)
+  for (int tl = 0; tl <= kFirst; ++tl)
     if (tl < n_tiles) dma_tile(tl, stage_ptr(tl));
-  // tiles 0 and 1 must have landed; the rest of the min(n_tiles, kLeadK+1)
-  // issued may still fly
-  vm_wait_barrier_tiles<kDmaPerTile, kLeadK - 1>(max(0, min(n_tiles, kLeadK + 1) - 2));
+  // the rest of the min(n_tiles, kFirst+1) requested may still fly
+  vm_wait_barrier_tiles<kDmaPerTile, kFirst + 1 - kReady>(max(0, min(n_tiles, kFirst + 1) - kReady));
   if (last_h >= 0) compute_s(lds0, 0, sA);
 
   // ---- tiles: 0 on the general path, then the steady state (both half

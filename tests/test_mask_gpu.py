@@ -181,3 +181,17 @@ def test_page_mask_polarity_example_on_the_gpu():
     check(xp, xp, xp, o_keep, l_keep, scale, False, keep, FP32, "page example")
     got = round(float((o_asis - o_keep).abs().max()), g["printed_decimals"])
     assert got == g["cases"]["boolean_mask_as_is_attends_only_key_3"], got
+
+
+@pytest.mark.parametrize("n", [64 * t + r for t in range(1, 21, 3) for r in (0, 37)] + [64 * 13, 64 * 19 + 5])
+def test_key_mask_ring_lengths(n):
+    """The key-mask kernel over key-tile counts 1 .. 19 (the 8-wave kernel's
+    paired ring: partial turns and general tails of every parity), with a
+    random tenth of the keys hidden and key 0 kept."""
+    rng = np.random.default_rng(7000 + n)
+    valid = rng.random((2, n)) > 0.1
+    valid[:, 0] = True
+    q, k, v = inputs(2, 2, n, "bf16", 7100 + n)
+    o, lse = run(q, k, v, 0.125, False, key_valid=valid)
+    check(q, k, v, o, lse, 0.125, False, valid, BF16, f"mask ring N={n}")
+

@@ -102,6 +102,22 @@ def test_edge_sizes_bf16(n, causal):
     compare(w, q, k, v, o, lse)
 
 
+# Key-tile counts 1 .. 20 with whole and ragged last tiles: every length of
+# the last, partial turn of the LDS ring (6 stages without a mask, 5 causal),
+# barriers after tiles of either parity, and the general tail after each.
+RING_N = [64 * t + r for t in range(1, 21) for r in (0, 37)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", RING_N)
+def test_ring_lengths_bf16(n, causal):
+    w = bf16_workload(n, causal, B=1, H=2, seed=5000 + n)
+    print(f"[case] ring bf16 N={n} causal={causal}", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = gpu_run(q, k, v, w.scale, causal)
+    compare(w, q, k, v, o, lse)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 100, 128, 129, 257])
 def test_edge_sizes_fp32(n, causal):
