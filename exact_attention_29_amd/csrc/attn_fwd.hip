@@ -389,6 +389,16 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // Hidden keys of half tile j become -inf (ragged end or valid length,
   // causal diagonal, and with a key mask every key it hides).
   const uint32_t* const mask_row = kKeyMask ? a.key_bits + (size_t)b_entry * ((n + 31) / 32) : nullptr;
+  // Mask words are the same in every lane and read-only while the kernel
+  // runs: read through the constant address space they become scalar loads.
+  // (A vector load would share its completion counter with the K/V DMA, and
+  // waiting for it would wait for every tile in flight.)  The index is
+  // clamped to the row's last word, so reading ahead stays in the buffer.
+  const int n_words = (n + 31) / 32;
+  auto mask_word = [&](int j) -> uint32_t {
+    typedef const __attribute__((address_space(4))) uint32_t cword;
+    return ((cword*)mask_row)[min(j, n_words - 1)];
+  };
   auto needs_lim = [&](int j) {
     const int jr = real_half(j);
     return 32 * jr + 32 > n_k || (kCausal && 32 * jr + 31 > q_wave);
@@ -407,7 +417,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     }
   };
   auto apply_mask = [&](int j, f32x16& s) __attribute__((always_inline)) {
-    if (kKeyMask) apply_bits(mask_row[j], s);  // j < n_half <= ceil(N/32)
+    if (kKeyMask) apply_bits(mask_word(j), s);  // j < n_half <= ceil(N/32)
     if (!kKeyMask || needs_lim(j)) {
       const int lim = kCausal ? min(qi, n_k - 1) : n_k - 1;  // last visible key
       const int jr = real_half(j);
@@ -480,6 +490,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     }
   };
 
+  // a key-mask kernel's words of the next fast tile, loaded one tile ahead
+  uint32_t vis_next0 = 0xffffffffu, vis_next1 = 0xffffffffu;
+
   // Operands of one steady-state step: V^T for PV(j-1) and K for S(j+1).
   struct Ops {
     bf16x8 v[2][2];
@@ -507,7 +520,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // with their FMA, sum and bf16 packing).
   auto step_fast = [&](const Ops& cur, Ops& nxt, const char* npv_base, int npv_h,
                        const char* ns_base, int ns_h, f32x16& s_cur, bf16x8 (&p_cur)[2],
-                       f32x16& s_nxt, const bf16x8 (&p_prv)[2], uint32_t vis) __attribute__((always_inline)) {
+                       f32x16& s_nxt, const bf16x8 (&p_prv)[2], uint32_t vis, bool fetch_words,
+                       int word_j) __attribute__((always_inline)) {
     // with a key mask, hide the masked keys of this half tile first (nothing
     // to do, and no instruction spent, when all 32 keys take part)
     if (kKeyMask && vis != 0xffffffffu) apply_bits(vis, s_cur);
@@ -535,6 +549,13 @@ attn_fwd_bf16_kernel(Bf16Args a) {
         if (slot == 0) {
           __builtin_amdgcn_sched_barrier(0);
           load_ops(npv_base, npv_h, ns_base, ns_h, nxt);
+          // the next tile's mask words: issued here, a whole step before the
+          // next wait on LDS operands (which then also covers them)
+          if (kKeyMask && fetch_words) {
+            asm volatile("" ::: "memory");  // keeps the loads below the MFMA above
+            vis_next0 = mask_word(word_j);
+            vis_next1 = mask_word(word_j + 1);
+          }
         }
       }
       if (slot >= 1) {
@@ -588,10 +609,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     constexpr int st = decltype(stage_tag)::value;
     char* const b_cur = stage_ptr(st);
     char* const b_next = stage_ptr((st + 1) % kStagesK);
-    const uint32_t vis0 = kKeyMask ? mask_row[real_half(2 * t)] : 0xffffffffu;
-    const uint32_t vis1 = kKeyMask ? mask_row[real_half(2 * t + 1)] : 0xffffffffu;
-    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0);  // j = 2t
-    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1);  // j = 2t + 1
+    const uint32_t vis0 = vis_next0, vis1 = vis_next1;
+    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0, true, 2 * t + 2);  // j = 2t
+    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1, false, 0);        // j = 2t + 1
     end_tile(t, st);
   };
 
@@ -645,6 +665,10 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   int t = 1;
   // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
   if (t < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
+  if constexpr (kKeyMask) {
+    vis_next0 = mask_word(2);
+    vis_next1 = mask_word(3);
+  }
   for (; t + kStagesK - 1 < t_fast_end; t += kStagesK) {
     // tiles t .. t+kStagesK-1 sit in stages 1, 2, .., kStagesK-1, 0
     Unroll<0, kStagesK>::run([&](auto i) {
