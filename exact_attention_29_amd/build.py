@@ -70,6 +70,12 @@ def build(verbose=False, extra_flags=()):
         raise RuntimeError("hipcc failed (%d):\n%s" % (proc.returncode, out))
     if verbose and out.strip():
         print(out, flush=True)
+    # A warning is a mistake here (an attribute the compiler dropped, say);
+    # the host pass's note about the packed-fp32 feature is filtered above.
+    warnings = [line for line in out.splitlines() if "warning:" in line]
+    if warnings:
+        os.remove(tmp)
+        raise RuntimeError("hipcc warnings:\n%s" % out)
     os.replace(tmp, LIB)
     with open(RESOURCES, "w") as f:
         for name in sorted(kernels):

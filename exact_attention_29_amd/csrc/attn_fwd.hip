@@ -62,7 +62,10 @@ constexpr int kBc = 64;                      // keys per K/V tile (two half tile
 // per CU) without a mask, 4 (128 rows, two workgroups per CU) when causal,
 // where shorter rows per workgroup balance the triangle better.
 constexpr int kWavesFull = 8;
-constexpr int kWavesCausal = 4;
+#ifndef ATTN_CAUSAL_WAVES
+#define ATTN_CAUSAL_WAVES 4
+#endif
+constexpr int kWavesCausal = ATTN_CAUSAL_WAVES;
 // Block-sparse calls: one workgroup per 128-row query block (4 waves), a
 // 4-stage ring (prefetch distance 2) and the list of the block's key tiles
 // in LDS (at most this many: N <= 64 * 4096).
@@ -175,9 +178,24 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 
   const int n = a.n;
   const int logical = xcd_remap(blockIdx.x, a.total_tiles);
-  const int bh = logical / a.q_tiles;
-  int qt = logical - bh * a.q_tiles;
-  if (kCausal) qt = a.q_tiles - 1 - qt;  // longest rows first
+  int bh, qt;
+  if constexpr (kCausal) {
+    // Longest rows first across a block of ceil(B*H/8) heads, the heads whose
+    // tiles one XCD takes (its logical tiles are consecutive): the tiles of
+    // rank r (r-th longest) of every head in the block, then rank r+1.  The
+    // XCD's CUs then take the long tiles first and finish on short ones.
+    const int n_bh = a.total_tiles / a.q_tiles;
+    const int hb = (n_bh + 7) / 8;
+    const int blk = logical / (hb * a.q_tiles);
+    const int within = logical - blk * hb * a.q_tiles;
+    const int nh = min(hb, n_bh - blk * hb);  // heads in this block
+    const int r = within / nh;
+    bh = blk * hb + (within - r * nh);
+    qt = a.q_tiles - 1 - r;
+  } else {
+    bh = logical / a.q_tiles;
+    qt = logical - bh * a.q_tiles;
+  }
   const int b_entry = bh / a.heads;
   const int h_idx = bh - b_entry * a.heads;
   auto head_off = [&](int t) { return (size_t)(b_entry * a.sb[t] + h_idx * a.sh[t]); };
@@ -431,7 +449,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 
   // exp2(c*s - m) for the 16 scores, packed into the two bf16 P operands;
   // returns this lane's fp32 partial row sum.
-  auto exp_pack = [&](const f32x16& s, float m, bf16x8 (&pop)[2]) -> float __attribute__((always_inline)) {
+  auto exp_pack = [&](const f32x16& s, float m, bf16x8 (&pop)[2]) __attribute__((always_inline)) -> float {
     float lsum = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -456,7 +474,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // probabilities are taken against; it is raised only when some row's max
   // exceeds it by more than kTau.  Any reference gives the same O and LSE.
   // Returns the factor acc must be scaled by (1 when unchanged).
-  auto softmax_exact = [&](const f32x16& s, bf16x8 (&pop)[2], bool& raised) -> float __attribute__((always_inline)) {
+  auto softmax_exact = [&](const f32x16& s, bf16x8 (&pop)[2], bool& raised) __attribute__((always_inline)) -> float {
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
