@@ -272,8 +272,13 @@ bwd_dkdv_kernel(BwdArgs a) {
 
   const int n = a.n;
   const int logical = xcd_remap(blockIdx.x, a.total);
-  const int bh = logical / a.blocks;
-  const int kb = logical - bh * a.blocks;
+  int bh, kb;
+  if constexpr (kCausal) {
+    causal_order(logical, a.bh_count, a.blocks, bh, kb);  // key block 0 sees every query
+  } else {
+    bh = logical / a.blocks;
+    kb = logical - bh * a.blocks;
+  }
   const size_t head = (size_t)bh * n * kD;
   const uint16_t* qg = a.q + head;
   const uint16_t* kg = a.k + head;
@@ -580,9 +585,15 @@ bwd_dq_kernel(BwdArgs a) {
 
   const int n = a.n;
   const int logical = xcd_remap(blockIdx.x, a.total);
-  const int bh = logical / a.blocks;
-  int qb = logical - bh * a.blocks;
-  if (kCausal) qb = a.blocks - 1 - qb;  // longest rows first
+  int bh, qb;
+  if constexpr (kCausal) {
+    int rank;  // the last query block of a head has the longest rows
+    causal_order(logical, a.bh_count, a.blocks, bh, rank);
+    qb = a.blocks - 1 - rank;
+  } else {
+    bh = logical / a.blocks;
+    qb = logical - bh * a.blocks;
+  }
   const size_t head = (size_t)bh * n * kD;
   const uint16_t* qg = a.q + head;
   const uint16_t* kg = a.k + head;

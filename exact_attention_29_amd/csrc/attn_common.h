@@ -52,6 +52,21 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
 }
 
+// Causal order of the logical tiles: n_bh heads of `blocks` row blocks each,
+// rank 0 the longest block of a head.  One XCD takes consecutive logical
+// tiles, i.e. a block of about n_bh/8 heads; within each block of
+// ceil(n_bh/8) heads the tiles run rank by rank (the longest of every head
+// first), so the XCD's CUs start on long tiles and finish on short ones.
+// (Head by head, a long tile of the block's last heads would start last.)
+__device__ __forceinline__ void causal_order(int logical, int n_bh, int blocks, int& bh, int& rank) {
+  const int hb = (n_bh + 7) / 8;
+  const int blk = logical / (hb * blocks);
+  const int within = logical - blk * hb * blocks;
+  const int nh = min(hb, n_bh - blk * hb);  // heads in this block
+  rank = within / nh;
+  bh = blk * hb + (within - rank * nh);
+}
+
 // 16-byte chunk c of tile row r lives at chunk position c ^ swz(r) of that
 // row: the row-operand reads (16 rows, one chunk) and the transpose reads (4
 // rows, 4 chunks per half wave) then hit 64 distinct banks.

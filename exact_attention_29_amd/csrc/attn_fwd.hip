@@ -180,18 +180,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const int logical = xcd_remap(blockIdx.x, a.total_tiles);
   int bh, qt;
   if constexpr (kCausal) {
-    // Longest rows first across a block of ceil(B*H/8) heads, the heads whose
-    // tiles one XCD takes (its logical tiles are consecutive): the tiles of
-    // rank r (r-th longest) of every head in the block, then rank r+1.  The
-    // XCD's CUs then take the long tiles first and finish on short ones.
-    const int n_bh = a.total_tiles / a.q_tiles;
-    const int hb = (n_bh + 7) / 8;
-    const int blk = logical / (hb * a.q_tiles);
-    const int within = logical - blk * hb * a.q_tiles;
-    const int nh = min(hb, n_bh - blk * hb);  // heads in this block
-    const int r = within / nh;
-    bh = blk * hb + (within - r * nh);
-    qt = a.q_tiles - 1 - r;
+    int rank;  // the last query tile of a head has the longest rows
+    causal_order(logical, a.total_tiles / a.q_tiles, a.q_tiles, bh, rank);
+    qt = a.q_tiles - 1 - rank;
   } else {
     bh = logical / a.q_tiles;
     qt = logical - bh * a.q_tiles;
