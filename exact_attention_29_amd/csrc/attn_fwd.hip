@@ -80,23 +80,27 @@ constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile: 16384
 #ifndef ATTN_LEAD
 #define ATTN_LEAD 3
 #endif
-// Paired barriers for 8-wave workgroups (one per CU, so the LDS has room for
-// a sixth stage): only odd tiles end in a wait and a barrier, which publish
-// the next two tiles at once and request the two after them.  Every tile
-// still gets two tiles' time to arrive; the workgroup meets half as often.
-#ifndef ATTN_PAIR
-#define ATTN_PAIR 1
+// Grouped barriers for 8-wave workgroups (one per CU, so the LDS has room
+// for a deeper ring): only every ATTN_GROUP-th tile ends in a wait and a
+// barrier, which publish the next ATTN_GROUP tiles at once and request the
+// ATTN_GROUP after them.  Every tile still gets ATTN_GROUP tiles' time to
+// arrive; the workgroup meets ATTN_GROUP times less often.  The ring then
+// holds 2*ATTN_GROUP+2 tiles, rounded up to a multiple of ATTN_GROUP.
+#ifndef ATTN_GROUP
+#define ATTN_GROUP 2
 #endif
-#if ATTN_PAIR && ATTN_LEAD + 2 < 6
-#define ATTN_STAGES 6
+#define ATTN_GROUP_STAGES (((2 * ATTN_GROUP + 2 + ATTN_GROUP - 1) / ATTN_GROUP) * ATTN_GROUP)
+#if ATTN_GROUP > 1 && ATTN_LEAD + 2 < ATTN_GROUP_STAGES
+#define ATTN_STAGES ATTN_GROUP_STAGES
 #else
 #define ATTN_STAGES (ATTN_LEAD + 2)
 #endif
 constexpr int kLead = ATTN_LEAD;
 constexpr int kStages = ATTN_STAGES;         // LDS ring of K/V tiles
-constexpr int kLdsBytes = kStages * kStageBytes;  // the largest ring (96 KiB paired);
+constexpr int kLdsBytes = kStages * kStageBytes;  // the largest ring (96 KiB grouped by 2);
                                                   // 4-wave workgroups use 80 KiB, two per CU
-static_assert(kLead >= 2 && kStages <= 8, "prefetch distance out of range");
+static_assert(kLead >= 2 && kStages <= 9 && ATTN_GROUP >= 1 && ATTN_GROUP <= 3,
+              "prefetch distance or barrier group out of range");
 static_assert(kLdsBytes <= 160 * 1024, "LDS ring exceeds the 160 KiB of a gfx950 CU");
 
 constexpr float kTau = 8.0f;                 // slack when the reference max is set
@@ -139,8 +143,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   static_assert(!kSparse || (kWaves * 32 == kSparseBlockQ && !kKeyMask),
                 "a block-sparse workgroup owns one query block; no key mask on that path");
   constexpr int kLeadK = kSparse ? 2 : kLead;  // prefetch distance (unpaired ring)
-  constexpr bool kPair = ATTN_PAIR && kWaves == 8 && !kSparse;
-  constexpr int kStagesK = kPair ? 6 : kLeadK + 2;  // LDS ring stages; tile t in stage t % kStagesK
+  constexpr int kGroup = kWaves == 8 && !kSparse ? ATTN_GROUP : 1;  // tiles per barrier
+  constexpr int kStagesK = kGroup > 1 ? ATTN_GROUP_STAGES : kLeadK + 2;  // tile t in stage t % kStagesK
   static_assert(kLeadK >= 2 && kStagesK <= ATTN_STAGES, "ring deeper than the declared stages");
   // One LDS object per ring stage: with the stage known at compile time (the
   // steady state), the compiler can tell a stage being filled by DMA from the
@@ -160,6 +164,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #if ATTN_STAGES > 7
   __shared__ __attribute__((aligned(1024))) char lds7[kStagesK > 7 ? kStageBytes : 16];
 #endif
+#if ATTN_STAGES > 8
+  __shared__ __attribute__((aligned(1024))) char lds8[kStagesK > 8 ? kStageBytes : 16];
+#endif
   // block-sparse: the key tiles this workgroup's query block visits, ascending
   __shared__ uint16_t tile_list[kSparse ? kMaxSparseTiles : 1];
   auto stage_ptr = [&](int st) -> char* {
@@ -172,6 +179,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #endif
 #if ATTN_STAGES > 7
     p = st == 7 ? lds7 : p;
+#endif
+#if ATTN_STAGES > 8
+    p = st == 8 ? lds8 : p;
 #endif
     return p;
   };
@@ -320,19 +330,21 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   auto dma_barrier = [&](int t) __attribute__((always_inline)) {
     vm_wait_barrier_tiles<kDmaPerTile, kLeadK - 2>(min(kLeadK - 2, max(0, n_tiles - 3 - t)));
   };
-  // End of tile t (in stage st).  Unpaired ring: the barrier above, then
-  // tile t+1+kLeadK is requested into the stage of tile t-1.  Paired ring:
-  // nothing after an even tile; after an odd tile, every request is waited
-  // for (tiles t+2 and t+3, requested two tiles ago), the barrier publishes
-  // them, and tiles t+4 and t+5 are requested into the stages of tiles t-2
-  // and t-1, whose last reads fed MFMAs of tile t at the latest.  A tile's
-  // parity is its stage's (the ring has an even number of stages).
+  // End of tile t (in stage st).  Per-tile ring: the barrier above, then
+  // tile t+1+kLeadK is requested into the stage of tile t-1.  Grouped ring
+  // (g = kGroup): only tiles with t % g == 1 end in a barrier.  There every
+  // request is waited for (tiles t+2 .. t+g+1, requested one group ago), the
+  // barrier publishes them (they are read up to the next barrier, t+g), and
+  // tiles t+g+2 .. t+2g+1 are requested into the stages of tiles
+  // t-g .. t-1, whose last reads fed MFMAs of tile t at the latest.  The
+  // ring's stage count is a multiple of g, so t % g == st % g.
   auto end_tile = [&](int t, int st) __attribute__((always_inline)) {
-    if constexpr (kPair) {
-      if (st & 1) {
+    if constexpr (kGroup > 1) {
+      if ((unsigned)st % kGroup == 1u) {  // st >= 0
         vm_wait_barrier<0>();
-        if (t + 4 < n_tiles) dma_tile(t + 4, stage_ptr((st + 4) % kStagesK));
-        if (t + 5 < n_tiles) dma_tile(t + 5, stage_ptr((st + 5) % kStagesK));
+#pragma unroll
+        for (int i = kGroup + 2; i <= 2 * kGroup + 1; ++i)
+          if (t + i < n_tiles) dma_tile(t + i, stage_ptr((st + i) % kStagesK));
       }
     } else {
       dma_barrier(t);
@@ -625,11 +637,12 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   };
 
   // ---- prologue: tiles 0 .. kFirst requested; the first kReady must land
-  // before the first barrier.  Unpaired: tiles 0 and 1 (tile t+kLeadK is
-  // requested right after the barrier ending tile t-1).  Paired: tiles 0, 1
-  // and 2 (tile 2 is read during tile 1, whose barrier publishes 3 and 4).
-  constexpr int kFirst = kPair ? 4 : kLeadK;
-  constexpr int kReady = kPair ? 3 : 2;
+  // before the first barrier.  Per-tile ring: tiles 0 and 1 (tile t+kLeadK
+  // is requested right after the barrier ending tile t-1).  Grouped ring:
+  // tiles 0, 1 and 2 (tile 2 is read during tile 1, whose barrier publishes
+  // 3 .. g+2).
+  constexpr int kFirst = kGroup > 1 ? kGroup + 2 : kLeadK;
+  constexpr int kReady = kGroup > 1 ? 3 : 2;
 #pragma unroll
   for (int tl = 0; tl <= kFirst; ++tl)
     if (tl < n_tiles) dma_tile(tl, stage_ptr(tl));
