@@ -125,8 +125,9 @@ struct Unroll {
   }
 };
 
-// Host side: ATTN_OK when the current device is a gfx950 (cached per device).
-__attribute__((visibility("hidden"))) attn_status check_device();
+// Host side: ATTN_OK when the current device is a gfx950 (cached per device);
+// *cus (if given) receives its compute-unit count.
+__attribute__((visibility("hidden"))) attn_status check_device(int* cus = nullptr);
 
 inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 

@@ -61,7 +61,10 @@ constexpr int kBc = 64;                      // keys per K/V tile (two half tile
 // Waves per workgroup (each owns 32 query rows): 8 (256 rows, one workgroup
 // per CU) without a mask, 4 (128 rows, two workgroups per CU) when causal,
 // where shorter rows per workgroup balance the triangle better.
-constexpr int kWavesFull = 8;
+#ifndef ATTN_FULL_WAVES
+#define ATTN_FULL_WAVES 8
+#endif
+constexpr int kWavesFull = ATTN_FULL_WAVES;
 #ifndef ATTN_CAUSAL_WAVES
 #define ATTN_CAUSAL_WAVES 4
 #endif
@@ -914,8 +917,9 @@ namespace attn_detail {
 constexpr int kMaxDevices = 64;
 // 0 = not checked, 1 = gfx950, 2 = other architecture
 int g_arch_state[kMaxDevices];
+int g_cu_count[kMaxDevices];  // compute units of the device (of its partition)
 
-attn_status check_device() {
+attn_status check_device(int* cus) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -929,8 +933,11 @@ attn_status check_device() {
       return ATTN_E_DEVICE;
     }
     state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    __atomic_store_n(&g_cu_count[dev], prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                     __ATOMIC_RELAXED);
     __atomic_store_n(&g_arch_state[dev], state, __ATOMIC_RELEASE);
   }
+  if (cus) *cus = __atomic_load_n(&g_cu_count[dev], __ATOMIC_RELAXED);
   return state == 1 ? ATTN_OK : ATTN_E_DEVICE;
 }
 
@@ -991,7 +998,8 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
   st = check_layouts(layouts ? layouts : none, H, N, sb, sh, sn);
   if (st != ATTN_OK) return st;
   if (block_mask && (key_bits || N > kSparseBlockK * kMaxSparseTiles)) return ATTN_E_INVALID;
-  st = check_device();
+  int cus = 0;
+  st = check_device(&cus);
   if (st != ATTN_OK) return st;
 
   Bf16Args a;
@@ -1001,7 +1009,11 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   a.n = N;
-  const int waves = block_mask ? kSparseBlockQ / 32 : causal ? kWavesCausal : kWavesFull;
+  // Non-causal: 8-wave workgroups (256 rows, one per CU) when they give
+  // every CU at least one; otherwise 4-wave ones, twice as many (a short
+  // sequence over few heads would leave CUs idle).
+  const bool few = (long long)B * H * ((N + kWavesFull * 32 - 1) / (kWavesFull * 32)) < cus;
+  const int waves = block_mask ? kSparseBlockQ / 32 : causal ? kWavesCausal : few ? 4 : kWavesFull;
   const int rows = waves * 32;
   a.q_tiles = (N + rows - 1) / rows;
   a.block_mask = block_mask;
@@ -1028,9 +1040,11 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
                 : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, 4, false, true>);
   else if (key_bits)
     fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal, true, false>)
+         : few  ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, 4, true, false>)
                 : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, true, false>);
   else
     fn = causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<true, kWavesCausal, false, false>)
+         : few  ? reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, 4, false, false>)
                 : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, false, false>);
   const hipError_t e = hipLaunchKernel(fn, dim3(a.total_tiles), dim3(waves * 64), args, 0,
                                        static_cast<hipStream_t>(stream));

@@ -195,3 +195,15 @@ def test_key_mask_ring_lengths(n):
     o, lse = run(q, k, v, 0.125, False, key_valid=valid)
     check(q, k, v, o, lse, 0.125, False, valid, BF16, f"mask ring N={n}")
 
+
+@pytest.mark.parametrize("B, H", [(3, 21), (4, 16)])
+def test_key_mask_wave_count_threshold(B, H):
+    """The key-mask kernel on both sides of the 4-wave / 8-wave choice
+    (N = 1000: 63 heads below it, 64 at it), a random tenth of keys hidden."""
+    rng = np.random.default_rng(7300 + B)
+    valid = rng.random((B, 1000)) > 0.1
+    valid[:, 0] = True
+    q, k, v = inputs(B, H, 1000, "bf16", 7400 + B)
+    o, lse = run(q, k, v, 0.125, False, key_valid=valid)
+    check(q, k, v, o, lse, 0.125, False, valid, BF16, f"mask threshold {B}x{H}")
+

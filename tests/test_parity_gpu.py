@@ -87,6 +87,17 @@ def test_patch_3mp_causal_variant_sampled(causal):
     compare(w, q, k, v, o, lse, rows=sample_rows(w.N, 40))
 
 
+@pytest.mark.parametrize("B, H", [(3, 21), (4, 16)])
+def test_wave_count_threshold(B, H):
+    """Non-causal calls take 8-wave workgroups (256 rows) when those give
+    each of the 256 CUs one, else 4-wave ones: at N = 1000 (4 row blocks of
+    256), 63 heads take the 4-wave kernel and 64 heads the 8-wave one."""
+    w = Workload(f"threshold_{B}x{H}", B, H, 1000, 64, "bf16", 1.0, 0.125, False, 4000 + H, "")
+    q, k, v = make_inputs(w)
+    o, lse = gpu_run(q, k, v, w.scale, False)
+    compare(w, q, k, v, o, lse)
+
+
 # ------------------------------------------------------------ edge sizes
 
 EDGE_N = [1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 511, 513, 1000]
