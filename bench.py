@@ -54,6 +54,22 @@ def kernel_sha():
     return h.hexdigest()[:16]
 
 
+def kernel_name(w, B, H, N, sparse, bit_mask):
+    """The forward kernel instantiation a call runs (the library's choice:
+    block-sparse and causal calls 4 waves; non-causal 8 waves when
+    B*H*ceil(N/256) reaches the CU count, else 4)."""
+    import torch
+    causal = "true" if w.causal else "false"
+    if sparse:
+        return "attn_fwd_bf16_kernel<%s, 4, false, true>" % causal
+    if w.causal:
+        waves = 4
+    else:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        waves = 8 if B * H * ((N + 255) // 256) >= cus else 4
+    return "attn_fwd_bf16_kernel<%s, %d, %s, false>" % (causal, waves, "true" if bit_mask else "false")
+
+
 def traffic_for(workload_name):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs, or
     None when absent or taken on a different kernel source."""
@@ -318,6 +334,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     value = flops / wall / 1e12
     achieved = flops / kern / 1e12
     traffic = traffic_for(w.name)
+    alg_bytes = 4 * B * H * N * d * 2 + 4 * B * H * N
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -354,12 +371,13 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": ("attn_fwd_bf16_kernel<%s, 4, false, true>" % ("true" if w.causal else "false")
-                       if block_density is not None else
-                       "attn_fwd_bf16_kernel<%s, %s, false>" % ("true, 4" if w.causal else "false, 8",
-                                                                 "true" if mask == "bytes" else "false")),
+            "kernel": kernel_name(w, B, H, N, block_density is not None, mask == "bytes"),
             "kernel_ms": round(kern * 1e3, 4),
-            "algorithmic_bytes": 4 * B * H * N * d * 2 + 4 * B * H * N,
+            "algorithmic_bytes": alg_bytes,
+            # at the ridge (short sequences) the HBM view matters as well
+            "hbm_view": {"achieved": round(alg_bytes / kern / 1e9, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s (algorithmic bytes / kernel time)",
+                         "frac": round(alg_bytes / kern / 1e9 / PEAK_HBM_GBS, 4)},
         },
         "workspace": {"extra_bytes": int(extra), "mem_get_info_delta": int(free_delta),
                       "output_bytes": int(out_bytes)},
