@@ -22,7 +22,7 @@ Gradients (``oracle.backward``): central finite differences of the forward
 oracle and torch's float64 autograd.
 """
 
-from .backward import attention_backward  # noqa: F401
+from .backward import attention_backward, attention_backward_sampled  # noqa: F401
 from .fp64 import (  # noqa: F401
     attention,
     attention_fsum,

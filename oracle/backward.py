@@ -83,3 +83,48 @@ def attention_backward(q, k, v, do, scale, causal=False):
             dq[b, h] = _dq(ds, k[b, h], scale)
             dk[b, h] = _dk(ds, q[b, h], scale)
     return dq, dk, dv
+
+
+def _delta_from_output(do, o):
+    """D_i = sum_f dO_if O_if (equal to sum_j P_ij dP_ij since O = P V)."""
+    return (do * o).sum(axis=1)
+
+
+def _probability_columns(q, k_cols, lse, scale, causal, cols):
+    """P [N, C] at key columns `cols` of one head: exp(S_ij - LSE_i) over
+    every query i, with LSE_i the row's log-sum-exp of scaled, masked
+    scores (so the column needs no other key)."""
+    s = fp64._scores(q, k_cols, scale)
+    vis = np.ones(s.shape, dtype=bool)
+    if causal:
+        vis &= cols[None, :] <= np.arange(q.shape[0])[:, None]
+    return np.where(vis, np.exp(np.where(vis, s, 0.0) - lse[:, None]), 0.0)
+
+
+def attention_backward_sampled(q, k, v, do, scale, causal, rows, keys):
+    """dQ at query rows `rows` and dK, dV at key rows `keys` (float64,
+    [B, H, len(rows), d] and [B, H, len(keys), d]): the gradients of
+    ``attention_backward`` for a sample of their rows, at sizes where the
+    full N x N matrices per head are too large.  Row i of dQ needs row i of
+    P and dP (and D_i); row j of dK and dV needs column j of P and dP, and D
+    for every query.  O and LSE of every query come from the forward oracle,
+    so column j of P is exp(S_ij - LSE_i) and D_i = sum_f dO_if O_if."""
+    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    B, H, N, d = q.shape
+    dq = np.zeros((B, H, len(rows), d))
+    dk, dv = (np.zeros((B, H, len(keys), d)) for _ in range(2))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
+            o, lse = fp64.attention(qh[None, None], kh[None, None], vh[None, None], scale, causal=causal)
+            delta = _delta_from_output(doh, o[0, 0])
+            p_r = _probabilities(qh, kh, scale, causal, rows)
+            ds_r = _ds(p_r, _dp(doh[rows], vh), delta[rows])
+            dq[b, h] = _dq(ds_r, kh, scale)
+            p_c = _probability_columns(qh, kh[keys], lse[0, 0], scale, causal, keys)
+            ds_c = _ds(p_c, _dp(doh, vh[keys]), delta)
+            dv[b, h] = _dv(p_c, doh)
+            dk[b, h] = _dk(ds_c, qh, scale)
+    return dq, dk, dv

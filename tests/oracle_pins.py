@@ -325,6 +325,24 @@ def pin_row_sampling():
         _close(ls, lse[:, :, rows], 1e-14, "sampled rows LSE")
 
 
+def pin_backward_row_sampling():
+    """The sampled gradients (dQ at some query rows, dK and dV at some keys,
+    from the forward oracle's O and LSE) are those rows of the full backward
+    oracle, for ragged, causal and single-key shapes."""
+    from oracle.backward import attention_backward, attention_backward_sampled
+    rng = _rng(13)
+    for n, causal in ((70, False), (70, True), (37, True), (1, False)):
+        q, k, v, do = rng.standard_normal((4, 1, 2, n, 8))
+        rows = np.array(sorted({0, n // 3, n - 1}))
+        keys = np.array(sorted({0, n // 2, n - 1}))
+        dq, dk, dv = attention_backward(q, k, v, do, 0.4, causal=causal)
+        sq, sk, sv = attention_backward_sampled(q, k, v, do, 0.4, causal, rows, keys)
+        # absolute: with one key the gradients of Q and K cancel to zero
+        for got, ref, what in ((sq, dq[:, :, rows], "dQ"), (sk, dk[:, :, keys], "dK"),
+                               (sv, dv[:, :, keys], "dV")):
+            assert np.abs(got - ref).max() <= 1e-12, f"sampled {what} (n={n}, causal={causal})"
+
+
 def _merge(o1, l1, o2, l2):
     """Combine the results of two disjoint key sets (the blockwise rule of the
     FlashAttention reading notes, section "proposed method", written with
@@ -503,4 +521,5 @@ ALL_PINS = INDEPENDENT_PINS + [
     pin_materialised_brute_force,
     pin_fsum_variant,
     pin_row_sampling,
+    pin_backward_row_sampling,
 ]

@@ -79,3 +79,29 @@ def assert_grad_within(name, got, ref, mag):
     assert np.all(np.isfinite(got)), f"{name}: non-finite"
     assert fro <= GRAD["rel_fro"], f"{name}: relative Frobenius error {fro:.3e} > {GRAD['rel_fro']}"
     assert mx <= GRAD["rel_max"], f"{name}: max error {mx:.3e} of max|ref| > {GRAD['rel_max']}"
+
+
+def grad_magnitudes_sampled(q, k, v, do, scale, causal, rows, keys):
+    """grad_magnitudes at query rows `rows` (dQ) and keys `keys` (dK, dV),
+    from rows and columns of P as in the oracle's sampled backward."""
+    from oracle import attention
+    from oracle import backward as ob
+    from workloads import to_f64
+    q, k, v, do = (to_f64(t) for t in (q, k, v, do))
+    rows, keys = np.asarray(rows), np.asarray(keys)
+    B, H, N, d = q.shape
+    mq = np.zeros((B, H, len(rows), d))
+    mk, mv = (np.zeros((B, H, len(keys), d)) for _ in range(2))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
+            o, lse = attention(qh[None, None], kh[None, None], vh[None, None], scale, causal=causal)
+            delta = np.abs(ob._delta_from_output(doh, o[0, 0]))
+            p_r = ob._probabilities(qh, kh, scale, causal, rows)
+            mds_r = p_r * (np.abs(ob._dp(doh[rows], vh)) + delta[rows][:, None])
+            mq[b, h] = abs(scale) * (mds_r @ np.abs(kh))
+            p_c = ob._probability_columns(qh, kh[keys], lse[0, 0], scale, causal, keys)
+            mds_c = p_c * (np.abs(ob._dp(doh, vh[keys])) + delta[:, None])
+            mk[b, h] = abs(scale) * (mds_c.T @ np.abs(qh))
+            mv[b, h] = p_c.T @ np.abs(doh)
+    return mq, mk, mv

@@ -25,9 +25,9 @@ import pytest
 import torch
 
 import exact_attention_29_amd as ea
-from oracle import attention_backward
-from tests.parity import assert_grad_within, grad_magnitudes
-from workloads import WORKLOADS, Workload, make_inputs, to_f64
+from oracle import attention_backward, attention_backward_sampled
+from tests.parity import assert_grad_within, grad_magnitudes, grad_magnitudes_sampled
+from workloads import WORKLOADS, Workload, make_inputs, sample_rows, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -85,6 +85,24 @@ def test_backward_workload_shapes(name):
     mags = grad_magnitudes(q, k, v, do, w.scale, w.causal)
     for nm, g, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv), mags):
         assert_grad_within(f"{nm} {name}", g, r, m)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_patch_3mp_sampled(causal):
+    """The 3 MP patch shape (N = 11,616, a ragged last tile) in the
+    backward's own launch configuration, on two of the workload's heads:
+    dQ at 40 sampled query rows and dK, dV at 40 sampled keys (both ends,
+    the ragged tail, random rows) against the oracle's gradients there."""
+    w = WORKLOADS["patch_3mp"]
+    q, k, v = (t[:, :2].contiguous() for t in make_inputs(w))
+    do = make_inputs(Workload("do", 1, 2, w.N, 64, "bf16", 1.0, w.scale, causal, w.seed + 50, ""))[0]
+    dq, dk, dv = grads_gpu(q, k, v, do, w.scale, causal)
+    rows, keys = sample_rows(w.N, 40), sample_rows(w.N, 40, seed=777)
+    ref = attention_backward_sampled(to_f64(q), to_f64(k), to_f64(v), to_f64(do), w.scale, causal, rows, keys)
+    mags = grad_magnitudes_sampled(q, k, v, do, w.scale, causal, rows, keys)
+    got = (dq[:, :, rows], dk[:, :, keys], dv[:, :, keys])
+    for name, g, r, m in zip(("dQ", "dK", "dV"), got, ref, mags):
+        assert_grad_within(f"{name} 3 MP causal={causal}", g, r, m)
 
 
 def test_backward_deterministic():
