@@ -95,3 +95,29 @@ def test_independent_pins_catch_backward_mutant(name, monkeypatch):
         except (AssertionError, ValueError, FloatingPointError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every independent pin"
+
+
+# mistakes in the steps only the sampled gradients use, caught by comparing
+# them with the full backward oracle (itself pinned above)
+SAMPLED_MUTANTS = {
+    "delta_from_output_dropped": ("_delta_from_output", lambda do, o: np.zeros(do.shape[0])),
+    "delta_from_output_values": ("_delta_from_output", lambda do, o: do.sum(axis=1)),
+    "columns_without_lse": ("_probability_columns", lambda q, kc, lse, scale, causal, cols: (
+        np.exp(scale * (q @ kc.T)))),
+    "columns_causal_reversed": ("_probability_columns", lambda q, kc, lse, scale, causal, cols: np.where(
+        (cols[None, :] >= np.arange(q.shape[0])[:, None]) if causal else True,
+        np.exp(scale * (q @ kc.T) - lse[:, None]), 0.0)),
+    "columns_scale_dropped": ("_probability_columns", lambda q, kc, lse, scale, causal, cols: np.where(
+        (cols[None, :] <= np.arange(q.shape[0])[:, None]) if causal else True,
+        np.exp(q @ kc.T - lse[:, None]), 0.0)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLED_MUTANTS))
+def test_row_sampling_pin_catches_sampled_mutant(name, monkeypatch):
+    from oracle import backward as OB
+    from tests.oracle_pins import pin_backward_row_sampling
+    attr, fn = SAMPLED_MUTANTS[name]
+    monkeypatch.setattr(OB, attr, fn)
+    with pytest.raises((AssertionError, ValueError, FloatingPointError, IndexError)):
+        pin_backward_row_sampling()
