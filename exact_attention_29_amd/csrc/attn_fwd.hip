@@ -12,11 +12,13 @@
 // GPU's shared memory; the tiles below are sized for gfx950 instead.
 //
 // bf16 kernel.  One workgroup = 8 waves = 256 query rows of one head, one
-// workgroup per CU, two waves per SIMD (causal: 4 waves = 128 rows, two
-// workgroups per CU, for a better balanced triangle):
+// workgroup per CU, two waves per SIMD (causal, and non-causal calls too
+// small to give every CU a 256-row tile: 4 waves = 128 rows, two workgroups
+// per CU):
 //   * each wave owns 32 query rows; their Q^T operands stay in VGPRs;
-//   * K and V tiles of 64 keys go through a 5-stage LDS ring, filled by
-//     global_load_lds_dwordx4 DMA three tiles ahead (no staging registers);
+//   * K and V tiles of 64 keys go through an LDS ring filled by buffer-load
+//     DMA (no staging registers): 6 stages with a barrier every second tile
+//     for 8 waves, 5 stages filled three tiles ahead for 4 waves;
 //     16-byte chunks are XOR-swizzled per row so both read patterns below
 //     are bank-conflict free, and every LDS address is a per-lane constant
 //     plus an immediate (the steady state is unrolled over the stages);
@@ -387,7 +389,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   const f32x16 zero16 = {};
 
   // ---- the three pieces of work on one half tile (32 keys).  Half tile j
-  // covers keys 32*j .. 32*j+31: tile j/2 (LDS stage (j/2) % 4), rows 32*(j%2)..
+  // covers keys 32*j .. 32*j+31: tile j/2 (LDS stage (j/2) % kStagesK), rows 32*(j%2)..
   //
   // S^T = K Q^T: s holds keys 32*j + 8*(r/4) + 4*hi + r%4 of query qi.
   auto compute_s = [&](const char* stage_base, int h, f32x16& s) __attribute__((always_inline)) {
