@@ -819,7 +819,7 @@ struct F32Args {
   const uint32_t* key_bits;   // [B][ceil(N/32)] or null
 };
 
-constexpr int kF32Keys = 32;  // keys per LDS tile in the fp32 kernel
+constexpr int kF32Keys = 16;  // keys per LDS tile in the fp32 kernel
 
 __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
   __shared__ float ks[kF32Keys][kD];
@@ -837,8 +837,14 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     qv[f] = live ? a.q[head + (size_t)qi * kD + f] : 0.f;
     acc[f] = 0.f;
   }
-  const float c = a.scale * kLog2e;
-  float m_run = -INFINITY, l_run = 0.f;
+  // Scores, the running max and t - m are kept in fp64: a 64-term fp32 dot
+  // product and the rounding of s * c would each cost about 2^-24 * |s| in
+  // the exponent, i.e. ~1e-5 in O and LSE once |s| reaches ~30 (a large
+  // scale); in fp64 the products of fp32 values are exact and only the
+  // small difference t - m is rounded to fp32 for exp2.
+  const double c = (double)a.scale * 1.4426950408889634;  // log2(e)
+  double m_run = -INFINITY;
+  float l_run = 0.f;
   const int b_entry = bh / a.heads;
   const int n_k = a.key_len ? min(max(a.key_len[b_entry], 0), n) : n;
   const uint32_t* const mask_row = a.key_bits ? a.key_bits + (size_t)b_entry * ((n + 31) / 32) : nullptr;
@@ -854,30 +860,30 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
       vs[r][f] = key < n ? a.v[head + (size_t)key * kD + f] : 0.f;
     }
     __syncthreads();
-    float t[kF32Keys];
-    float mx = -INFINITY;
-    // the tile's 32 keys are one mask word (k0 is a multiple of 32, k0 < N)
-    static_assert(kF32Keys == 32, "one mask word per key tile");
-    const uint32_t word = mask_row ? mask_row[k0 >> 5] : 0xffffffffu;
+    double t[kF32Keys];
+    double mx = -INFINITY;
+    // the tile's 16 keys are half of one mask word (k0 is a multiple of 16, k0 < N)
+    static_assert(kF32Keys == 16, "half a mask word per key tile");
+    const uint32_t word = mask_row ? mask_row[k0 >> 5] >> (k0 & 31) : 0xffffffffu;
 #pragma unroll
     for (int r = 0; r < kF32Keys; ++r) {
-      float s = 0.f;
+      double s = 0.0;
 #pragma unroll
-      for (int f = 0; f < kD; ++f) s = __builtin_fmaf(qv[f], ks[r][f], s);
+      for (int f = 0; f < kD; ++f) s = __builtin_fma((double)qv[f], (double)ks[r][f], s);
       const bool vis = k0 + r <= row_last && ((word >> r) & 1u);
       t[r] = vis ? s * c : -INFINITY;
-      mx = fmaxf(mx, t[r]);
+      mx = fmax(mx, t[r]);
     }
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+    const double m_new = fmax(m_run, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((float)(m_run - m_new));
+    const double msub = (m_new == -INFINITY) ? 0.0 : m_new;
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
     for (int f = 0; f < kD; ++f) acc[f] *= alpha;
 #pragma unroll
     for (int r = 0; r < kF32Keys; ++r) {
-      const float p = __builtin_amdgcn_exp2f(t[r] - msub);
+      const float p = __builtin_amdgcn_exp2f((float)(t[r] - msub));
       l_run += p;
 #pragma unroll
       for (int f = 0; f < kD; ++f) acc[f] = __builtin_fmaf(p, vs[r][f], acc[f]);
@@ -888,7 +894,8 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
     for (int f = 0; f < kD; ++f) a.o[head + (size_t)qi * kD + f] = acc[f] * inv;
-    a.lse[(size_t)bh * n + qi] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    a.lse[(size_t)bh * n + qi] = l_run > 0.f ? (float)((m_run + (double)__log2f(l_run)) * 0.6931471805599453)
+                                             : -INFINITY;
   }
 }
 
