@@ -1,7 +1,8 @@
 """Seeded random combinations of the forward's and backward's features on the
 GPU against the fp64 oracle: shapes (lengths near and between tile
 boundaries), causal or not, both key-mask forms (with entries that hide every
-key), packed strided views, fp32 I/O, negative and unusual scales.  Each
+key), packed strided views, fp32 I/O, negative and unusual scales, random
+block-sparse masks, and the backward.  Each
 feature has its own tests; these check that they combine.  The cases are
 drawn once from a fixed seed, so every run sees the same list.
 """
@@ -116,3 +117,37 @@ def test_random_backward(case):
     mags = grad_magnitudes(q, k, v, do, case["scale"], case["causal"])
     for name, g, r, m in zip(("dQ", "dK", "dV"), grads, ref, mags):
         assert_grad_within(f"{name} case {case['i']}", g, r, m)
+
+
+def _sparse_cases(count=12, seed=6072):
+    rng = np.random.default_rng(seed)
+    return [dict(i=i, B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), N=_length(rng),
+                 causal=bool(rng.random() < 0.5), density=float(rng.uniform(0.05, 1.0)),
+                 scale=float(0.125 if rng.random() < 0.7 else rng.uniform(-0.5, 1.0)),
+                 seed=int(rng.integers(0, 2**31))) for i in range(count)]
+
+
+@pytest.mark.parametrize("case", _sparse_cases(), ids=lambda c: "s%02d_N%d%s_d%.2f" % (
+    c["i"], c["N"], "_causal" if c["causal"] else "", c["density"]))
+def test_random_block_sparse(case):
+    """Random block masks (128-query by 64-key blocks) at random density,
+    rows whose blocks are all unset included."""
+    B, H, N = case["B"], case["H"], case["N"]
+    print(f"[fuzz] {case}", flush=True)
+    w = Workload("fuzz_sparse", B, H, N, 64, "bf16", 1.0, case["scale"], case["causal"], case["seed"], "")
+    q, k, v = make_inputs(w)
+    rng = np.random.default_rng(case["seed"])
+    nbq, nbk = -(-N // ea.SPARSE_BLOCK_Q), -(-N // ea.SPARSE_BLOCK_K)
+    m = rng.random((nbq, nbk)) < case["density"]
+    o, lse = ea.forward(q.to(DEV), k.to(DEV), v.to(DEV), scale=case["scale"], causal=case["causal"],
+                        block_mask=torch.from_numpy(m).to(DEV))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention(to_f64(q), to_f64(k), to_f64(v), case["scale"], causal=case["causal"],
+                               block_mask=(m, ea.SPARSE_BLOCK_Q, ea.SPARSE_BLOCK_K))
+    o_h, lse_h = to_f64(o), to_f64(lse)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_h), empty), "rows that see no key differ"
+    assert np.all(o_h[empty] == 0.0), "a row that sees no key has O != 0"
+    keep = ~empty
+    if keep.any():
+        assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), BF16, f"case {case['i']}")
