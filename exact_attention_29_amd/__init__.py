@@ -56,7 +56,7 @@ def load_library():
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(
             f"HIP library not built: {_LIB_PATH} is missing "
-            "(run `python -c 'import __graft_entry__ as g; g.build()'` first)")
+            "(run `python exact_attention_29_amd/build.py` first)")
     lib = ctypes.CDLL(_LIB_PATH)
     ptr, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     sig = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32, ptr]
