@@ -28,7 +28,8 @@
 // issues the MFMAs of S and dP for step j+1 and of the accumulating products
 // of step j-1, one by one, each beside a slice of the vector work of step j
 // (exp2, dS, bf16 packing), and reads its MFMA operands from LDS four MFMAs
-// ahead.  -D enters dP as the initial value of its accumulator.
+// ahead.  -D enters dP as the initial value of its accumulator.  Causal
+// calls run each XCD's block of heads longest row block first (causal_order).
 // No atomics: every output element is written by exactly one lane, so the
 // result is deterministic.  All products on v_mfma_f32_32x32x16_bf16 with
 // fp32 accumulation; P and dS are rounded to bf16 for the products, as in
