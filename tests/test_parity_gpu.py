@@ -388,3 +388,17 @@ def test_errors_leave_outputs_untouched():
                     1, 2, 64, 64, float("nan"), 0, None)
     torch.cuda.synchronize()
     assert bool((o == 3.0).all()) and bool((lse == 3.0).all())
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 0, 64), (0, 2, 5, 64), (2, 0, 5, 64)])
+def test_empty_inputs_give_empty_outputs(shape):
+    """Shapes with nothing to compute return empty outputs of the right shape
+    (the C entry points take B, H, N >= 1; the binding answers these itself)."""
+    q = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    o, lse = ea.forward(q, q, q)
+    assert o.shape == shape and lse.shape == shape[:3]
+    dq, dk, dv = ea.backward(q, q, q, o, lse, q)
+    assert dq.shape == dk.shape == dv.shape == shape
+    with pytest.raises(ea.AttnError):
+        bad = torch.empty(shape[:3] + (32,), dtype=torch.bfloat16, device=DEV)
+        ea.forward(bad, bad, bad)
