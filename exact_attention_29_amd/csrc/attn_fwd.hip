@@ -655,11 +655,11 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   vm_wait_barrier_tiles<kDmaPerTile, kFirst + 1 - kReady>(max(0, min(n_tiles, kFirst + 1) - kReady));
   if (last_h >= 0) compute_s(lds0, 0, sA);
 
-  // ---- tiles: 0 on the general path, then the steady state (both half
-  // steps fast) unrolled over the ring's stages, then the rest on the general
-  // path
-  tile_general(0);
-  // tile t is steady when 2t+2 < n_half, 2t+2 <= last_h and neither 2t nor
+  // ---- tiles: 0 (its first half on the exact path, which sets the
+  // reference; its second half pipelined when tile 1 is), then the steady
+  // state (both half steps fast) unrolled over the ring's stages, then the
+  // rest on the general path.
+  // Tile t is steady when 2t+2 < n_half, 2t+2 <= last_h and neither 2t nor
   // 2t+1 needs a mask; all three conditions only get stricter with t
   int t_fast_end = 1;
   {
@@ -683,19 +683,35 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     }
     if (full < 2) lim = 0;
     t_fast_end = max(1, lim + 1);
-    // The steady state needs a finite reference in every row: with a key
-    // mask, a row whose first tile was all hidden has none yet, so such a
-    // wave stays on the exact-max path (no -inf - -inf, no NaN).  Without a
-    // key mask, key 0 is visible to every row.
-    if ((kKeyMask || kSparse) && __any(m_run == -INFINITY)) t_fast_end = 1;
   }
+  const int t_fast_steady = t_fast_end;
+  // The steady state needs a finite reference in every row: with a key mask
+  // or a block list, a row whose first half was all hidden has none yet, so
+  // such a wave stays on the exact-max path (no -inf - -inf, no NaN) until
+  // it has one.  Without them, key 0 is visible to every row.
+  auto no_reference = [&]() { return (kKeyMask || kSparse) && __any(m_run == -INFINITY); };
+  step_general(0, sA, pA, sB, pB);  // S(1) -> sB, P(0) -> pA
+  if (no_reference()) t_fast_end = 1;
+  if (t_fast_end > 1) {
+    // half 1 on the pipelined path: its operands (PV(0) from tile 0's first
+    // half, S(2) from tile 1's) are read here; it reads those of step 2
+    // (PV(1), S(3)) and, with a key mask, tile 1's words
+    load_ops(lds0, 0, lds1, 0, opB);
+    step_fast(opB, opA, lds0, 1, lds1, 1, sB, pB, sA, pA, kKeyMask ? mask_word(1) : 0xffffffffu, true, 2);
+  } else if (1 < n_half) {
+    step_general(1, sB, pB, sA, pA);
+    if (!no_reference()) t_fast_end = t_fast_steady;
+    if (t_fast_end > 1) {
+      // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
+      load_ops(lds0, 1, lds1, 1, opA);
+      if constexpr (kKeyMask) {
+        vis_next0 = mask_word(2);
+        vis_next1 = mask_word(3);
+      }
+    }
+  }
+  end_tile(0, 0);
   int t = 1;
-  // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
-  if (t < t_fast_end) load_ops(lds0, 1, lds1, 1, opA);
-  if constexpr (kKeyMask) {
-    vis_next0 = mask_word(2);
-    vis_next1 = mask_word(3);
-  }
   for (; t + kStagesK - 1 < t_fast_end; t += kStagesK) {
     // tiles t .. t+kStagesK-1 sit in stages 1, 2, .., kStagesK-1, 0
     Unroll<0, kStagesK>::run([&](auto i) {
