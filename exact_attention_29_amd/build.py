@@ -25,7 +25,7 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Xarch_device", "-fno-honor-nans",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wextra",
     "-Rpass-analysis=kernel-resource-usage",
 ]
 
