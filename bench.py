@@ -25,7 +25,6 @@ published dense bf16 MFMA rate (256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz).
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
