@@ -105,6 +105,43 @@ def time_gpu(fn, steps, warmup, stream):
     return wall / steps, ev[0].elapsed_time(ev[steps]) * 1e-3 / steps, per
 
 
+def time_gpu_graph(fn, steps, warmup, stream):
+    """As time_gpu, with the timed steps replayed from a HIP graph: a batch
+    of G calls (the largest G <= 25 dividing steps) is captured once and
+    replayed steps/G times, so the host never paces short kernels.  Events
+    bracket every replay; per-launch durations are a replay's time / G."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    per_graph = next(g for g in range(min(25, steps), 0, -1) if steps % g == 0)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()  # once untimed: the graph's first launch uploads it
+    torch.cuda.synchronize()
+    reps = steps // per_graph
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(reps):
+        graph.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 / per_graph for i in range(reps)]
+    return wall / steps, ev[0].elapsed_time(ev[reps]) * 1e-3 / steps, per
+
+
+# the timer of the warm steps: graph replay (default) or eager launches
+TIMER = {"fn": time_gpu_graph, "method": "HIP graph replays of a captured batch of calls"}
+
+
 def time_cold(fn, launches, stream, scratch_mib=512):
     """Per-launch kernel durations with the caches flushed before each launch:
     a 512 MiB scratch buffer (twice the 256 MB MALL) is rewritten between
@@ -315,11 +352,11 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     def step():
         ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, **masks)
 
-    wall, kern, per = time_gpu(step, steps, warmup, stream)
+    wall, kern, per = TIMER["fn"](step, steps, warmup, stream)
     if block_density is not None:
         # the same call without the block mask, for the time ratio
         dense_masks = {kk: vv for kk, vv in masks.items() if kk != "block_mask"}
-        _, dense_kern, _ = time_gpu(lambda: ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o,
+        _, dense_kern, _ = TIMER["fn"](lambda: ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o,
                                                        lse=lse, **dense_masks), steps, warmup, stream)
     clock_info = None
     if clock:
@@ -383,6 +420,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
         "timing": {"kernel_ms_mean": round(kern * 1e3, 4), "kernel_ms_median": round(median(per) * 1e3, 4),
                    "kernel_ms_min": round(min(per) * 1e3, 4), "launches": steps,
                    "tflops_at_median": round(flops / median(per) / 1e12, 2),
+                   "method": TIMER["method"],
                    "cache": "warm: inputs stay resident in L2/MALL between launches"},
     }
     if clock_info is not None:
@@ -423,14 +461,14 @@ def bench_backward(w, steps, warmup):
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = torch.empty(ea.attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
 
     def step():
+        # the current stream at call time (a capture stream while recording a graph)
         ea.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, N, d, w.scale,
-                    w.causal, sh)
+                    w.causal, torch.cuda.current_stream(dev).cuda_stream)
 
-    wall, kern, per = time_gpu(step, steps, warmup, stream)
+    wall, kern, per = TIMER["fn"](step, steps, warmup, stream)
     flops = 10.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
     return {
         "metric": "attention backward (dQ, dK, dV) TFLOP/s",
@@ -442,6 +480,7 @@ def bench_backward(w, steps, warmup):
         "pct_of_bf16_peak": round(100.0 * flops / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
         "timing": {"ms_mean": round(kern * 1e3, 4), "ms_median": round(median(per) * 1e3, 4),
                    "ms_min": round(min(per) * 1e3, 4),
+                   "method": TIMER["method"],
                    "note": "the three kernels of one call, between events on the launch stream"},
         "workspace": {"bytes": int(ws.numel()),
                       "note": "caller-owned attn_bwd_workspace_size(B, H, N): LSE*log2(e) and -D per padded row"},
@@ -508,6 +547,8 @@ def main():
     ap.add_argument("--cold", type=int, default=30,
                     help="launches timed with flushed caches after the warm steps (0: skip)")
     ap.add_argument("--no-clock", action="store_true", help="do not sample the clock with amd-smi")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the warm steps as eager launches from Python instead of HIP graph replays")
     ap.add_argument("--backward", action="store_true",
                     help="time attn_bwd (dQ, dK, dV) instead of the forward pass")
     ap.add_argument("--block-density", type=float, default=None,
@@ -531,6 +572,9 @@ def main():
 
     import torch
     from workloads import PATCH_SWEEP, WORKLOADS
+
+    if args.eager:
+        TIMER.update(fn=time_gpu, method="eager launches from Python, events between launches")
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
