@@ -337,7 +337,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   };
   // End of tile t (in stage st).  Per-tile ring: the barrier above, then
   // tile t+1+kLeadK is requested into the stage of tile t-1.  Grouped ring
-  // (g = kGroup): only tiles with t % g == 1 end in a barrier.  There every
+  // (g = kGroup): only tiles with t % g == 0 end in a barrier.  There every
   // request is waited for (tiles t+2 .. t+g+1, requested one group ago), the
   // barrier publishes them (they are read up to the next barrier, t+g), and
   // tiles t+g+2 .. t+2g+1 are requested into the stages of tiles
@@ -345,7 +345,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // ring's stage count is a multiple of g, so t % g == st % g.
   auto end_tile = [&](int t, int st) __attribute__((always_inline)) {
     if constexpr (kGroup > 1) {
-      if ((unsigned)st % kGroup == 1u) {  // st >= 0
+      if ((unsigned)st % kGroup == 0u) {  // st >= 0
         vm_wait_barrier<0>();
 #pragma unroll
         for (int i = kGroup + 2; i <= 2 * kGroup + 1; ++i)
@@ -641,13 +641,12 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     end_tile(t, st);
   };
 
-  // ---- prologue: tiles 0 .. kFirst requested; the first kReady must land
-  // before the first barrier.  Per-tile ring: tiles 0 and 1 (tile t+kLeadK
-  // is requested right after the barrier ending tile t-1).  Grouped ring:
-  // tiles 0, 1 and 2 (tile 2 is read during tile 1, whose barrier publishes
-  // 3 .. g+2).
-  constexpr int kFirst = kGroup > 1 ? kGroup + 2 : kLeadK;
-  constexpr int kReady = kGroup > 1 ? 3 : 2;
+  // ---- prologue: tiles 0 .. kFirst requested; tiles 0 and 1 (read during
+  // tile 0) must land before the first barrier.  Per-tile ring: tile
+  // t+kLeadK is requested right after the barrier ending tile t-1.  Grouped
+  // ring: the barrier ending tile 0 publishes tiles 2 .. g+1.
+  constexpr int kFirst = kGroup > 1 ? kGroup + 1 : kLeadK;
+  constexpr int kReady = 2;
 #pragma unroll
   for (int tl = 0; tl <= kFirst; ++tl)
     if (tl < n_tiles) dma_tile(tl, stage_ptr(tl));
