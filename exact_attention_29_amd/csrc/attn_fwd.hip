@@ -547,7 +547,10 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   auto step_fast = [&](const Ops& cur, Ops& nxt, const char* npv_base, int npv_h,
                        const char* ns_base, int ns_h, f32x16& s_cur, bf16x8 (&p_cur)[2],
                        f32x16& s_nxt, const bf16x8 (&p_prv)[2], uint32_t vis, bool fetch_words,
-                       int word_j) __attribute__((always_inline)) {
+                       int word_j, auto drain_tag) __attribute__((always_inline)) {
+    // a drain step (the sequence's last half tiles): no S of a next half, no
+    // operands to read ahead
+    constexpr bool kDrain = decltype(drain_tag)::value;
     // with a key mask, hide the masked keys of this half tile first (nothing
     // to do, and no instruction spent, when all 32 keys take part)
     if (kKeyMask && vis != 0xffffffffu) apply_bits(vis, s_cur);
@@ -568,11 +571,11 @@ attn_fwd_bf16_kernel(Bf16Args a) {
         if ((slot & 1) == 1) {
           const int i = slot >> 1, tt = i >> 1, db = i & 1;
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[tt][db], p_prv[tt], acc[db], 0, 0, 0);
-        } else {
+        } else if constexpr (!kDrain) {
           const int ks = slot >> 1;
           s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.k[ks], qop[ks], ks == 0 ? zero16 : s_nxt, 0, 0, 0);
         }
-        if (slot == 0) {
+        if (slot == 0 && !kDrain) {
           __builtin_amdgcn_sched_barrier(0);
           load_ops(npv_base, npv_h, ns_base, ns_h, nxt);
           // the next tile's mask words: issued here, a whole step before the
@@ -636,8 +639,25 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     char* const b_cur = stage_ptr(st);
     char* const b_next = stage_ptr((st + 1) % kStagesK);
     const uint32_t vis0 = vis_next0, vis1 = vis_next1;
-    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0, true, 2 * t + 2);  // j = 2t
-    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1, false, 0);        // j = 2t + 1
+    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0, true, 2 * t + 2, std::false_type());  // j = 2t
+    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1, false, 0, std::false_type());  // j = 2t + 1
+    end_tile(t, st);
+  };
+  // The last tile, when its keys need no mask, after a pipelined tile (so
+  // opA holds its operands and, with a key mask, vis_next its words): its
+  // last step is a drain step; the last PV follows the loop as usual.  The
+  // K operands its first step reads for the non-existent next tile are never
+  // used (any stage is safe to read: every request has landed by now).
+  auto tile_drain = [&](int t) __attribute__((always_inline)) {
+    const int st = t % kStagesK;
+    char* const b_cur = stage_ptr(st);
+    char* const b_next = stage_ptr((st + 1) % kStagesK);
+    if (2 * t + 1 < n_half) {
+      step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis_next0, false, 0, std::false_type());
+      step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis_next1, false, 0, std::true_type());
+    } else {
+      step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis_next0, false, 0, std::true_type());
+    }
     end_tile(t, st);
   };
 
@@ -696,7 +716,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     // half, S(2) from tile 1's) are read here; it reads those of step 2
     // (PV(1), S(3)) and, with a key mask, tile 1's words
     load_ops(lds0, 0, lds1, 0, opB);
-    step_fast(opB, opA, lds0, 1, lds1, 1, sB, pB, sA, pA, kKeyMask ? mask_word(1) : 0xffffffffu, true, 2);
+    step_fast(opB, opA, lds0, 1, lds1, 1, sB, pB, sA, pA, kKeyMask ? mask_word(1) : 0xffffffffu, true, 2,
+              std::false_type());
   } else if (1 < n_half) {
     step_general(1, sB, pB, sA, pA);
     if (!no_reference()) t_fast_end = t_fast_steady;
@@ -729,7 +750,12 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       if (t + I < t_fast_end) tile_fast(t + I, std::integral_constant<int, (I + 1) % kStagesK>());
     });
   }
-  for (t = t_fast_end; t < n_tiles; ++t) tile_general(t);
+  t = t_fast_end;
+  if (!kSparse && t >= 2 && t == n_tiles - 1 && n_half - 1 <= last_h && !needs_lim(n_half - 1)) {
+    tile_drain(t);
+    ++t;
+  }
+  for (; t < n_tiles; ++t) tile_general(t);
   // the last half tile's PV
   if (n_half >= 1 && n_half - 1 <= last_h) {
     if ((n_half - 1) & 1) compute_pv(stage_base(n_half - 1), 1, pB);

@@ -57,13 +57,14 @@ def inputs(B, H, N, dtype, seed, sigma=1.0):
     return make_inputs(w)
 
 
-LENGTHS = [512, 300, 1, 0, 257, 64, 33, 511]
+LENGTHS = [512, 300, 1, 0, 257, 64, 33, 511, 480, 448]
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_valid_length_bf16(causal):
     """Right padding by length on a BERT-sized batch: full, ragged, one key,
-    none (every row empty), one tile, one key past a tile, all but one."""
+    none (every row empty), one tile, one key past a tile, all but one, and
+    lengths ending on a half tile and on a whole tile."""
     B, H, N = len(LENGTHS), 4, 512
     q, k, v = inputs(B, H, N, "bf16", seed=700 + causal)
     o, lse = run(q, k, v, 0.125, causal, key_len=LENGTHS)
@@ -183,11 +184,13 @@ def test_page_mask_polarity_example_on_the_gpu():
     assert got == g["cases"]["boolean_mask_as_is_attends_only_key_3"], got
 
 
-@pytest.mark.parametrize("n", [64 * t + r for t in range(1, 21, 3) for r in (0, 37)] + [64 * 13, 64 * 19 + 5])
+@pytest.mark.parametrize("n", [64 * t + r for t in range(1, 21, 3) for r in (0, 37)] +
+                         [64 * 13, 64 * 19 + 5, 64 * 5 + 32, 64 * 12 + 32])
 def test_key_mask_ring_lengths(n):
     """The key-mask kernel over key-tile counts 1 .. 19 (the 8-wave kernel's
-    paired ring: partial turns and general tails of every parity), with a
-    random tenth of the keys hidden and key 0 kept."""
+    paired ring: partial turns and general tails of every parity, last tiles
+    of one and two whole half tiles, which drain with the mask words read
+    ahead), with a random tenth of the keys hidden and key 0 kept."""
     rng = np.random.default_rng(7000 + n)
     valid = rng.random((2, n)) > 0.1
     valid[:, 0] = True

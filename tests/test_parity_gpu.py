@@ -113,10 +113,12 @@ def test_edge_sizes_bf16(n, causal):
     compare(w, q, k, v, o, lse)
 
 
-# Key-tile counts 1 .. 20 with whole and ragged last tiles: every length of
-# the last, partial turn of the LDS ring (6 stages without a mask, 5 causal),
-# barriers after tiles of either parity, and the general tail after each.
-RING_N = [64 * t + r for t in range(1, 21) for r in (0, 37)]
+# Key-tile counts 1 .. 21 with whole, one-half (32 keys) and ragged last
+# tiles: every length of the last, partial turn of the LDS ring (6 stages
+# without a mask, 5 causal), barriers after tiles of either parity, and the
+# tail after each (a drain of one or two half tiles when the last tile needs
+# no mask, the general path otherwise).
+RING_N = [64 * t + r for t in range(1, 21) for r in (0, 37)] + [64 * t + 32 for t in range(1, 21, 2)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
