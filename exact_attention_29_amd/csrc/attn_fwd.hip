@@ -114,6 +114,13 @@ constexpr unsigned kRedoBits = 0x4f800000u;  // bit pattern of 2^32: a partial
                                              // reference max is stale
 constexpr unsigned kInfBits = 0x7f800000u;   // bit pattern of +inf
 
+// kinds of pipelined step: steady state; drain (no next S, no read-ahead);
+// drain with a per-row last visible key (a causal diagonal or ragged half)
+constexpr int kStepNormal = 0, kStepDrain = 1, kStepLimit = 2;
+using StepNormal = std::integral_constant<int, kStepNormal>;
+using StepDrain = std::integral_constant<int, kStepDrain>;
+using StepLimit = std::integral_constant<int, kStepLimit>;
+
 struct Bf16Args {
   const uint16_t* q;
   const uint16_t* k;
@@ -544,13 +551,21 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // basic block: 8 slots of one MFMA (PV and S alternating, so dependent
   // MFMAs are two slots apart) and one vector-ALU chunk (two exponentials
   // with their FMA, sum and bf16 packing).
+  int drain_lim = 31;  // a limited drain step's last visible key offset in its half, per row
   auto step_fast = [&](const Ops& cur, Ops& nxt, const char* npv_base, int npv_h,
                        const char* ns_base, int ns_h, f32x16& s_cur, bf16x8 (&p_cur)[2],
                        f32x16& s_nxt, const bf16x8 (&p_prv)[2], uint32_t vis, bool fetch_words,
-                       int word_j, auto drain_tag) __attribute__((always_inline)) {
-    // a drain step (the sequence's last half tiles): no S of a next half, no
-    // operands to read ahead
-    constexpr bool kDrain = decltype(drain_tag)::value;
+                       int word_j, auto mode_tag) __attribute__((always_inline)) {
+    // a drain step (the wave's last visible half tile): no S of a next half,
+    // no operands to read ahead; kStepLimit also hides the keys of the half
+    // past offset drain_lim of this lane's row (causal diagonal, sequence end)
+    constexpr int kMode = decltype(mode_tag)::value;
+    constexpr bool kDrain = kMode != kStepNormal;
+    if constexpr (kMode == kStepLimit) {
+      const int lim = drain_lim - 4 * hi;  // register r holds key offset 8*(r/4) + 4*hi + r%4
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_cur[r] = 8 * (r >> 2) + (r & 3) <= lim ? s_cur[r] : -INFINITY;
+    }
     // with a key mask, hide the masked keys of this half tile first (nothing
     // to do, and no instruction spent, when all 32 keys take part)
     if (kKeyMask && vis != 0xffffffffu) apply_bits(vis, s_cur);
@@ -639,24 +654,30 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     char* const b_cur = stage_ptr(st);
     char* const b_next = stage_ptr((st + 1) % kStagesK);
     const uint32_t vis0 = vis_next0, vis1 = vis_next1;
-    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0, true, 2 * t + 2, std::false_type());  // j = 2t
-    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1, false, 0, std::false_type());  // j = 2t + 1
+    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0, true, 2 * t + 2, StepNormal());  // j = 2t
+    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1, false, 0, StepNormal());  // j = 2t + 1
     end_tile(t, st);
   };
-  // The last tile, when its keys need no mask, after a pipelined tile (so
-  // opA holds its operands and, with a key mask, vis_next its words): its
-  // last step is a drain step; the last PV follows the loop as usual.  The
-  // K operands its first step reads for the non-existent next tile are never
-  // used (any stage is safe to read: every request has landed by now).
-  auto tile_drain = [&](int t) __attribute__((always_inline)) {
+  // Tile t holding this wave's last visible half tile last_h (2t or 2t+1),
+  // after a pipelined tile (so opA holds its operands and, with a key mask,
+  // vis_next its words), when the halves before last_h need no mask: last_h
+  // is a drain step, limited (per row, drain_lim) when it needs a mask.  Its
+  // PV follows in the next step of the general path, or after the loop when
+  // last_h is the sequence's last half.  K operands read ahead for a half
+  // with no S are never used (stage memory, in bounds, whatever it holds).
+  auto tile_drain = [&](int t, bool limited) __attribute__((always_inline)) {
     const int st = t % kStagesK;
     char* const b_cur = stage_ptr(st);
     char* const b_next = stage_ptr((st + 1) % kStagesK);
-    if (2 * t + 1 < n_half) {
-      step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis_next0, false, 0, std::false_type());
-      step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis_next1, false, 0, std::true_type());
+    if (last_h == 2 * t + 1) {
+      step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis_next0, false, 0, StepNormal());
+      if (limited) step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis_next1, false, 0, StepLimit());
+      else step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis_next1, false, 0, StepDrain());
     } else {
-      step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis_next0, false, 0, std::true_type());
+      if (limited) step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis_next0, false, 0, StepLimit());
+      else step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis_next0, false, 0, StepDrain());
+      // half 2t+1 exists but is hidden from this wave: PV(2t) now
+      if (2 * t + 1 < n_half) compute_pv(b_cur, 0, pA);
     }
     end_tile(t, st);
   };
@@ -717,7 +738,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     // (PV(1), S(3)) and, with a key mask, tile 1's words
     load_ops(lds0, 0, lds1, 0, opB);
     step_fast(opB, opA, lds0, 1, lds1, 1, sB, pB, sA, pA, kKeyMask ? mask_word(1) : 0xffffffffu, true, 2,
-              std::false_type());
+              StepNormal());
   } else if (1 < n_half) {
     step_general(1, sB, pB, sA, pA);
     if (!no_reference()) t_fast_end = t_fast_steady;
@@ -751,8 +772,12 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     });
   }
   t = t_fast_end;
-  if (!kSparse && t >= 2 && t == n_tiles - 1 && n_half - 1 <= last_h && !needs_lim(n_half - 1)) {
-    tile_drain(t);
+  if (!kSparse && t >= 2 && (last_h >> 1) == t && (last_h == 2 * t || !needs_lim(2 * t))) {
+    // the last visible key of this lane's row, as an offset in half last_h
+    // (the general path's limit; only keys below n_k, whose LDS rows hold
+    // loaded data, stay visible)
+    drain_lim = (kCausal ? min(qi, n_k - 1) : n_k - 1) - 32 * last_h;
+    tile_drain(t, needs_lim(last_h));
     ++t;
   }
   for (; t < n_tiles; ++t) tile_general(t);
