@@ -199,6 +199,25 @@ def test_key_mask_ring_lengths(n):
     check(q, k, v, o, lse, 0.125, False, valid, BF16, f"mask ring N={n}")
 
 
+@pytest.mark.parametrize("n", [64 * t + r for t in (3, 6, 10, 17) for r in (0, 32, 45)])
+def test_causal_key_mask_ring_lengths(n):
+    """Causal rows with both key-mask forms over several tile counts and
+    ends (whole tile, one half tile, ragged): each wave's last visible half
+    tile drains in the pipeline with the diagonal or the valid length as a
+    per-row limit, the mask words on top.  Entry 1's valid length ends
+    inside the sequence, so rows past it are limited by the length instead
+    of the diagonal; entry 2's ends on a half-tile boundary."""
+    B, H = 3, 2
+    rng = np.random.default_rng(7300 + n)
+    valid = rng.random((B, n)) > 0.1
+    valid[:, 0] = True
+    lens = [n, max(1, (2 * n) // 3), max(32, 32 * (n // 64))]
+    q, k, v = inputs(B, H, n, "bf16", 7310 + n)
+    o, lse = run(q, k, v, 0.125, True, key_len=lens, key_valid=valid)
+    both = valid & (np.arange(n)[None, :] < np.array(lens)[:, None])
+    check(q, k, v, o, lse, 0.125, True, both, BF16, f"causal mask ring N={n}")
+
+
 @pytest.mark.parametrize("B, H", [(3, 21), (4, 16)])
 def test_key_mask_wave_count_threshold(B, H):
     """The key-mask kernel on both sides of the 4-wave / 8-wave choice
