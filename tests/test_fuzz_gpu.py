@@ -27,7 +27,7 @@ def _length(rng):
     return int(rng.integers(1, 2100))
 
 
-def _forward_cases(count=48, seed=2024):
+def _forward_cases(count=96, seed=2024):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(count):
