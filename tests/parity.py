@@ -18,6 +18,18 @@ BF16 = dict(o_max=2e-2, o_mean=2e-3, lse_max=1e-3, rel_fro=1e-2)
 FP32 = dict(o_max=1e-5, o_mean=1e-5, lse_max=1e-3, rel_fro=1e-5)
 
 
+def bf16_bar_for(v_max, o_ref_max):
+    """The bf16 bars for inputs wider than the workloads' (standard normal
+    values, scales up to 1).  Rounding P to bf16 (unit roundoff 2^-8) moves
+    a weighted average of V rows by up to 2^-8 * max|v_j - O_i| <= 2^-8 *
+    2 max|V|, and rounding O moves it by up to 2^-8 * |O|; where that sum
+    exceeds the fixed max bar (|V| above ~2.5), the max bar is that sum.
+    The mean and relative bars stay fixed."""
+    bar = dict(BF16)
+    bar["o_max"] = max(BF16["o_max"], 2.0 ** -8 * (2.0 * v_max + o_ref_max))
+    return bar
+
+
 def errors(o, lse, o_ref, lse_ref):
     o = np.asarray(o, dtype=np.float64)
     lse = np.asarray(lse, dtype=np.float64)

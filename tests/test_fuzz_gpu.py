@@ -4,7 +4,9 @@ boundaries), causal or not, both key-mask forms (with entries that hide every
 key), packed strided views, fp32 I/O, negative and unusual scales, random
 block-sparse masks, and the backward.  Each
 feature has its own tests; these check that they combine.  The cases are
-drawn once from a fixed seed, so every run sees the same list.
+drawn once from a fixed seed, so every run sees the same list.  Inputs are
+standard normal, wider than the workloads' (sigma 0.5): with sharp rows
+(scales near 1) the bf16 max bar is the rounding bound of bf16_bar_for.
 """
 
 import numpy as np
@@ -13,7 +15,7 @@ import torch
 
 import exact_attention_29_amd as ea
 from oracle import attention, attention_backward
-from tests.parity import BF16, FP32, assert_grad_within, assert_within, errors, grad_magnitudes
+from tests.parity import BF16, FP32, assert_grad_within, assert_within, bf16_bar_for, errors, grad_magnitudes
 from workloads import Workload, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -88,8 +90,8 @@ def test_random_forward(case):
     assert np.all(o_h[empty] == 0.0), "a row that sees no key has O != 0"
     keep = ~empty
     if keep.any():
-        assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]),
-                      FP32 if case["dtype"] == "fp32" else BF16, f"case {case['i']}")
+        bar = FP32 if case["dtype"] == "fp32" else bf16_bar_for(float(v.abs().max()), float(np.abs(o_ref[keep]).max()))
+        assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), bar, f"case {case['i']}")
 
 
 def _backward_cases(count=12, seed=4048):
@@ -150,4 +152,5 @@ def test_random_block_sparse(case):
     assert np.all(o_h[empty] == 0.0), "a row that sees no key has O != 0"
     keep = ~empty
     if keep.any():
-        assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), BF16, f"case {case['i']}")
+        bar = bf16_bar_for(float(v.abs().max()), float(np.abs(o_ref[keep]).max()))
+        assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), bar, f"case {case['i']}")
