@@ -772,11 +772,13 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     });
   }
   t = t_fast_end;
-  if (!kSparse && t >= 2 && (last_h >> 1) == t && (last_h == 2 * t || !needs_lim(2 * t))) {
+  // (not for causal block lists: there every wave's last listed half is the
+  // diagonal tile's, which measured slower drained)
+  if (!(kSparse && kCausal) && t >= 2 && (last_h >> 1) == t && (last_h == 2 * t || !needs_lim(2 * t))) {
     // the last visible key of this lane's row, as an offset in half last_h
     // (the general path's limit; only keys below n_k, whose LDS rows hold
     // loaded data, stay visible)
-    drain_lim = (kCausal ? min(qi, n_k - 1) : n_k - 1) - 32 * last_h;
+    drain_lim = (kCausal ? min(qi, n_k - 1) : n_k - 1) - 32 * real_half(last_h);
     tile_drain(t, needs_lim(last_h));
     ++t;
   }
