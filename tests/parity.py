@@ -19,8 +19,8 @@ FP32 = dict(o_max=1e-5, o_mean=1e-5, lse_max=1e-3, rel_fro=1e-5)
 
 
 def bf16_bar_for(v_max, o_ref_max):
-    """The bf16 bars for inputs wider than the workloads' (standard normal
-    values, scales up to 1).  Rounding P to bf16 (unit roundoff 2^-8) moves
+    """The bf16 bars for sharper rows than the workloads' (standard normal
+    values with scales up to 1, not 1/8).  Rounding P to bf16 (unit roundoff 2^-8) moves
     a weighted average of V rows by up to 2^-8 * max|v_j - O_i| <= 2^-8 *
     2 max|V|, and rounding O moves it by up to 2^-8 * |O|; where that sum
     exceeds the fixed max bar (|V| above ~2.5), the max bar is that sum.

@@ -5,8 +5,8 @@ key), packed strided views, fp32 I/O, negative and unusual scales, random
 block-sparse masks, and the backward.  Each
 feature has its own tests; these check that they combine.  The cases are
 drawn once from a fixed seed, so every run sees the same list.  Inputs are
-standard normal, wider than the workloads' (sigma 0.5): with sharp rows
-(scales near 1) the bf16 max bar is the rounding bound of bf16_bar_for.
+standard normal and scales reach 1 (eight times the workloads'), so rows
+can be far sharper: the bf16 max bar is the rounding bound of bf16_bar_for.
 """
 
 import numpy as np
