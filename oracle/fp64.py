@@ -37,6 +37,13 @@ and l (row sum of exp(s - m)) for the backward pass (FlashAttention reading
 notes, section "recomputation").  They are returned folded into one number
 per row, LSE_i = m_i + ln(l_i), natural log of the scaled, masked scores.
 
+Non-finite inputs are not scrubbed (the pages say nothing about them; the
+plainest reading is the definition applied as written): a NaN in a visible
+key's K row makes that row's scores, hence its O and LSE, NaN; a NaN in a
+visible key's V row makes that feature of O NaN.  A hidden key takes no part
+at all: its score is replaced by -inf before the softmax and its V row is
+left out of the weighted sum.
+
 Arithmetic: inputs are converted exactly to float64 (bf16 and fp32 values
 are exact there); scores, exponentials, sums and the final division are
 float64.  The softmax is evaluated in two passes over a full row (max, then
@@ -88,9 +95,21 @@ def _row_sum(e):
     return e.sum(axis=1)
 
 
-def _weighted_values(e, v):
-    """sum_j exp(s_ij - m_i) * v_j, before normalisation: [R, N] x [N, d]."""
-    return e @ v
+def _weighted_values(e, v, vis):
+    """sum_j exp(s_ij - m_i) * v_j over the keys row i sees, before
+    normalisation: [R, N] x [N, d].
+
+    A hidden key takes no part in the sum (its -inf bias removes it), so a
+    non-finite value in a hidden key's V row never reaches the row.  Keys
+    whose V rows are finite go through one matrix product (a hidden key's
+    e_ij is exactly 0 there); the few others are summed over the visible
+    entries only."""
+    fin = np.isfinite(v).all(axis=1)
+    out = e[:, fin] @ v[fin]
+    if not fin.all():
+        eb, vb, visb = e[:, ~fin], v[~fin], vis[:, ~fin]
+        out = out + np.where(visb[:, :, None], eb[:, :, None] * vb[None, :, :], 0.0).sum(axis=1)
+    return out
 
 
 def _normalise(o_unnormalised, l):
@@ -156,7 +175,7 @@ def attention(q, k, v, scale, causal=False, key_valid=None, rows=None,
                     m = np.where(empty, 0.0, m)   # any finite shift: every e_ij is 0
                     e = _exp_shifted(s, m)
                     l = _row_sum(e)
-                    o_r = _normalise(_weighted_values(e, v[b, h]), l)
+                    o_r = _normalise(_weighted_values(e, v[b, h], vis), l)
                     lse_r = _lse(m, l)
                     o_r, lse_r = _empty_row_result(o_r, lse_r, empty)
                     o[b, h, c0:c0 + len(r)] = o_r

@@ -497,6 +497,43 @@ def pin_backward_invariants():
     _close(dk2, dk, 1e-12, "dK under a shared key shift")
 
 
+def pin_nonfinite_inputs():
+    """What a NaN in Q, K or V does under the definition.  Causal rows i < j
+    never see key j, so NaN in K_j and V_j leaves them exactly as with finite
+    values, while rows i >= j (whose scores include q_i . k_j) are NaN in O
+    and LSE.  A key hidden by the padding mask takes no part either.  A NaN
+    in feature f of a visible V row makes column f of O NaN and leaves the
+    other features and LSE alone (features of O are independent)."""
+    rng = _rng(26)
+    B, H, N, d, j, f = 1, 2, 11, 8, 6, 3
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    k_bad, v_bad = k.copy(), v.copy()
+    k_bad[:, :, j] = np.nan
+    v_bad[:, :, j] = np.nan
+    with np.errstate(invalid="ignore"):
+        ref_o, ref_l = O.attention(q, k, v, 0.4, causal=True, row_chunk=4)
+        o, lse = O.attention(q, k_bad, v_bad, 0.4, causal=True, row_chunk=4)
+    _close(o[:, :, :j], ref_o[:, :, :j], 1e-12, "causal rows before a NaN key")
+    _close(lse[:, :, :j], ref_l[:, :, :j], 1e-12, "causal LSE before a NaN key")
+    assert np.isnan(o[:, :, j:]).all() and np.isnan(lse[:, :, j:]).all(), "rows that see a NaN key"
+    valid = np.ones((B, N), dtype=bool)
+    valid[:, j] = False
+    with np.errstate(invalid="ignore"):
+        ref_o, ref_l = O.attention(q, k, v, 0.4, key_valid=valid)
+        o, lse = O.attention(q, k_bad, v_bad, 0.4, key_valid=valid)
+    _close(o, ref_o, 1e-12, "a padded NaN key")
+    _close(lse, ref_l, 1e-12, "LSE with a padded NaN key")
+    v_one = v.copy()
+    v_one[:, :, j, f] = np.nan
+    with np.errstate(invalid="ignore"):
+        ref_o, ref_l = O.attention(q, k, v, 0.4)
+        o, lse = O.attention(q, k, v_one, 0.4)
+    assert np.isnan(o[..., f]).all(), "a NaN value reaches its feature in every row"
+    keep = [g for g in range(d) if g != f]
+    _close(o[..., keep], ref_o[..., keep], 1e-12, "the other features")
+    _close(lse, ref_l, 1e-12, "LSE with a NaN value")
+
+
 INDEPENDENT_PINS = [
     pin_uniform_closed_form,
     pin_identity_closed_form,
@@ -513,6 +550,7 @@ INDEPENDENT_PINS = [
     pin_block_sparse,
     pin_backward_finite_differences,
     pin_backward_invariants,
+    pin_nonfinite_inputs,
 ]
 
 ALL_PINS = INDEPENDENT_PINS + [

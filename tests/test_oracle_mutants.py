@@ -35,7 +35,8 @@ MUTANTS = {
     "exp_sign_flipped": ("_exp_shifted", lambda s, m: np.exp(m[:, None] - s)),
     "exp_base_two": ("_exp_shifted", lambda s, m: np.exp2(s - m[:, None])),
     "sum_drops_last_key": ("_row_sum", lambda e: e[:, :-1].sum(axis=1)),
-    "values_reversed": ("_weighted_values", lambda e, v: e @ v[::-1]),
+    "values_reversed": ("_weighted_values", lambda e, v, vis: e @ v[::-1]),
+    "hidden_values_multiplied": ("_weighted_values", lambda e, v, vis: e @ v),
     "not_normalised": ("_normalise", lambda ou, l: ou),
     "lse_without_max": ("_lse", lambda m, l: np.log(l)),
     "lse_base_two": ("_lse", lambda m, l: m + np.log2(l)),
