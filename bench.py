@@ -240,47 +240,75 @@ class ClockSampler:
                 "window": "sampled while the same launches ran back to back for about 4 s"}
 
 
-def cpu_baseline(w, q, k, v, seconds):
+def cpu_baseline(w, q, k, v, seconds, o_gpu=None, lse_gpu=None):
     """The fp64 oracle, as it stands, on a time-boxed sample of the same
-    workload: the first query rows of head 0, 1, ... against all N keys."""
+    workload: the first query rows of head 0, 1, ... against all N keys, with
+    the BLAS thread pool set to every usable core.  When the GPU's O and LSE
+    (host tensors of the timed launch) are given, the oracle rows it computed
+    are also compared with them."""
     import numpy as np
     from oracle import attention
     from workloads import to_f64
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:  # noqa: BLE001
-        blas = 1
+        limiter = None
     chunk = 256
     rows_done, t0 = 0, time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            qf, kf, vf = (to_f64(t[b:b + 1, h:h + 1]) for t in (q, k, v))
-            for r0 in range(0, w.N, chunk):
-                rows = np.arange(r0, min(r0 + chunk, w.N))
-                attention(qf, kf, vf, w.scale, causal=w.causal, rows=rows)
-                rows_done += len(rows)
+    done = []  # (b, h, rows, o_ref, lse_ref)
+    try:
+        for b in range(w.B):
+            for h in range(w.H):
+                qf, kf, vf = (to_f64(t[b:b + 1, h:h + 1]) for t in (q, k, v))
+                for r0 in range(0, w.N, chunk):
+                    rows = np.arange(r0, min(r0 + chunk, w.N))
+                    o_r, l_r = attention(qf, kf, vf, w.scale, causal=w.causal, rows=rows)
+                    done.append((b, h, rows, o_r[0, 0], l_r[0, 0]))
+                    rows_done += len(rows)
+                    if time.perf_counter() - t0 >= seconds:
+                        break
                 if time.perf_counter() - t0 >= seconds:
                     break
             if time.perf_counter() - t0 >= seconds:
                 break
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+    finally:
+        if limiter is not None:
+            limiter.unregister()
     if w.causal:
-        flops = 0.0  # not used for the default workload
+        pairs = sum(float((rows + 1).sum()) for _, _, rows, _, _ in done)
     else:
-        flops = rows_done * w.N * w.d * 4.0
-    return {
+        pairs = float(rows_done) * w.N
+    flops = pairs * w.d * 4.0
+    out = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas),
+        "cores": int(cores),
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle on {rows_done} query rows x {w.N} keys of {w.name} "
                    f"({rows_done / (w.B * w.H * w.N):.2%} of the workload), {dt:.1f} s wall; "
-                   f"matmuls on {blas} BLAS threads, exp single-threaded; "
-                   f"host has {len(os.sched_getaffinity(0))} usable cores"),
+                   f"matmuls on {cores} BLAS threads (set explicitly), exp single-threaded"),
     }
+    if o_gpu is not None:
+        og, lg = to_f64(o_gpu), to_f64(lse_gpu)
+        dmax = dsum = dl = num = den = 0.0
+        cnt = 0
+        for b, h, rows, o_r, l_r in done:
+            d = np.abs(og[b, h, rows] - o_r)
+            dmax = max(dmax, float(d.max()))
+            dsum += float(d.sum())
+            cnt += d.size
+            dl = max(dl, float(np.abs(lg[b, h, rows] - l_r).max()))
+            num += float(((og[b, h, rows] - o_r) ** 2).sum())
+            den += float((o_r ** 2).sum())
+        out["error_vs_oracle"] = {
+            "rows": rows_done, "o_max_abs": dmax, "o_mean_abs": dsum / max(cnt, 1),
+            "lse_max_abs": dl, "o_rel_fro": (num / den) ** 0.5 if den > 0 else 0.0,
+            "bars": "bf16: max 2e-2, mean 2e-3, LSE 1e-3 (relative Frobenius checked at 1e-2 in the tests)",
+            "of": "the O and LSE of the last timed launch, on the rows the oracle computed"}
+    return out
 
 
 def sparse_flops(w, m):
@@ -438,7 +466,13 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
                         "cache": "cold: a 512 MiB buffer is rewritten before every launch"}
     if with_cpu:
         log("[bench] timing the fp64 oracle on a sample ...")
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, cpu_seconds)
+        # o and lse still hold the last timed launch's output
+        o_host, lse_host = o.cpu(), lse.cpu()
+        cb = cpu_baseline(w, q, k, v, cpu_seconds, o_host, lse_host)
+        err = cb.pop("error_vs_oracle", None)
+        line["cpu_baseline"] = cb
+        if err is not None:
+            line["error_vs_oracle"] = err
     return line
 
 

@@ -849,11 +849,15 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  A row that saw no
-  // key (all hidden by the valid length or the mask) has l = 0: O = 0 and
-  // LSE = -inf, the empty sum.
+  // key (all hidden by the valid length or the mask) has l = +0 exactly: O = 0
+  // and LSE = -inf, the empty sum.  The test is on the bits (l is a sum of
+  // exp2 results: +0, positive or NaN), so a NaN row sum -- a NaN in a key or
+  // query the row sees -- stays NaN in O and LSE (and no NaN-aware compare is
+  // needed under -fno-honor-nans).
   const float l_tot = half_swap_sum(l_run);
+  const bool empty_row = __builtin_bit_cast(unsigned, l_tot) == 0u;
   if (qi < n) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = empty_row ? 0.f : 1.f / l_tot;
     uint16_t* orow = a.o + head_off(3) + (size_t)qi * a.sn[3];
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
@@ -866,7 +870,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
         *(u32x2*)(orow + f0) = w;
       }
     }
-    if (hi == 0) a.lse[(size_t)bh * n + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (hi == 0) a.lse[(size_t)bh * n + qi] = empty_row ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -887,7 +891,7 @@ struct F32Args {
   const uint32_t* key_bits;   // [B][ceil(N/32)] or null
 };
 
-constexpr int kF32Keys = 16;  // keys per LDS tile in the fp32 kernel
+constexpr int kF32Keys = 8;   // keys per LDS tile in the fp32 kernel
 
 __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
   __shared__ float ks[kF32Keys][kD];
@@ -930,8 +934,9 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     __syncthreads();
     double t[kF32Keys];
     double mx = -INFINITY;
-    // the tile's 16 keys are half of one mask word (k0 is a multiple of 16, k0 < N)
-    static_assert(kF32Keys == 16, "half a mask word per key tile");
+    uint32_t seen = 0;  // bit r: key k0 + r takes part in this row
+    // the tile's keys are a quarter of one mask word (k0 is a multiple of 8, k0 < N)
+    static_assert(32 % kF32Keys == 0, "a key tile within one mask word");
     const uint32_t word = mask_row ? mask_row[k0 >> 5] >> (k0 & 31) : 0xffffffffu;
 #pragma unroll
     for (int r = 0; r < kF32Keys; ++r) {
@@ -939,6 +944,7 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
 #pragma unroll
       for (int f = 0; f < kD; ++f) s = __builtin_fma((double)qv[f], (double)ks[r][f], s);
       const bool vis = k0 + r <= row_last && ((word >> r) & 1u);
+      seen |= (vis ? 1u : 0u) << r;
       t[r] = vis ? s * c : -INFINITY;
       mx = fmax(mx, t[r]);
     }
@@ -949,8 +955,11 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     l_run *= alpha;
 #pragma unroll
     for (int f = 0; f < kD; ++f) acc[f] *= alpha;
+    // a hidden key takes no part: its V row is skipped, not multiplied by
+    // p = 0 (so a non-finite value there cannot reach this row)
 #pragma unroll
     for (int r = 0; r < kF32Keys; ++r) {
+      if (!((seen >> r) & 1u)) continue;
       const float p = __builtin_amdgcn_exp2f((float)(t[r] - msub));
       l_run += p;
 #pragma unroll
@@ -958,12 +967,14 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     }
   }
   if (live) {
-    // a row that saw no key: O = 0, LSE = -inf (the empty sum)
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    // a row that saw no key: O = 0, LSE = -inf (the empty sum); l is +0,
+    // positive or NaN, and a NaN stays NaN (the test is on the bits)
+    const bool empty_row = __builtin_bit_cast(unsigned, l_run) == 0u;
+    const float inv = empty_row ? 0.f : 1.f / l_run;
 #pragma unroll
     for (int f = 0; f < kD; ++f) a.o[head + (size_t)qi * kD + f] = acc[f] * inv;
-    a.lse[(size_t)bh * n + qi] = l_run > 0.f ? (float)((m_run + (double)__log2f(l_run)) * 0.6931471805599453)
-                                             : -INFINITY;
+    a.lse[(size_t)bh * n + qi] = empty_row ? -INFINITY
+                                           : (float)((m_run + (double)__log2f(l_run)) * 0.6931471805599453);
   }
 }
 

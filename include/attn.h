@@ -33,8 +33,14 @@
  *   - causal: 0 = every query sees all N keys; non-zero = query i sees keys
  *     0..i (the diagonal included, so no row is empty without a key mask).
  *   - Numerics: scores, the online softmax and both products accumulate in
- *     fp32.  Non-finite inputs are not scrubbed; they propagate as the
- *     definition says.
+ *     fp32 (the fp32 entry points form scores in fp64).  Non-finite inputs
+ *     are not scrubbed: a NaN in the K row of a key a query sees, or in that
+ *     query, makes the query's O row and LSE NaN; a NaN in feature f of a
+ *     seen key's V row makes feature f of O NaN.  A hidden key's score never
+ *     enters the softmax.  The bf16 paths multiply whole 32-key blocks of V
+ *     by their probabilities, a hidden key's being exactly 0, so a
+ *     non-finite V value of a hidden key can still reach the rows that visit
+ *     its block (0 * NaN); the fp32 paths skip hidden keys.
  *   - Errors are reported synchronously, before anything is enqueued; on an
  *     error the outputs are untouched.  A fault inside the kernel surfaces at
  *     the caller's next synchronisation (HIP convention).  No C++ exception
@@ -83,9 +89,11 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o,
                      int causal, void *stream);
 
 /*
- * attn_fwd_fp32: the same operation with fp32 input, output and arithmetic
- * throughout (no bf16 or reduced-precision products).  Same layout,
- * ownership, stream and error rules as attn_fwd; q, k, v, o are float.
+ * attn_fwd_fp32: the same operation with fp32 input and output and no bf16
+ * or reduced-precision products: scores, the running row max and their
+ * difference are formed in fp64 (products of fp32 values are exact there),
+ * exp2 and the sums of P and P V in fp32.  Same layout, ownership, stream
+ * and error rules as attn_fwd; q, k, v, o are float.
  */
 attn_status attn_fwd_fp32(const float *q, const float *k, const float *v,
                           float *o, float *lse, int B, int H, int N, int d,

@@ -50,3 +50,25 @@ def test_flop_count():
     assert w.flops == 4 * 1 * 16 * 11616 ** 2 * 64 == 552_679_243_776
     g = WORKLOADS["gpt2_small_causal"]
     assert g.flops == 2 * 8 * 12 * 1024 ** 2 * 64
+
+
+def test_cpu_baseline_compares_the_gpu_rows():
+    """cpu_baseline's error fields: the oracle's own output (rounded to bf16)
+    is within half a bf16 ulp, and a changed row shows up in the maxima."""
+    import numpy as np
+    import torch
+    from dataclasses import replace
+    from oracle import attention
+    from workloads import make_inputs
+    w = replace(WORKLOADS["bert_large"], B=1, H=2, N=300)
+    q, k, v = make_inputs(w)
+    o, lse = attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), w.scale)
+    og, lg = torch.from_numpy(o).to(torch.bfloat16), torch.from_numpy(lse).float()
+    r = bench.cpu_baseline(w, q, k, v, 30.0, og, lg)
+    e = r["error_vs_oracle"]
+    assert r["cores"] == len(os.sched_getaffinity(0)) and e["rows"] == 600
+    assert e["o_max_abs"] <= 2.0 ** -8 * np.abs(o).max() and e["lse_max_abs"] < 1e-6
+    og[0, 1, 17] += 0.5
+    lg[0, 0, 5] += 0.01
+    e = bench.cpu_baseline(w, q, k, v, 30.0, og, lg)["error_vs_oracle"]
+    assert e["o_max_abs"] >= 0.49 and abs(e["lse_max_abs"] - 0.01) < 1e-4

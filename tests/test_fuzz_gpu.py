@@ -6,7 +6,8 @@ block-sparse masks, and the backward.  Each
 feature has its own tests; these check that they combine.  The cases are
 drawn once from a fixed seed, so every run sees the same list.  Inputs are
 standard normal and scales reach 1 (eight times the workloads'), so rows
-can be far sharper: the bf16 max bar is the rounding bound of bf16_bar_for.
+can be far sharper: cases at the workloads' scale 1/8 keep the fixed bf16
+bars, the others take the per-element rounding bound of bf16_max_bound.
 """
 
 import numpy as np
@@ -15,7 +16,8 @@ import torch
 
 import exact_attention_29_amd as ea
 from oracle import attention, attention_backward
-from tests.parity import BF16, FP32, assert_grad_within, assert_within, bf16_bar_for, errors, grad_magnitudes
+from tests.parity import (BF16, FP32, assert_bf16_elementwise, assert_grad_within, assert_within, errors,
+                          grad_magnitudes)
 from workloads import Workload, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -90,8 +92,14 @@ def test_random_forward(case):
     assert np.all(o_h[empty] == 0.0), "a row that sees no key has O != 0"
     keep = ~empty
     if keep.any():
-        bar = FP32 if case["dtype"] == "fp32" else bf16_bar_for(float(v.abs().max()), float(np.abs(o_ref[keep]).max()))
-        assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), bar, f"case {case['i']}")
+        if case["dtype"] == "fp32" or case["scale"] == 0.125:
+            bar = FP32 if case["dtype"] == "fp32" else BF16
+            assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), bar, f"case {case['i']}")
+        else:
+            o_abs, _ = attention(to_f64(q), to_f64(k), np.abs(to_f64(v)), case["scale"], causal=case["causal"],
+                                 key_valid=valid)
+            assert_bf16_elementwise(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep], o_abs[keep],
+                                    f"case {case['i']}")
 
 
 def _backward_cases(count=12, seed=4048):
@@ -152,5 +160,10 @@ def test_random_block_sparse(case):
     assert np.all(o_h[empty] == 0.0), "a row that sees no key has O != 0"
     keep = ~empty
     if keep.any():
-        bar = bf16_bar_for(float(v.abs().max()), float(np.abs(o_ref[keep]).max()))
-        assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), bar, f"case {case['i']}")
+        if case["scale"] == 0.125:
+            assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), BF16, f"case {case['i']}")
+        else:
+            o_abs, _ = attention(to_f64(q), to_f64(k), np.abs(to_f64(v)), case["scale"], causal=case["causal"],
+                                 block_mask=(m, ea.SPARSE_BLOCK_Q, ea.SPARSE_BLOCK_K))
+            assert_bf16_elementwise(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep], o_abs[keep],
+                                    f"case {case['i']}")

@@ -229,3 +229,33 @@ def test_key_mask_wave_count_threshold(B, H):
     o, lse = run(q, k, v, 0.125, False, key_valid=valid)
     check(q, k, v, o, lse, 0.125, False, valid, BF16, f"mask threshold {B}x{H}")
 
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_patch_3mp_random_key_mask(causal):
+    """The 3 MP patch workload (B=1 plus a second entry, H=16, N=11,616) with
+    real padding: entry 0 has a random ~10% of keys masked, entry 1 a valid
+    length of 10,000 and the same kind of random mask; both masks go to the
+    masked kernel at once.  Compared with the oracle on eight random 256-row
+    blocks per head (every row offset of a workgroup) plus the last block."""
+    from workloads import WORKLOADS, block_rows
+    base = WORKLOADS["patch_3mp"]
+    w = Workload("patch_3mp_masked", 2, base.H, base.N, 64, "bf16", base.sigma, base.scale, causal,
+                 base.seed + 10, "")
+    q, k, v = make_inputs(w)
+    rng = np.random.default_rng(77)
+    valid = rng.random((2, w.N)) >= 0.10
+    key_len = [w.N, 10000]
+    print(f"[case] 3 MP masked causal={causal}: {int((~valid).sum())} keys masked, key_len={key_len}", flush=True)
+    o, lse = run(q, k, v, w.scale, causal, key_len=key_len, key_valid=valid)
+    eff = valid & (np.arange(w.N)[None, :] < np.array(key_len)[:, None])
+    rows = block_rows(w.N, 8, seed=78)
+    o_ref, lse_ref = oracle_attention(to_f64(q), to_f64(k), to_f64(v), w.scale, causal=causal,
+                                      key_valid=eff, rows=rows)
+    o_h, lse_h = to_f64(o)[:, :, rows], to_f64(lse)[:, :, rows]
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_h), empty), "empty rows differ"
+    keep = ~empty
+    err = errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep])
+    assert_within(err, BF16, "3 MP masked")
+    print(f"[ok] 3 MP masked causal={causal} rows/head={len(rows)} {err}", flush=True)

@@ -105,6 +105,17 @@ def sample_rows(n, count, seed=12345):
     return np.array(sorted(i for i in fixed if 0 <= i < n), dtype=np.int64)
 
 
+def block_rows(n, blocks, seed, rows_per_block=256):
+    """Sorted query indices of `blocks` distinct random aligned blocks of
+    `rows_per_block` rows (every row offset 0 .. rows_per_block-1 of a
+    workgroup's row block), plus the last, possibly ragged, block."""
+    rng = np.random.default_rng(seed)
+    nb = -(-n // rows_per_block)
+    pick = set(rng.choice(nb, size=min(blocks, nb), replace=False).tolist()) | {nb - 1}
+    rows = [np.arange(b * rows_per_block, min(n, (b + 1) * rows_per_block)) for b in sorted(pick)]
+    return np.concatenate(rows).astype(np.int64)
+
+
 def make_device_normal(shape, seed, device, dtype="bf16", sigma=1.0):
     """A seeded i.i.d. normal tensor drawn on `device` itself, for tensors too
     large to draw on the host and copy (several GiB).  Recipe:
