@@ -79,7 +79,8 @@ def test_patch_workload_full(n):
 
 def test_patch_8mp_blocks():
     """8 MP (P = 38,400): per head, eight random 256-row blocks (every row
-    offset of an 8-wave workgroup) plus the last block, 2,304 rows a head."""
+    offset of an 8-wave workgroup) plus the last block, 2,048-2,304 rows a
+    head."""
     w = WORKLOADS["patch_8mp"]
     print(f"[case] {w.name} {w.shape}", flush=True)
     q, k, v = make_inputs(w)
@@ -95,10 +96,11 @@ def test_patch_8mp_blocks():
         ref_l.append(rl)
         got_o.append(o_h[:, h:h + 1, rows])
         got_l.append(lse_h[:, h:h + 1, rows])
-    err = errors(np.concatenate(got_o, 1), np.concatenate(got_l, 1), np.concatenate(ref_o, 1),
-                 np.concatenate(ref_l, 1))
+    # heads may differ in row count (a random block can be the last one)
+    err = errors(np.concatenate(got_o, 2), np.concatenate(got_l, 2), np.concatenate(ref_o, 2),
+                 np.concatenate(ref_l, 2))
     assert_within(err, BF16, w.name)
-    print(f"[ok] {w.name} rows/head={len(rows)} {err}", flush=True)
+    print(f"[ok] {w.name} rows={sum(r.shape[2] for r in ref_o)} {err}", flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
