@@ -553,16 +553,22 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // epilogue: lane = key, register 4*r4 + e = feature 32*db + 8*r4 + 4*hi + e
-  if (key < n) {
-    uint16_t* dkrow = a.dk + head + (size_t)key * kD;
-    uint16_t* dvrow = a.dv + head + (size_t)key * kD;
+  // epilogue: lane = key, register 4*r4 + e = feature 32*db + 8*r4 + 4*hi + e.
+  // The lane's key and its row addresses are formed again here from the lane
+  // id (v_mbcnt) and uniform values, so nothing per-lane stays live across
+  // the loop for them (the causal instance would spill it to scratch).
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int key_e = key0 + (lane_e & 31);
+  const int hi_e = lane_e >> 5;
+  if (key_e < n) {
+    uint16_t* dkrow = a.dk + head + (size_t)key_e * kD;
+    uint16_t* dvrow = a.dv + head + (size_t)key_e * kD;
     const float scale = a.scale;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int f0 = 32 * db + 8 * r4 + 4 * hi;
+        const int f0 = 32 * db + 8 * r4 + 4 * hi_e;
         const unsigned k01 = pack_bf16(acc_dk[db][4 * r4] * scale, acc_dk[db][4 * r4 + 1] * scale);
         const unsigned k23 = pack_bf16(acc_dk[db][4 * r4 + 2] * scale, acc_dk[db][4 * r4 + 3] * scale);
         const unsigned v01 = pack_bf16(acc_dv[db][4 * r4], acc_dv[db][4 * r4 + 1]);
