@@ -2,8 +2,8 @@
 
 The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
 ``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_fwd_block_sparse``,
-``attn_bwd``, ``attn_bwd_workspace_size``, ``attn_pack_key_mask`` and
-``attn_strerror`` carry the names and
+``attn_bwd``, ``attn_bwd_noalloc``, ``attn_bwd_workspace_size``,
+``attn_pack_key_mask`` and ``attn_strerror`` carry the names and
 arguments
 of the C entry points declared in include/attn.h and only marshal arguments;
 every step of the computation runs in the HIP kernels.
@@ -18,7 +18,7 @@ import os
 import torch  # imported first: the library then binds to torch's HIP runtime
 
 __all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-           "attn_fwd_strided", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_workspace_size",
+           "attn_fwd_strided", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_size",
            "attn_pack_key_mask", "AttnLayout",
            "backward", "attn_strerror", "forward", "pack_key_mask", "AttnError",
            "library_path", "load_library"]
@@ -27,8 +27,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libattn.so")
 _lib = None
 
-ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH = range(5)
-EXPORTED = ("attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
+ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH, ATTN_E_SCRATCH = range(6)
+# the static scratch of attn_bwd_noalloc (ATTN_BWD_NOALLOC_SCRATCH_BYTES in attn.h)
+BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
+EXPORTED = ("attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
             "attn_fwd_strided", "attn_fwd_block_sparse", "attn_pack_key_mask", "attn_strerror")
 SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 128, 64
 
@@ -77,6 +79,8 @@ def load_library():
     lib.attn_fwd_block_sparse.restype = i32
     lib.attn_bwd.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_noalloc.argtypes = [ptr] * 9 + [i32, i32, i32, i32, f32, i32, ptr]
+    lib.attn_bwd_noalloc.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_pack_key_mask.argtypes = [ptr, ptr, i32, i32, ptr]
@@ -137,6 +141,13 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, ca
     """C entry point attn_bwd: raw addresses of the nine tensors and the workspace."""
     _check(load_library().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, float(scale),
                                    int(bool(causal)), stream))
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream):
+    """C entry point attn_bwd_noalloc: attn_bwd without a workspace argument
+    (the library's static device scratch; allocates nothing)."""
+    _check(load_library().attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, float(scale),
+                                           int(bool(causal)), stream))
 
 
 def attn_bwd_workspace_size(B, H, N):

@@ -881,19 +881,26 @@ extern "C" size_t attn_bwd_workspace_size(int B, int H, int N) {
   return (size_t)(2LL * B * H * n_pad * (long long)sizeof(float));
 }
 
-extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                                const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
-                                int N, int d, float scale, int causal, void* stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_E_INVALID;
+namespace {
+
+// Checks and launches shared by attn_bwd and attn_bwd_noalloc; ws is the
+// workspace of attn_bwd_workspace_size(B, H, N) bytes (already checked).
+attn_status bwd_validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                         float scale) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_E_INVALID;
   if (B < 1 || H < 1 || N < 1 || d != kD || !std::isfinite(scale)) return ATTN_E_INVALID;
   if (!sizes_fit(B, H, N)) return ATTN_E_INVALID;
-  const void* vec[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+  const void* vec[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : vec)
     if (misaligned(p, 16)) return ATTN_E_ALIGN;
   if (misaligned(lse, 4)) return ATTN_E_ALIGN;
-  const attn_status st = check_device();
-  if (st != ATTN_OK) return st;
+  return ATTN_OK;
+}
 
+attn_status bwd_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N,
+                       float scale, int causal, void* stream) {
   BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -901,7 +908,7 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
   a.o = static_cast<const uint16_t*>(o);
   a.dout = static_cast<const uint16_t*>(dout);
   a.lse = lse;
-  a.ws = static_cast<float*>(workspace);
+  a.ws = ws;
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
@@ -913,6 +920,8 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
   a.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  // bwd_prep writes every entry of the workspace (padding rows included)
+  // before the main kernels read it: nothing has to start at zero
   long long rows = (long long)B * H * a.n_pad;
   void* pargs[] = {&a, &rows};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_kernel),
@@ -929,4 +938,62 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
       e = launch_main<kWavesDq>(reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq>), a, B, H, N, s);
   }
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+// The workspace of attn_bwd_noalloc: a static device array, one copy per
+// device, alive until the process ends.  Host code never uses its name as an
+// address (that is a host-side stand-in); it asks the runtime once per device
+// for the array's device address and passes that to the kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_BWD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device; null = not looked up
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with that device current).
+attn_status scratch_address(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return ATTN_E_DEVICE;
+  }
+  void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return ATTN_E_DEVICE;
+    }
+    __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+  }
+  *out = static_cast<float*>(p);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
+                                int N, int d, float scale, int causal, void* stream) {
+  if (!workspace) return ATTN_E_INVALID;
+  attn_status st = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (misaligned(workspace, 16)) return ATTN_E_ALIGN;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
+                    stream);
+}
+
+extern "C" attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                                        int H, int N, int d, float scale, int causal, void* stream) {
+  attn_status st = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (attn_bwd_workspace_size(B, H, N) > (size_t)ATTN_BWD_NOALLOC_SCRATCH_BYTES) return ATTN_E_SCRATCH;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  float* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != ATTN_OK) return st;
+  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, scale, causal, stream);
 }

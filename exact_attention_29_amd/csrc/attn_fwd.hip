@@ -1242,6 +1242,8 @@ extern "C" const char* attn_strerror(attn_status s) {
     case ATTN_E_ALIGN: return "misaligned pointer (q, k, v, o need 16 bytes, lse 4 bytes)";
     case ATTN_E_DEVICE: return "no usable device (no HIP device current, or it is not gfx950)";
     case ATTN_E_LAUNCH: return "kernel launch failed";
+    case ATTN_E_SCRATCH:
+      return "the call needs more than the static scratch of attn_bwd_noalloc (16 MiB: 8*B*H*ceil(N/256)*256 bytes)";
   }
   return "unknown status";
 }

@@ -69,7 +69,10 @@ typedef enum attn_status {
     /* No HIP device is current, or the current device is not gfx950. */
     ATTN_E_DEVICE = 3,
     /* The kernel launch was rejected by the runtime. */
-    ATTN_E_LAUNCH = 4
+    ATTN_E_LAUNCH = 4,
+    /* attn_bwd_noalloc only: the call needs more workspace than the
+     * library's static scratch holds (ATTN_BWD_NOALLOC_SCRATCH_BYTES). */
+    ATTN_E_SCRATCH = 5
 } attn_status;
 
 /*
@@ -246,6 +249,31 @@ attn_status attn_bwd(const void *q, const void *k, const void *v,
  * fp32 values per padded row of every head); 0 when B, H or N is below 1.
  */
 size_t attn_bwd_workspace_size(int B, int H, int N);
+
+/*
+ * attn_bwd_noalloc: attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, layout, results and errors as attn_bwd, minus
+ * the workspace: the per-row terms go to a static device array of
+ * ATTN_BWD_NOALLOC_SCRATCH_BYTES (16 MiB) inside the library, one copy per
+ * device, held until the process ends.  The call allocates nothing and needs
+ * no set-up; its first call on a device looks up that device's copy.
+ *   - Size: attn_bwd_workspace_size(B, H, N) must fit the array, i.e.
+ *     B * H * ceil(N / 256) <= 8192 (e.g. 16 heads up to N = 131,072);
+ *     larger calls return ATTN_E_SCRATCH and enqueue nothing.
+ *   - Every call on a device shares that device's array: calls that overlap
+ *     in time on one device (two streams, two host threads) race and give
+ *     wrong gradients.  Serialise them, or use attn_bwd with separate
+ *     workspaces.  The array keeps the last call's contents; every entry a
+ *     call reads is written by the same call first, so nothing needs
+ *     clearing.
+ */
+#define ATTN_BWD_NOALLOC_SCRATCH_BYTES (16u << 20)
+attn_status attn_bwd_noalloc(const void *q, const void *k, const void *v,
+                             const void *o, const float *lse,
+                             const void *dout, void *dq, void *dk, void *dv,
+                             int B, int H, int N, int d, float scale,
+                             int causal, void *stream);
 
 /* Static, human-readable text for a status code; never NULL. */
 const char *attn_strerror(attn_status status);

@@ -41,9 +41,9 @@ def test_library_exports_nothing_else_c_visible():
 
 
 def test_strerror_covers_every_status():
-    texts = [ea.attn_strerror(s) for s in range(5)]
+    texts = [ea.attn_strerror(s) for s in range(6)]
     assert texts[0] == "success"
-    assert len(set(texts)) == 5
+    assert len(set(texts)) == 6
     assert ea.attn_strerror(99) == "unknown status"
 
 
@@ -132,6 +132,31 @@ def test_backward_validation():
     if not torch.cuda.is_available():
         assert bwd(lse=ALIGNED + 4) == ea.ATTN_E_DEVICE
         assert bwd(B=1 << 20, N=64) == ea.ATTN_E_DEVICE   # 2^32 elements per tensor
+
+
+def test_backward_noalloc_validation():
+    """attn_bwd_noalloc: attn_bwd's checks, then the static scratch limit
+    (16 MiB = 8 * B * H * ceil(N/256) * 256 bytes), all before any device
+    call."""
+    lib = ea.load_library()
+
+    def bwd(**kw):
+        ptrs = [kw.get(n, ALIGNED) for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv")]
+        return lib.attn_bwd_noalloc(*ptrs, kw.get("B", 1), kw.get("H", 1), kw.get("N", 100), kw.get("d", 64),
+                                    0.125, 0, None)
+    assert bwd(dq=None) == ea.ATTN_E_INVALID
+    assert bwd(d=32) == ea.ATTN_E_INVALID
+    assert bwd(N=0) == ea.ATTN_E_INVALID
+    assert bwd(dout=ALIGNED + 8) == ea.ATTN_E_ALIGN
+    # 16 heads: N = 131,072 fits exactly, one more row does not
+    assert ea.attn_bwd_workspace_size(1, 16, 131072) == ea.BWD_NOALLOC_SCRATCH_BYTES
+    assert bwd(H=16, N=131073) == ea.ATTN_E_SCRATCH
+    assert bwd(B=8193, H=1, N=256) == ea.ATTN_E_SCRATCH
+    assert "scratch" in ea.attn_strerror(ea.ATTN_E_SCRATCH)
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd(H=16, N=131072) == ea.ATTN_E_DEVICE
+        assert bwd(B=8192, H=1, N=256) == ea.ATTN_E_DEVICE
 
 
 def test_backward_workspace_size():

@@ -6,7 +6,7 @@ scratch memory (private, per-lane HBM); at the sizes of these kernels that
 slows a kernel by tens of times without changing a result, so the parity
 tests cannot see it.  And a kernel that uses any scratch makes the runtime
 allocate private memory for it at its first launch, which a caller that
-must not allocate (graph capture, say) cannot have.  The bar:
+must not allocate (attn_bwd_noalloc, graph capture) cannot have.  The bar:
 no dynamic stack and no scratch anywhere, and two waves per SIMD for every
 bf16 attention kernel (the occupancy the tile sizes and LDS rings are built
 around).
