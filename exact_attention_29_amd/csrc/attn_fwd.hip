@@ -384,6 +384,25 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       const int byte = 2 * (32 * db + 16 * (g & 1) + 4 * (j16 & 3));
       v_off[sec][db] = kTileBytes + row * kRow + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
     }
+  // The same offsets plus kHiShift, opaque to the compiler.  A ds_read takes
+  // a VGPR address plus a 16-bit immediate: reads from a stage at LDS address
+  // 48 KiB or more would need an add per read to form the address.  Reads of
+  // the stages a steady-state step knows at compile time to be high use
+  // these registers with (stage address - kHiShift) as the immediate instead.
+  constexpr int kHiShift = 32768;
+  int k_off_hi[4], v_off_hi[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    k_off_hi[ks] = k_off[ks] + kHiShift;
+    asm volatile("" : "+v"(k_off_hi[ks]));
+  }
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      v_off_hi[sec][db] = v_off[sec][db] + kHiShift;
+      asm volatile("" : "+v"(v_off_hi[sec][db]));
+    }
 
   const float c = a.c;
   f32x16 acc[2];  // O^T, feature blocks db = 0, 1
@@ -531,7 +550,10 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     bf16x8 v[2][2];
     bf16x8 k[4];
   };
-  auto load_ops = [&](const char* pv_base, int pv_h, const char* s_base, int s_h, Ops& o) __attribute__((always_inline)) {
+  // pv_hi / s_hi (compile-time in the steady state): the stage lies at LDS
+  // address 32 KiB or above, read through the shifted offsets
+  auto load_ops = [&](const char* pv_base, int pv_h, const char* s_base, int s_h, Ops& o, bool pv_hi = false,
+                      bool s_hi = false) __attribute__((always_inline)) {
     const char* vb = pv_base + 32 * pv_h * kRow;
     const char* kb = s_base + 32 * s_h * kRow;
 #pragma unroll
@@ -539,10 +561,14 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const char* p = vb + 16 * tt * kRow;
-        o.v[tt][db] = lds_read_vt(p + v_off[0][db], p + v_off[1][db]);
+        if (pv_hi)
+          o.v[tt][db] = lds_read_vt(p + (v_off_hi[0][db] - kHiShift), p + (v_off_hi[1][db] - kHiShift));
+        else
+          o.v[tt][db] = lds_read_vt(p + v_off[0][db], p + v_off[1][db]);
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.k[ks] = lds_read_b128(kb, k_off[ks]);
+    for (int ks = 0; ks < 4; ++ks)
+      o.k[ks] = s_hi ? lds_read_b128(kb, k_off_hi[ks] - kHiShift) : lds_read_b128(kb, k_off[ks]);
   };
 
   // Steady-state step: the operands `cur` (read during the previous step)
@@ -555,7 +581,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   auto step_fast = [&](const Ops& cur, Ops& nxt, const char* npv_base, int npv_h,
                        const char* ns_base, int ns_h, f32x16& s_cur, bf16x8 (&p_cur)[2],
                        f32x16& s_nxt, const bf16x8 (&p_prv)[2], uint32_t vis, bool fetch_words,
-                       int word_j, auto mode_tag) __attribute__((always_inline)) {
+                       int word_j, auto mode_tag, bool npv_hi = false,
+                       bool ns_hi = false) __attribute__((always_inline)) {
     // a drain step (the wave's last visible half tile): no S of a next half,
     // no operands to read ahead; kStepLimit also hides the keys of the half
     // past offset drain_lim of this lane's row (causal diagonal, sequence end)
@@ -592,7 +619,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
         }
         if (slot == 0 && !kDrain) {
           __builtin_amdgcn_sched_barrier(0);
-          load_ops(npv_base, npv_h, ns_base, ns_h, nxt);
+          load_ops(npv_base, npv_h, ns_base, ns_h, nxt, npv_hi, ns_hi);
           // the next tile's mask words: issued here, a whole step before the
           // next wait on LDS operands (which then also covers them)
           if (kKeyMask && fetch_words) {
@@ -651,11 +678,17 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   Ops opA, opB;
   auto tile_fast = [&](int t, auto stage_tag) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_tag)::value;
+    constexpr int st_next = (st + 1) % kStagesK;
     char* const b_cur = stage_ptr(st);
-    char* const b_next = stage_ptr((st + 1) % kStagesK);
+    char* const b_next = stage_ptr(st_next);
     const uint32_t vis0 = vis_next0, vis1 = vis_next1;
-    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0, true, 2 * t + 2, StepNormal());  // j = 2t
-    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1, false, 0, StepNormal());  // j = 2t + 1
+    // stages 2 and up sit at LDS addresses of 32 KiB and more (16 KiB each,
+    // in declaration order): read through the shifted offsets
+    constexpr bool cur_hi = st >= 2, next_hi = st_next >= 2;
+    step_fast(opA, opB, b_cur, 0, b_next, 0, sA, pA, sB, pB, vis0, true, 2 * t + 2, StepNormal(), cur_hi,
+              next_hi);  // j = 2t
+    step_fast(opB, opA, b_cur, 1, b_next, 1, sB, pB, sA, pA, vis1, false, 0, StepNormal(), cur_hi,
+              next_hi);  // j = 2t + 1
     end_tile(t, st);
   };
   // Tile t holding this wave's last visible half tile last_h (2t or 2t+1),
