@@ -115,11 +115,13 @@ constexpr unsigned kRedoBits = 0x4f800000u;  // bit pattern of 2^32: a partial
 constexpr unsigned kInfBits = 0x7f800000u;   // bit pattern of +inf
 
 // kinds of pipelined step: steady state; drain (no next S, no read-ahead);
-// drain with a per-row last visible key (a causal diagonal or ragged half)
-constexpr int kStepNormal = 0, kStepDrain = 1, kStepLimit = 2;
+// drain with a per-row last visible key (a causal diagonal or ragged half);
+// first (half tile 0: no PV of a previous half)
+constexpr int kStepNormal = 0, kStepDrain = 1, kStepLimit = 2, kStepFirst = 3;
 using StepNormal = std::integral_constant<int, kStepNormal>;
 using StepDrain = std::integral_constant<int, kStepDrain>;
 using StepLimit = std::integral_constant<int, kStepLimit>;
+using StepFirst = std::integral_constant<int, kStepFirst>;
 
 struct Bf16Args {
   const uint16_t* q;
@@ -587,7 +589,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     // no operands to read ahead; kStepLimit also hides the keys of the half
     // past offset drain_lim of this lane's row (causal diagonal, sequence end)
     constexpr int kMode = decltype(mode_tag)::value;
-    constexpr bool kDrain = kMode != kStepNormal;
+    constexpr bool kDrain = kMode == kStepDrain || kMode == kStepLimit;
     if constexpr (kMode == kStepLimit) {
       const int lim = drain_lim - 4 * hi;  // register r holds key offset 8*(r/4) + 4*hi + r%4
 #pragma unroll
@@ -611,8 +613,10 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     for (int slot = 0; slot <= 8; ++slot) {
       if (slot < 8) {
         if ((slot & 1) == 1) {
-          const int i = slot >> 1, tt = i >> 1, db = i & 1;
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[tt][db], p_prv[tt], acc[db], 0, 0, 0);
+          if constexpr (kMode != kStepFirst) {
+            const int i = slot >> 1, tt = i >> 1, db = i & 1;
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[tt][db], p_prv[tt], acc[db], 0, 0, 0);
+          }
         } else if constexpr (!kDrain) {
           const int ks = slot >> 1;
           s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.k[ks], qop[ks], ks == 0 ? zero16 : s_nxt, 0, 0, 0);
@@ -763,24 +767,39 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // such a wave stays on the exact-max path (no -inf - -inf, no NaN) until
   // it has one.  Without them, key 0 is visible to every row.
   auto no_reference = [&]() { return (kKeyMask || kSparse) && __any(m_run == -INFINITY); };
-  step_general(0, sA, pA, sB, pB);  // S(1) -> sB, P(0) -> pA
-  if (no_reference()) t_fast_end = 1;
-  if (t_fast_end > 1) {
-    // half 1 on the pipelined path: its operands (PV(0) from tile 0's first
-    // half, S(2) from tile 1's) are read here; it reads those of step 2
-    // (PV(1), S(3)) and, with a key mask, tile 1's words
-    load_ops(lds0, 0, lds1, 0, opB);
-    step_fast(opB, opA, lds0, 1, lds1, 1, sB, pB, sA, pA, kKeyMask ? mask_word(1) : 0xffffffffu, true, 2,
-              StepNormal());
-  } else if (1 < n_half) {
-    step_general(1, sB, pB, sA, pA);
-    if (!no_reference()) t_fast_end = t_fast_steady;
+  if (!kKeyMask && !kSparse && t_fast_end > 1) {
+    // Half 0 needs no mask: it runs on the pipelined path too (S(1) beside
+    // its softmax), with its own row max as the reference (any finite
+    // reference gives the same O and LSE; this is the one the exact path
+    // would set).  Its K operands for S(1) are read here; the step reads
+    // those of half 1 (PV(0), S(2)).  Then half 1 as below.
+    float mx = fmaxf(sA[0], sA[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sA[r], sA[r + 1]));
+    m_run = half_swap_max(mx) * c;
+    load_ops(lds0, 0, lds0, 1, opA);  // K of S(1); its V^T part is not used
+    step_fast(opA, opB, lds0, 0, lds1, 0, sA, pA, sB, pB, 0xffffffffu, false, 0, StepFirst());
+    step_fast(opB, opA, lds0, 1, lds1, 1, sB, pB, sA, pA, 0xffffffffu, false, 0, StepNormal());
+  } else {
+    step_general(0, sA, pA, sB, pB);  // S(1) -> sB, P(0) -> pA
+    if (no_reference()) t_fast_end = 1;
     if (t_fast_end > 1) {
-      // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
-      load_ops(lds0, 1, lds1, 1, opA);
-      if constexpr (kKeyMask) {
-        vis_next0 = mask_word(2);
-        vis_next1 = mask_word(3);
+      // half 1 on the pipelined path: its operands (PV(0) from tile 0's first
+      // half, S(2) from tile 1's) are read here; it reads those of step 2
+      // (PV(1), S(3)) and, with a key mask, tile 1's words
+      load_ops(lds0, 0, lds1, 0, opB);
+      step_fast(opB, opA, lds0, 1, lds1, 1, sB, pB, sA, pA, kKeyMask ? mask_word(1) : 0xffffffffu, true, 2,
+                StepNormal());
+    } else if (1 < n_half) {
+      step_general(1, sB, pB, sA, pA);
+      if (!no_reference()) t_fast_end = t_fast_steady;
+      if (t_fast_end > 1) {
+        // operands of step 2: PV(1) from tile 0's second half, S(3) from tile 1's
+        load_ops(lds0, 1, lds1, 1, opA);
+        if constexpr (kKeyMask) {
+          vis_next0 = mask_word(2);
+          vis_next1 = mask_word(3);
+        }
       }
     }
   }
