@@ -27,7 +27,7 @@ import torch
 import exact_attention_29_amd as ea
 from oracle import attention_backward, attention_backward_sampled
 from tests.parity import assert_grad_within, grad_magnitudes, grad_magnitudes_sampled
-from workloads import WORKLOADS, Workload, make_inputs, sample_rows, to_f64
+from workloads import WORKLOADS, Workload, block_rows, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -89,15 +89,17 @@ def test_backward_workload_shapes(name):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_patch_3mp_sampled(causal):
-    """The 3 MP patch shape (N = 11,616, a ragged last tile) in the
-    backward's own launch configuration, on two of the workload's heads:
-    dQ at 40 sampled query rows and dK, dV at 40 sampled keys (both ends,
-    the ragged tail, random rows) against the oracle's gradients there."""
+    """The 3 MP patch shape (N = 11,616, a ragged last tile) on two of the
+    workload's heads: dQ at three random 128-row blocks plus the last block
+    (every row offset of a dQ workgroup) and dK, dV at three random
+    128-key blocks plus the last (every key offset of a dK/dV workgroup),
+    against the oracle's gradients there."""
     w = WORKLOADS["patch_3mp"]
     q, k, v = (t[:, :2].contiguous() for t in make_inputs(w))
     do = make_inputs(Workload("do", 1, 2, w.N, 64, "bf16", 1.0, w.scale, causal, w.seed + 50, ""))[0]
     dq, dk, dv = grads_gpu(q, k, v, do, w.scale, causal)
-    rows, keys = sample_rows(w.N, 40), sample_rows(w.N, 40, seed=777)
+    rows = block_rows(w.N, 3, seed=81, rows_per_block=128)
+    keys = block_rows(w.N, 3, seed=82, rows_per_block=128)
     ref = attention_backward_sampled(to_f64(q), to_f64(k), to_f64(v), to_f64(do), w.scale, causal, rows, keys)
     mags = grad_magnitudes_sampled(q, k, v, do, w.scale, causal, rows, keys)
     got = (dq[:, :, rows], dk[:, :, keys], dv[:, :, keys])
