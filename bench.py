@@ -43,13 +43,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """C++ source without comments and blank lines, each line stripped: the
+    part of the source that decides the compiled kernel."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.strip() for line in text.splitlines() if line.strip())
+
+
 def kernel_sha():
-    """Hash of the forward kernel's sources (the traffic counters are only
-    reported for the source they were taken on)."""
+    """Hash of the forward kernel's sources, comments and whitespace left out
+    (the traffic counters are only reported for the code they were taken
+    on; a comment edit does not change the kernel)."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -35,15 +35,18 @@
 //     way; another wave's do not;
 //   * online softmax in fp32: exp2 with scale*log2(e) folded into one FMA,
 //     l sums the fp32 probabilities, P is rounded to bf16 for the PV product.
-//     Edge tiles take the exact tile max; the steady state reuses the running
-//     reference max and needs none.  A partial row sum above 2^32 (a score
+//     The first half tile sets the reference max from its own scores (on the
+//     pipelined path when it needs no mask); masked edge tiles take the
+//     exact tile max; the steady state reuses the running reference max and
+//     computes none.  A partial row sum above 2^32 (a score
 //     far above the reference, or an overflow) flags the wave, which then
 //     recomputes its rows with the exact max on every tile (a rare path that
 //     reads K and V straight from global memory);
 //   * causal: key tiles past a wave's last query are skipped, only the
 //     diagonal and ragged half tiles pay for masking.
-// fp32 kernel: one thread per query row, fp32 FMA on the vector ALU, K/V
-// tiles broadcast from LDS; same online softmax.  Used for fp32 I/O.
+// fp32 kernel: one thread per query row on the vector ALU (scores in fp64,
+// exp2 and sums in fp32), 8-key K/V tiles broadcast from LDS, hidden keys
+// skipped; same online softmax.  Used for fp32 I/O.
 
 #include <hip/hip_runtime.h>
 

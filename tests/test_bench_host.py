@@ -72,3 +72,13 @@ def test_cpu_baseline_compares_the_gpu_rows():
     lg[0, 0, 5] += 0.01
     e = bench.cpu_baseline(w, q, k, v, 30.0, og, lg)["error_vs_oracle"]
     assert e["o_max_abs"] >= 0.49 and abs(e["lse_max_abs"] - 0.01) < 1e-4
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The traffic counters stay tied to the kernel's code: editing a comment
+    or blank lines keeps the hash, changing a token does not."""
+    src = "int a = 1; // one\n/* block\n comment */\n\nint b = a + 2;\n"
+    same = "int a = 1;   // another comment\n\n  int b = a + 2;  /* trailing */\n"
+    other = "int a = 1;\nint b = a + 3;\n"
+    assert bench._code_only(src) == bench._code_only(same)
+    assert bench._code_only(src) != bench._code_only(other)
