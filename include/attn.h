@@ -23,8 +23,11 @@
  *   - Ownership: the caller owns every buffer.  q, k, v are only read;
  *     o and lse are only written, and must not overlap q, k, v or each other.
  *     The library keeps no pointer after the call returns, allocates no
- *     device memory (no workspace at any size) and holds no per-call state;
- *     calls are reentrant and may come from several host threads.
+ *     device memory and holds no per-call state: the forward entry points
+ *     need no workspace at any size, attn_bwd takes the caller's, and only
+ *     attn_bwd_noalloc uses memory of the library's own (a static device
+ *     array, see there).  Calls are reentrant and may come from several host
+ *     threads (attn_bwd_noalloc calls on one device must not overlap).
  *   - Stream: `stream` is a hipStream_t passed as void*; NULL means the
  *     default stream.  The call only enqueues work: it returns before the
  *     kernel runs, and the caller synchronises.
