@@ -95,14 +95,39 @@ def traffic_for(workload_name):
     return entry["hbm_bytes_per_launch"]
 
 
+# From idle the shader clock takes ~60 launches of the 3 MP kernel (~35 ms)
+# to ramp up; after the requested warm-up steps, untimed launches (graph
+# replays, for the graph timer) continue until the warm-up has kept the GPU
+# busy this long, so the timed steps see the steady state however few
+# warm-up steps were asked for.
+MIN_WARMUP_SECONDS = 0.5
+WARMUP_RUN = {"launches": 0}
+
+
+def warm_up(fn, warmup):
+    """The requested warm-up steps, then more untimed launches until
+    MIN_WARMUP_SECONDS have passed; the count run is kept in WARMUP_RUN."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(warmup):
+        fn()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < MIN_WARMUP_SECONDS:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    WARMUP_RUN["launches"] = n
+
+
 def time_gpu(fn, steps, warmup, stream):
     """Wall seconds per step (synchronised on both sides of the timed steps)
     and the per-launch durations from HIP events recorded on the launch
     stream between consecutive launches."""
     import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn, warmup)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
     ev[0].record(stream)
@@ -133,8 +158,21 @@ def time_gpu_graph(fn, steps, warmup, stream):
             for _ in range(per_graph):
                 fn()
     torch.cuda.current_stream().wait_stream(side)
-    graph.replay()  # once untimed: the graph's first launch uploads it
+    # The graph's first replay uploads it.  Then untimed replays until the
+    # warm-up has lasted MIN_WARMUP_SECONDS, ending right before the timed
+    # ones: the capture leaves the GPU idle for a moment, and a timed replay
+    # straight after it would start at a lowered clock.
+    t0 = time.perf_counter()
+    replays = 0
+    while True:
+        graph.replay()
+        replays += 1
+        if replays % 4 == 0:  # keep the host at most a few replays ahead
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= MIN_WARMUP_SECONDS:
+                break
     torch.cuda.synchronize()
+    WARMUP_RUN["launches"] = warmup + replays * per_graph
     reps = steps // per_graph
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     t0 = time.perf_counter()
@@ -391,6 +429,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
         ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, **masks)
 
     wall, kern, per = TIMER["fn"](step, steps, warmup, stream)
+    warm_run = WARMUP_RUN["launches"]
     if block_density is not None:
         # the same call without the block mask, for the time ratio
         dense_masks = {kk: vv for kk, vv in masks.items() if kk != "block_mask"}
@@ -455,6 +494,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
         },
         "workspace": {"extra_bytes": int(extra), "mem_get_info_delta": int(free_delta),
                       "output_bytes": int(out_bytes)},
+        "warmup_launches_run": warm_run,
         "timing": {"kernel_ms_mean": round(kern * 1e3, 4), "kernel_ms_median": round(median(per) * 1e3, 4),
                    "kernel_ms_min": round(min(per) * 1e3, 4), "launches": steps,
                    "tflops_at_median": round(flops / median(per) / 1e12, 2),
@@ -513,6 +553,7 @@ def bench_backward(w, steps, warmup):
                     w.causal, torch.cuda.current_stream(dev).cuda_stream)
 
     wall, kern, per = TIMER["fn"](step, steps, warmup, stream)
+    warm_run = WARMUP_RUN["launches"]
     flops = 10.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
     return {
         "metric": "attention backward (dQ, dK, dV) TFLOP/s",
@@ -522,6 +563,7 @@ def bench_backward(w, steps, warmup):
         "config": {"workload": f"{w.name}: {w.what}", "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "scale": w.scale, "flops_counted": "10*B*H*N^2*d (x0.5 causal)"},
         "pct_of_bf16_peak": round(100.0 * flops / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "warmup_launches_run": warm_run,
         "timing": {"ms_mean": round(kern * 1e3, 4), "ms_median": round(median(per) * 1e3, 4),
                    "ms_min": round(min(per) * 1e3, 4),
                    "method": TIMER["method"],

@@ -82,3 +82,23 @@ def test_kernel_hash_ignores_comments_only():
     other = "int a = 1;\nint b = a + 3;\n"
     assert bench._code_only(src) == bench._code_only(same)
     assert bench._code_only(src) != bench._code_only(other)
+
+
+def test_warm_up_lasts_the_minimum_time(monkeypatch):
+    """The warm-up runs the requested steps and then untimed launches until
+    MIN_WARMUP_SECONDS have passed; the count is reported."""
+    import time
+    calls = []
+    monkeypatch.setattr(bench, "MIN_WARMUP_SECONDS", 0.05)
+
+    class FakeCuda:
+        @staticmethod
+        def synchronize():
+            pass
+
+    import torch
+    monkeypatch.setattr(torch, "cuda", FakeCuda)
+    t0 = time.perf_counter()
+    bench.warm_up(lambda: calls.append(time.sleep(0.001)), 3)
+    assert time.perf_counter() - t0 >= 0.05
+    assert bench.WARMUP_RUN["launches"] == len(calls) > 3
