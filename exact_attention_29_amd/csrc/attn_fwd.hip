@@ -390,10 +390,11 @@ attn_fwd_bf16_kernel(Bf16Args a) {
       v_off[sec][db] = kTileBytes + row * kRow + (((byte >> 4) ^ swz(row)) << 4) + (byte & 15);
     }
   // The same offsets plus kHiShift, opaque to the compiler.  A ds_read takes
-  // a VGPR address plus a 16-bit immediate: reads from a stage at LDS address
-  // 48 KiB or more would need an add per read to form the address.  Reads of
-  // the stages a steady-state step knows at compile time to be high use
-  // these registers with (stage address - kHiShift) as the immediate instead.
+  // a VGPR address plus a 16-bit immediate: reads from the stages at LDS
+  // address 64 KiB and above would need an add per read to form the address.
+  // Reads of the stages a steady-state step knows at compile time to lie at
+  // 32 KiB or above use these registers with (stage address - kHiShift) as
+  // the immediate instead.
   constexpr int kHiShift = 32768;
   int k_off_hi[4], v_off_hi[2][2];
 #pragma unroll
