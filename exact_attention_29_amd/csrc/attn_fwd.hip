@@ -559,11 +559,13 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // The K operands of S(j+1) and the V^T operands of one 16-key block tt of
   // PV(j).  s_hi / pv_hi (compile-time in the steady state): the stage lies
   // at LDS address 32 KiB or above, read through the shifted offsets.
-  auto load_k = [&](const char* s_base, int s_h, Ops& o, bool s_hi = false) __attribute__((always_inline)) {
+  auto load_k = [&](const char* s_base, int s_h, Ops& o, bool s_hi = false, int ks0 = 0,
+                    int ks1 = 4) __attribute__((always_inline)) {
     const char* kb = s_base + 32 * s_h * kRow;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      o.k[ks] = s_hi ? lds_read_b128(kb, k_off_hi[ks] - kHiShift) : lds_read_b128(kb, k_off[ks]);
+      if (ks >= ks0 && ks < ks1)
+        o.k[ks] = s_hi ? lds_read_b128(kb, k_off_hi[ks] - kHiShift) : lds_read_b128(kb, k_off[ks]);
   };
   auto load_vt = [&](const char* pv_base, int pv_h, int tt, Ops& o, bool pv_hi = false) __attribute__((always_inline)) {
     const char* p = pv_base + 32 * pv_h * kRow + 16 * tt * kRow;
@@ -583,7 +585,7 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 
   // Steady-state step: the operands `cur` (read during the previous step)
   // feed PV(j-1) and S(j+1); the reads for the next step go out during the
-  // step (K after slot 0, V^T after slots 4 and 6); the softmax of S(j) uses
+  // step (K after slot 0, or 0 and 2, V^T after slots 4 and 6); the softmax of S(j) uses
   // the current reference.  One
   // basic block: 8 slots of one MFMA (PV and S alternating, so dependent
   // MFMAs are two slots apart) and one vector-ALU chunk (two exponentials
@@ -630,17 +632,22 @@ attn_fwd_bf16_kernel(Bf16Args a) {
           const int ks = slot >> 1;
           s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.k[ks], qop[ks], ks == 0 ? zero16 : s_nxt, 0, 0, 0);
         }
-        // the next step's operands: K right after the first MFMA, the two
-        // V^T blocks after the third and fourth PV slots' MFMAs (spreading
-        // the reads over the step evens out the LDS load of the CU's waves:
-        // 3 MP +1.6%, 8 MP +2.9% against reading them all at slot 0)
+        // the next step's operands: K right after the first MFMA (causal
+        // kernels: its second half after slot 2), the two V^T blocks after
+        // slots 4 and 6 (spreading the reads over the step evens out the LDS
+        // load of the CU's waves: 3 MP +1.6%, 8 MP +2.9%, 3 MP causal +4%
+        // against reading them all at slot 0)
         if ((slot == 4 || slot == 6) && !kDrain) {
           __builtin_amdgcn_sched_barrier(0);
           load_vt(npv_base, npv_h, (slot - 4) >> 1, nxt, npv_hi);
         }
+        if (kCausal && slot == 2 && !kDrain) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_k(ns_base, ns_h, nxt, ns_hi, 2, 4);
+        }
         if (slot == 0 && !kDrain) {
           __builtin_amdgcn_sched_barrier(0);
-          load_k(ns_base, ns_h, nxt, ns_hi);
+          load_k(ns_base, ns_h, nxt, ns_hi, 0, kCausal ? 2 : 4);
           // the next tile's mask words: issued here, a whole step before the
           // next wait on LDS operands (which then also covers them)
           if (kKeyMask && fetch_words) {
