@@ -1,14 +1,16 @@
 """Exact attention forward on MI355X: a thin Python binding over libattn.so.
 
 The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
-``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_fwd_block_sparse``,
+``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_fwd_split``,
+``attn_fwd_split_workspace_size``, ``attn_fwd_block_sparse``,
 ``attn_bwd``, ``attn_bwd_noalloc``, ``attn_bwd_workspace_size``,
 ``attn_pack_key_mask`` and ``attn_strerror`` carry the names and
 arguments
 of the C entry points declared in include/attn.h and only marshal arguments;
 every step of the computation runs in the HIP kernels.
-``forward`` is a convenience wrapper that allocates the outputs with torch
-and launches on torch's current stream.  There is no CPU fallback: without
+``forward`` is a convenience wrapper that allocates the outputs (and the
+split workspace, once per device and stream) with torch and launches on
+torch's current stream.  There is no CPU fallback: without
 the built library (or without a gfx950 device) every call raises.
 """
 
@@ -18,10 +20,10 @@ import os
 import torch  # imported first: the library then binds to torch's HIP runtime
 
 __all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-           "attn_fwd_strided", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_size",
+           "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_size",
            "attn_pack_key_mask", "AttnLayout",
            "backward", "attn_strerror", "forward", "pack_key_mask", "AttnError",
-           "library_path", "load_library"]
+           "library_path", "load_library", "split_workspace"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libattn.so")
@@ -31,7 +33,8 @@ ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH, ATTN_E_SCRA
 # the static scratch of attn_bwd_noalloc (ATTN_BWD_NOALLOC_SCRATCH_BYTES in attn.h)
 BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
 EXPORTED = ("attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-            "attn_fwd_strided", "attn_fwd_block_sparse", "attn_pack_key_mask", "attn_strerror")
+            "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse",
+            "attn_pack_key_mask", "attn_strerror")
 SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 128, 64
 
 
@@ -75,6 +78,11 @@ def load_library():
     lib.attn_fwd_strided.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32,
                                      lay, lay, lay, lay, ptr, ptr, ptr]
     lib.attn_fwd_strided.restype = i32
+    lib.attn_fwd_split.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32,
+                                   lay, lay, lay, lay, ptr, ptr, ptr, ctypes.c_size_t, ptr]
+    lib.attn_fwd_split.restype = i32
+    lib.attn_fwd_split_workspace_size.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_fwd_split_workspace_size.restype = i32
     lib.attn_fwd_block_sparse.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32, ptr, ptr]
     lib.attn_fwd_block_sparse.restype = i32
     lib.attn_bwd.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr]
@@ -129,6 +137,22 @@ def attn_fwd_strided(q, k, v, o, lse, B, H, N, d, scale, causal, q_layout, k_lay
     _check(load_library().attn_fwd_strided(q, k, v, o, lse, B, H, N, d, float(scale), int(bool(causal)),
                                            ref(q_layout), ref(k_layout), ref(v_layout), ref(o_layout),
                                            key_len, key_bits, stream))
+
+
+def attn_fwd_split(q, k, v, o, lse, B, H, N, d, scale, causal, q_layout, k_layout, v_layout,
+                   o_layout, key_len, key_bits, workspace, workspace_bytes, stream):
+    """C entry point attn_fwd_split: attn_fwd_strided plus a workspace (raw
+    address and size in bytes; layouts AttnLayout or None)."""
+    _check(load_library().attn_fwd_split(q, k, v, o, lse, B, H, N, d, float(scale), int(bool(causal)),
+                                         q_layout, k_layout, v_layout, o_layout, key_len, key_bits,
+                                         workspace, workspace_bytes, stream))
+
+
+def attn_fwd_split_workspace_size():
+    """C entry point attn_fwd_split_workspace_size: bytes for the current device."""
+    n = ctypes.c_size_t(0)
+    _check(load_library().attn_fwd_split_workspace_size(ctypes.byref(n)))
+    return n.value
 
 
 def attn_fwd_block_sparse(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, stream):
@@ -202,6 +226,34 @@ def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+# forward()'s split workspaces: one per (device index, stream handle), so
+# that calls on different streams never share one
+_SPLIT_WS = {}
+# the first bytes of a workspace hold the arrival counters (at most 64 ints
+# per XCD, 8 XCDs); attn_fwd_split needs them zero at the start of a call
+_SPLIT_COUNT_BYTES = 2048
+
+
+def split_workspace(device, stream):
+    """The workspace forward() hands attn_fwd_split on (device, stream): a
+    uint8 tensor of attn_fwd_split_workspace_size() bytes whose counters
+    start at zero; every completed call leaves them zero.  Made on first
+    use; under graph capture it comes from the graph's memory pool and only
+    its counter block is cleared, by a fill kernel captured with it."""
+    key = (device.index, stream)
+    ws = _SPLIT_WS.get(key)
+    if ws is None:
+        with torch.cuda.device(device):
+            n = attn_fwd_split_workspace_size()
+            if torch.cuda.is_current_stream_capturing():
+                ws = torch.empty(n, dtype=torch.uint8, device=device)
+                ws[:_SPLIT_COUNT_BYTES].zero_()
+            else:
+                ws = torch.zeros(n, dtype=torch.uint8, device=device)
+        _SPLIT_WS[key] = ws
+    return ws
+
+
 def _layout(t):
     """AttnLayout of a [B, H, N, d] tensor view with contiguous features."""
     sb, sh, sn, sf = t.stride()
@@ -211,7 +263,7 @@ def _layout(t):
 
 
 def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None, key_valid=None,
-            key_bits=None, block_mask=None):
+            key_bits=None, block_mask=None, split=True):
     """O, LSE for [B, H, N, d] tensors on one device.
 
     bf16 tensors use attn_fwd, fp32 tensors attn_fwd_fp32.  ``scale``
@@ -229,6 +281,12 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
     tensor on the same device (query blocks of 128 rows, key blocks of 64
     keys; only set blocks are computed), with contiguous bf16 q, k, v, out
     and no key mask (attn_fwd_block_sparse).
+    Non-causal bf16 calls without a block mask go through attn_fwd_split
+    (unless ``split=False``) with the workspace split_workspace() keeps for
+    the device and stream; it splits the key tiles of a partial last round
+    of workgroups across the idle CUs.  (A graph captured with it uses the
+    capture stream's workspace: do not replay it while other forward calls
+    run on that stream.)
     Launches on torch's current stream and returns without synchronising.
     """
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -287,7 +345,12 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
         stream = _stream_handle(q.device)
-        if strided:
+        if split and not causal and q.dtype == torch.bfloat16:
+            ws = split_workspace(q.device, stream)
+            lays = [_layout(t) if strided else None for t in (q, k, v, out)]
+            attn_fwd_split(*ptrs, B, H, N, d, scale, causal, *lays, kl_ptr, kv_ptr, ws.data_ptr(), ws.numel(),
+                           stream)
+        elif strided:
             attn_fwd_strided(*ptrs, B, H, N, d, scale, causal, _layout(q), _layout(k), _layout(v),
                              _layout(out), kl_ptr, kv_ptr, stream)
         elif kl_ptr or kv_ptr:

@@ -24,7 +24,8 @@
  *     o and lse are only written, and must not overlap q, k, v or each other.
  *     The library keeps no pointer after the call returns, allocates no
  *     device memory and holds no per-call state: the forward entry points
- *     need no workspace at any size, attn_bwd takes the caller's, and only
+ *     need no workspace at any size (attn_fwd_split optionally takes the
+ *     caller's to run faster), attn_bwd takes the caller's, and only
  *     attn_bwd_noalloc uses memory of the library's own (a static device
  *     array, see there).  Calls are reentrant and may come from several host
  *     threads (attn_bwd_noalloc calls on one device must not overlap).
@@ -182,6 +183,59 @@ attn_status attn_fwd_strided(const void *q, const void *k, const void *v,
                              const attn_layout *v_layout,
                              const attn_layout *o_layout, const int *key_len,
                              const unsigned *key_bits, void *stream);
+
+/*
+ * attn_fwd_split: attn_fwd_strided, faster when the query tiles leave the
+ * last round of workgroups mostly empty.  A non-causal call runs query
+ * tiles of 256 rows, one workgroup per compute unit at a time; when the
+ * tiles left after the whole rounds fill at most half of a round (8 MP
+ * patches at 16 heads: 2,400 tiles = 9 rounds of 256 CUs and 96 left; 16
+ * heads at N = 5,120: 320 tiles = 1 round and 64 left), the workgroups of
+ * that round instead share the leftover tiles' keys: each takes an equal,
+ * contiguous run of (tile, 64-key tile) pairs -- one or two pieces of
+ * query tiles, done one after the other -- and the pieces of one query
+ * tile are combined from their row maxima, row sums and unnormalised
+ * outputs: the blockwise softmax identity of the FlashAttention reading
+ * notes (section "proposed method", tiling), applied across workgroups.
+ * The result is the same attention up to rounding (the bf16 product and
+ * fp32 sums are split at different keys); it is deterministic (pieces are
+ * merged in a fixed order whichever finishes last).  A nearly full last
+ * round is left alone: the part is power-limited, and with a few CUs idle
+ * the others clock higher, so splitting it gains nothing.
+ *   workspace       : device memory owned by the caller, 256-byte aligned,
+ *                     at least attn_fwd_split_workspace_size() bytes (about
+ *                     35 MB on a 256-CU device; ATTN_E_INVALID when smaller
+ *                     or NULL, ATTN_E_ALIGN when misaligned).  Its first
+ *                     256 * ceil(32 * (CUs/8) / 256) bytes are arrival
+ *                     counters that must be zero when a call starts: zero
+ *                     the whole workspace once after allocating it; every
+ *                     call leaves the counters zero when it completes.  The
+ *                     rest holds partial results and needs no clearing.
+ *                     Calls that overlap in time (two streams) need separate
+ *                     workspaces.
+ * Causal calls, calls whose last round is more than half full, calls with
+ * no whole round and rows shorter than 10,240 keys (there the 4-wave
+ * launch of attn_fwd_strided already spreads the rows over every CU), and
+ * rows shorter than 64 * (CUs / 8) keys run exactly as attn_fwd_strided
+ * and do not touch the workspace.  Other arguments, layouts, masks and
+ * errors as attn_fwd_strided.
+ */
+attn_status attn_fwd_split(const void *q, const void *k, const void *v,
+                           void *o, float *lse, int B, int H, int N, int d,
+                           float scale, int causal,
+                           const attn_layout *q_layout,
+                           const attn_layout *k_layout,
+                           const attn_layout *v_layout,
+                           const attn_layout *o_layout, const int *key_len,
+                           const unsigned *key_bits, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace attn_fwd_split needs on the current device (it depends
+ * only on the device's compute-unit count), into *bytes.  ATTN_E_INVALID
+ * for a NULL bytes, ATTN_E_DEVICE as attn_fwd.
+ */
+attn_status attn_fwd_split_workspace_size(size_t *bytes);
 
 /*
  * attn_fwd_block_sparse: block-sparse attention, the variant described on
