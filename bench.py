@@ -63,20 +63,40 @@ def kernel_sha():
     return h.hexdigest()[:16]
 
 
-def kernel_name(w, B, H, N, sparse, bit_mask):
+def library_splits(B, H, N, cus):
+    """Whether attn_fwd_split splits the last round of a non-causal call
+    (the library's rule, restated: 256-row tiles dealt to 8 XCDs of C = cus/8
+    CUs; split when the tiles left past the whole rounds fill at most half a
+    round, there is a whole round before them or the rows have at least 160
+    key tiles, no XCD's leftover is a whole round, the rows are at least
+    64*C keys long, and C*C*ceil(N/64) < 2^31)."""
+    c = cus // 8 if cus >= 16 else 1
+    tiles = B * H * -(-N // 256)
+    n_kt = -(-N // 64)
+    per, r8 = divmod(tiles, 8)
+    rounds = per // c
+    rem_max = per + (1 if r8 else 0) - rounds * c
+    left = tiles - 8 * rounds * c
+    return (0 < rem_max < c and n_kt >= c and 2 * left <= 8 * c and (rounds >= 1 or n_kt >= 160)
+            and c * c * n_kt < 2 ** 31 and c <= 64)
+
+
+def kernel_name(w, B, H, N, sparse, bit_mask, split=True):
     """The forward kernel instantiation a call runs (the library's choice:
-    block-sparse and causal calls 4 waves; non-causal 8 waves when
-    B*H*ceil(N/256) reaches the CU count, else 4)."""
+    block-sparse and causal calls 4 waves; non-causal through
+    attn_fwd_split the split 8-wave kernel when library_splits, else 8
+    waves when B*H*ceil(N/256) reaches the CU count, else 4)."""
     import torch
-    causal = "true" if w.causal else "false"
+    mask = "true" if bit_mask else "false"
     if sparse:
-        return "attn_fwd_bf16_kernel<%s, 4, false, true>" % causal
+        return "attn_fwd_bf16_kernel<%s, 4, false, true, false>" % ("true" if w.causal else "false")
     if w.causal:
-        waves = 4
-    else:
-        cus = torch.cuda.get_device_properties(0).multi_processor_count
-        waves = 8 if B * H * ((N + 255) // 256) >= cus else 4
-    return "attn_fwd_bf16_kernel<%s, %d, %s, false>" % (causal, waves, "true" if bit_mask else "false")
+        return "attn_fwd_bf16_kernel<true, 4, %s, false, false>" % mask
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if split and library_splits(B, H, N, cus):
+        return "attn_fwd_bf16_kernel<false, 8, %s, false, true>" % mask
+    waves = 8 if B * H * ((N + 255) // 256) >= cus else 4
+    return "attn_fwd_bf16_kernel<false, %d, %s, false, false>" % (waves, mask)
 
 
 def traffic_for(workload_name):
@@ -371,7 +391,7 @@ def sparse_flops(w, m):
 
 
 def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=False, mask="none",
-              layout="contiguous", block_density=None):
+              layout="contiguous", block_density=None, split=True):
     import torch
     import exact_attention_29_amd as ea
     from workloads import make_inputs
@@ -393,7 +413,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     stream = torch.cuda.current_stream(dev)
     # key padding as the pages' layer passes it: every key valid (an all-False
     # padding mask), given as a per-entry length or as a byte mask
-    masks = {}
+    masks = {"split": split}
     if mask == "len":
         masks["key_len"] = torch.full((B,), N, dtype=torch.int32, device=dev)
     elif mask == "bytes":
@@ -433,6 +453,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     if block_density is not None:
         # the same call without the block mask, for the time ratio
         dense_masks = {kk: vv for kk, vv in masks.items() if kk != "block_mask"}
+        dense_masks["split"] = False  # the kernel the block-sparse one mirrors
         _, dense_kern, _ = TIMER["fn"](lambda: ea.forward(qd, kd, vd, scale=w.scale, causal=w.causal, out=o,
                                                        lse=lse, **dense_masks), steps, warmup, stream)
     clock_info = None
@@ -484,7 +505,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": kernel_name(w, B, H, N, block_density is not None, mask == "bytes"),
+            "kernel": kernel_name(w, B, H, N, block_density is not None, mask == "bytes", split),
             "kernel_ms": round(kern * 1e3, 4),
             "algorithmic_bytes": alg_bytes,
             # at the ridge (short sequences) the HBM view matters as well
@@ -493,7 +514,10 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
                          "frac": round(alg_bytes / kern / 1e9 / PEAK_HBM_GBS, 4)},
         },
         "workspace": {"extra_bytes": int(extra), "mem_get_info_delta": int(free_delta),
-                      "output_bytes": int(out_bytes)},
+                      "output_bytes": int(out_bytes),
+                      "split_workspace_bytes": int(ea.attn_fwd_split_workspace_size()) if split else 0,
+                      "note": "extra: per call, beyond O and LSE; split_workspace_bytes: held once per "
+                              "device and stream by forward() for attn_fwd_split, the same at any size"},
         "warmup_launches_run": warm_run,
         "timing": {"kernel_ms_mean": round(kern * 1e3, 4), "kernel_ms_median": round(median(per) * 1e3, 4),
                    "kernel_ms_min": round(min(per) * 1e3, 4), "launches": steps,
@@ -626,6 +650,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="patch_3mp")
     ap.add_argument("--n", type=int, default=None, help="override the sequence length")
+    ap.add_argument("--heads", type=int, default=None, help="override the head count")
     ap.add_argument("--causal", choices=["yes", "no"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -643,6 +668,8 @@ def main():
                     help="read q, k, v as head views of one packed projection output")
     ap.add_argument("--mask", choices=["none", "len", "bytes"], default="none",
                     help="time attn_fwd_masked with every key valid, as a length or a byte mask")
+    ap.add_argument("--no-split", action="store_true",
+                    help="call forward(split=False): no key split of the last round (attn_fwd / attn_fwd_strided)")
     ap.add_argument("--workspace-sweep", action="store_true",
                     help="only measure the device memory a call needs beyond O and LSE, "
                          "at P = 1,944 .. 38,400, and fit it against P")
@@ -713,7 +740,8 @@ def main():
                 steps = max(args.steps, 200) if w.flops < 2e10 else args.steps
                 warm = max(args.warmup, 1000) if w.flops < 2e10 else args.warmup
                 log(f"[bench] {w.name} {w.shape} causal={w.causal} mask={mask} layout={layout} density={dens}")
-                line = bench_one(w, steps, warm, False, 0, mask=mask, layout=layout, block_density=dens)
+                line = bench_one(w, steps, warm, False, 0, mask=mask, layout=layout, block_density=dens,
+                                 split=not args.no_split)
                 f.write(json.dumps(line) + "\n")
                 f.flush()
                 log(f"[bench] {w.name}: {line['value']} TFLOP/s, kernel {line['roofline']['kernel_ms']} ms")
@@ -722,13 +750,16 @@ def main():
     w = WORKLOADS[args.workload]
     if args.n:
         w = w.with_n(args.n)
+    if args.heads:
+        from dataclasses import replace
+        w = replace(w, H=args.heads, name=f"{w.name}_h{args.heads}")
     if args.causal:
         from dataclasses import replace
         w = replace(w, causal=args.causal == "yes")
     log(f"[bench] {w.name} {w.shape} {w.dtype} causal={w.causal} steps={args.steps} warmup={args.warmup}")
     line = bench_one(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds,
                      cold_launches=args.cold, clock=not args.no_clock, mask=args.mask,
-                     layout=args.layout, block_density=args.block_density)
+                     layout=args.layout, block_density=args.block_density, split=not args.no_split)
     print(json.dumps(line), flush=True)
 
 

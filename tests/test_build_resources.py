@@ -35,7 +35,8 @@ def report():
 def test_report_lists_every_kernel():
     names = report()
     fwd = [n for n in names if "attn_fwd_bf16_kernel" in n]
-    assert len(fwd) == 8, fwd  # {non-causal 8 and 4 waves, causal} x {key mask or not}, 2 block-sparse
+    # {non-causal 8 and 4 waves, non-causal split, causal} x {key mask or not}, 2 block-sparse
+    assert len(fwd) == 10, fwd
     for kind in ("attn_fwd_f32_kernel", "attn_pack_key_mask_kernel", "bwd_prep_kernel"):
         assert sum(kind in n for n in names) == 1, kind
     assert sum("bwd_dkdv_kernel" in n for n in names) == 2
