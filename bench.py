@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_29_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_common.h")]
+KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_29_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_common.h", "attn_split.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak at H=16,d=64,P=11616"
 

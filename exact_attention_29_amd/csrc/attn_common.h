@@ -46,7 +46,7 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // XCD-aware block remap.  Workgroups are dealt round-robin to the 8 XCDs; this
 // makes the workgroups that land on one XCD take consecutive logical tiles, so
 // the query tiles of one head share that XCD's L2 while they stream its K/V.
-__device__ __forceinline__ int xcd_remap(int w, int total) {
+__host__ __device__ __forceinline__ int xcd_remap(int w, int total) {
   const int per = total >> 3, rem = total & 7;
   const int x = w & 7, i = w >> 3;
   return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;

@@ -230,3 +230,22 @@ def test_binding_raises_without_compute_on_cpu_tensors():
         ea.forward(q, q, q)
     with pytest.raises(TypeError):
         ea.forward(q.half(), q.half(), q.half())
+
+
+def test_split_validation():
+    lib = ea.load_library()
+
+    def split(ws=ALIGNED, size=1 << 30, q=ALIGNED, N=8):
+        return lib.attn_fwd_split(q, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, N, 64, 0.125, 0,
+                                  None, None, None, None, None, None, ws, size, None)
+    assert split(ws=None) == ea.ATTN_E_INVALID           # the workspace is required
+    assert split(q=None) == ea.ATTN_E_INVALID
+    assert split(N=0) == ea.ATTN_E_INVALID
+    assert split(q=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    n = ctypes.c_size_t(7)
+    assert lib.attn_fwd_split_workspace_size(None) == ea.ATTN_E_INVALID
+    import torch
+    if not torch.cuda.is_available():
+        assert split() == ea.ATTN_E_DEVICE
+        assert lib.attn_fwd_split_workspace_size(ctypes.byref(n)) == ea.ATTN_E_DEVICE
+        assert n.value == 7  # untouched on error
