@@ -515,9 +515,11 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
         },
         "workspace": {"extra_bytes": int(extra), "mem_get_info_delta": int(free_delta),
                       "output_bytes": int(out_bytes),
-                      "split_workspace_bytes": int(ea.attn_fwd_split_workspace_size()) if split else 0,
-                      "note": "extra: per call, beyond O and LSE; split_workspace_bytes: held once per "
-                              "device and stream by forward() for attn_fwd_split, the same at any size"},
+                      "split_workspace_bytes": int(ea.attn_fwd_split_workspace_size(B, H, N, w.causal))
+                      if split and not w.causal and block_density is None else 0,
+                      "note": "extra: per call, beyond O and LSE; split_workspace_bytes: what this call "
+                              "needs for attn_fwd_split (0: not split), held once per device and stream by "
+                              "forward(), the same for every split call"},
         "warmup_launches_run": warm_run,
         "timing": {"kernel_ms_mean": round(kern * 1e3, 4), "kernel_ms_median": round(median(per) * 1e3, 4),
                    "kernel_ms_min": round(min(per) * 1e3, 4), "launches": steps,

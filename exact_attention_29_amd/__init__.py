@@ -81,7 +81,7 @@ def load_library():
     lib.attn_fwd_split.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32,
                                    lay, lay, lay, lay, ptr, ptr, ptr, ctypes.c_size_t, ptr]
     lib.attn_fwd_split.restype = i32
-    lib.attn_fwd_split_workspace_size.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_fwd_split_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_fwd_split_workspace_size.restype = i32
     lib.attn_fwd_block_sparse.argtypes = [ptr, ptr, ptr, ptr, ptr, i32, i32, i32, i32, f32, i32, ptr, ptr]
     lib.attn_fwd_block_sparse.restype = i32
@@ -148,10 +148,11 @@ def attn_fwd_split(q, k, v, o, lse, B, H, N, d, scale, causal, q_layout, k_layou
                                          workspace, workspace_bytes, stream))
 
 
-def attn_fwd_split_workspace_size():
-    """C entry point attn_fwd_split_workspace_size: bytes for the current device."""
+def attn_fwd_split_workspace_size(B, H, N, causal):
+    """C entry point attn_fwd_split_workspace_size: bytes of workspace the
+    call needs on the current device (0: not split)."""
     n = ctypes.c_size_t(0)
-    _check(load_library().attn_fwd_split_workspace_size(ctypes.byref(n)))
+    _check(load_library().attn_fwd_split_workspace_size(B, H, N, int(bool(causal)), ctypes.byref(n)))
     return n.value
 
 
@@ -234,17 +235,17 @@ _SPLIT_WS = {}
 _SPLIT_COUNT_BYTES = 2048
 
 
-def split_workspace(device, stream):
+def split_workspace(device, stream, n):
     """The workspace forward() hands attn_fwd_split on (device, stream): a
-    uint8 tensor of attn_fwd_split_workspace_size() bytes whose counters
+    uint8 tensor of n bytes (what attn_fwd_split_workspace_size reports for
+    a split call; the same for every split call on a device) whose counters
     start at zero; every completed call leaves them zero.  Made on first
     use; under graph capture it comes from the graph's memory pool and only
     its counter block is cleared, by a fill kernel captured with it."""
     key = (device.index, stream)
     ws = _SPLIT_WS.get(key)
-    if ws is None:
+    if ws is None or ws.numel() < n:
         with torch.cuda.device(device):
-            n = attn_fwd_split_workspace_size()
             if torch.cuda.is_current_stream_capturing():
                 ws = torch.empty(n, dtype=torch.uint8, device=device)
                 ws[:_SPLIT_COUNT_BYTES].zero_()
@@ -281,10 +282,10 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
     tensor on the same device (query blocks of 128 rows, key blocks of 64
     keys; only set blocks are computed), with contiguous bf16 q, k, v, out
     and no key mask (attn_fwd_block_sparse).
-    Non-causal bf16 calls without a block mask go through attn_fwd_split
-    (unless ``split=False``) with the workspace split_workspace() keeps for
-    the device and stream; it splits the key tiles of a partial last round
-    of workgroups across the idle CUs.  (A graph captured with it uses the
+    Non-causal bf16 calls without a block mask that attn_fwd_split would
+    split (a mostly empty last round of workgroups; unless ``split=False``)
+    go through it, with the workspace split_workspace() keeps for the device
+    and stream.  (A graph captured with it uses the
     capture stream's workspace: do not replay it while other forward calls
     run on that stream.)
     Launches on torch's current stream and returns without synchronising.
@@ -345,8 +346,10 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
         stream = _stream_handle(q.device)
-        if split and not causal and q.dtype == torch.bfloat16:
-            ws = split_workspace(q.device, stream)
+        need = attn_fwd_split_workspace_size(B, H, N, causal) if split and not causal \
+            and q.dtype == torch.bfloat16 else 0
+        if need:
+            ws = split_workspace(q.device, stream, need)
             lays = [_layout(t) if strided else None for t in (q, k, v, out)]
             attn_fwd_split(*ptrs, B, H, N, d, scale, causal, *lays, kl_ptr, kv_ptr, ws.data_ptr(), ws.numel(),
                            stream)

@@ -1337,11 +1337,11 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
                         int H, int N, int d, float scale, int causal, const int* key_len,
                         const uint32_t* key_bits, void* stream,
                         const attn_layout* const layouts[4] = nullptr,
-                        const uint8_t* block_mask = nullptr, void* workspace = nullptr,
-                        size_t workspace_bytes = 0) {
+                        const uint8_t* block_mask = nullptr, bool allow_split = false,
+                        void* workspace = nullptr, size_t workspace_bytes = 0) {
   attn_status st = validate(q, k, v, o, lse, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
-  if (misaligned(key_len, 4) || misaligned(key_bits, 4)) return ATTN_E_ALIGN;
+  if (misaligned(key_len, 4) || misaligned(key_bits, 4) || misaligned(workspace, 256)) return ATTN_E_ALIGN;
   long long sb[4], sh[4];
   int sn[4];
   const attn_layout* const none[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -1351,10 +1351,6 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
   int cus = 0;
   st = check_device(&cus);
   if (st != ATTN_OK) return st;
-  if (workspace) {
-    if (misaligned(workspace, 256)) return ATTN_E_ALIGN;
-    if (workspace_bytes < split_workspace_bytes(cus)) return ATTN_E_INVALID;
-  }
 
   Bf16Args a;
   a.q = static_cast<const uint16_t*>(q);
@@ -1366,12 +1362,13 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
   // Non-causal: 8-wave workgroups (256 rows, one per CU) when they give
   // every CU at least one; otherwise 4-wave ones, twice as many (a short
   // sequence over few heads would leave CUs idle).
-  // With a workspace, a non-causal dense call may instead split the key
-  // tiles of its last, partial round of 8-wave workgroups (plan_split).
+  // Through attn_fwd_split, a non-causal dense call may instead split the
+  // key tiles of its last, partial round of 8-wave workgroups (plan_split).
   const long long tiles8 = (long long)B * H * ((N + kWavesFull * 32 - 1) / (kWavesFull * 32));
   const int n_kt = (N + kBc - 1) / kBc;
-  const SplitPlan sp = workspace && !causal && !block_mask && kWavesFull == 8 ? plan_split(tiles8, n_kt, cus)
-                                                                              : SplitPlan{false, false, 0, 1};
+  const SplitPlan sp = allow_split && !causal && !block_mask && kWavesFull == 8 ? plan_split(tiles8, n_kt, cus)
+                                                                                : SplitPlan{false, false, 0, 1};
+  if (sp.on && (!workspace || workspace_bytes < split_workspace_bytes(cus))) return ATTN_E_INVALID;
   const bool few = !sp.on && tiles8 < cus;
   const int waves = block_mask ? kSparseBlockQ / 32 : causal ? kWavesCausal : few ? 4 : kWavesFull;
   const int rows = waves * 32;
@@ -1505,18 +1502,19 @@ extern "C" attn_status attn_fwd_split(const void* q, const void* k, const void* 
                                       const attn_layout* o_layout, const int* key_len,
                                       const unsigned* key_bits, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  if (!workspace) return ATTN_E_INVALID;
   const attn_layout* const layouts[4] = {q_layout, k_layout, v_layout, o_layout};
   return launch_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, key_bits, stream, layouts,
-                     nullptr, workspace, workspace_bytes);
+                     nullptr, true, workspace, workspace_bytes);
 }
 
-extern "C" attn_status attn_fwd_split_workspace_size(size_t* bytes) {
-  if (!bytes) return ATTN_E_INVALID;
+extern "C" attn_status attn_fwd_split_workspace_size(int B, int H, int N, int causal, size_t* bytes) {
+  if (!bytes || B < 1 || H < 1 || N < 1 || !sizes_fit(B, H, N)) return ATTN_E_INVALID;
   int cus = 0;
   const attn_status st = check_device(&cus);
   if (st != ATTN_OK) return st;
-  *bytes = split_workspace_bytes(cus);
+  const long long tiles8 = (long long)B * H * ((N + kWavesFull * 32 - 1) / (kWavesFull * 32));
+  const bool on = !causal && kWavesFull == 8 && plan_split(tiles8, (N + kBc - 1) / kBc, cus).on;
+  *bytes = on ? split_workspace_bytes(cus) : 0;
   return ATTN_OK;
 }
 

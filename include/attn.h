@@ -202,11 +202,13 @@ attn_status attn_fwd_strided(const void *q, const void *k, const void *v,
  * merged in a fixed order whichever finishes last).  A nearly full last
  * round is left alone: the part is power-limited, and with a few CUs idle
  * the others clock higher, so splitting it gains nothing.
- *   workspace       : device memory owned by the caller, 256-byte aligned,
- *                     at least attn_fwd_split_workspace_size() bytes (about
- *                     35 MB on a 256-CU device; ATTN_E_INVALID when smaller
- *                     or NULL, ATTN_E_ALIGN when misaligned).  Its first
- *                     256 * ceil(32 * (CUs/8) / 256) bytes are arrival
+ *   workspace       : device memory owned by the caller, 256-byte aligned
+ *                     (ATTN_E_ALIGN otherwise), of at least the bytes
+ *                     attn_fwd_split_workspace_size reports for the call:
+ *                     0 when the call is not split (then NULL is fine), else
+ *                     about 35.7 MB on a 256-CU device, the same for every
+ *                     split call (ATTN_E_INVALID when NULL or smaller).  Its
+ *                     first 256 * ceil(32 * (CUs/8) / 256) bytes are arrival
  *                     counters that must be zero when a call starts: zero
  *                     the whole workspace once after allocating it; every
  *                     call leaves the counters zero when it completes.  The
@@ -231,11 +233,14 @@ attn_status attn_fwd_split(const void *q, const void *k, const void *v,
                            size_t workspace_bytes, void *stream);
 
 /*
- * Bytes of workspace attn_fwd_split needs on the current device (it depends
- * only on the device's compute-unit count), into *bytes.  ATTN_E_INVALID
- * for a NULL bytes, ATTN_E_DEVICE as attn_fwd.
+ * Bytes of workspace attn_fwd_split needs for a B x H x N call (causal or
+ * not) on the current device, into *bytes: 0 when that call is not split,
+ * otherwise a size that depends only on the device's compute-unit count.
+ * ATTN_E_INVALID for a NULL bytes or sizes attn_fwd rejects, ATTN_E_DEVICE
+ * as attn_fwd.
  */
-attn_status attn_fwd_split_workspace_size(size_t *bytes);
+attn_status attn_fwd_split_workspace_size(int B, int H, int N, int causal,
+                                          size_t *bytes);
 
 /*
  * attn_fwd_block_sparse: block-sparse attention, the variant described on

@@ -238,14 +238,17 @@ def test_split_validation():
     def split(ws=ALIGNED, size=1 << 30, q=ALIGNED, N=8):
         return lib.attn_fwd_split(q, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, N, 64, 0.125, 0,
                                   None, None, None, None, None, None, ws, size, None)
-    assert split(ws=None) == ea.ATTN_E_INVALID           # the workspace is required
+    assert split(ws=ALIGNED + 16) == ea.ATTN_E_ALIGN     # 256-byte alignment, checked first
     assert split(q=None) == ea.ATTN_E_INVALID
     assert split(N=0) == ea.ATTN_E_INVALID
     assert split(q=ALIGNED + 2) == ea.ATTN_E_ALIGN
     n = ctypes.c_size_t(7)
-    assert lib.attn_fwd_split_workspace_size(None) == ea.ATTN_E_INVALID
+    assert lib.attn_fwd_split_workspace_size(1, 1, 8, 0, None) == ea.ATTN_E_INVALID
+    assert lib.attn_fwd_split_workspace_size(0, 1, 8, 0, ctypes.byref(n)) == ea.ATTN_E_INVALID
+    assert lib.attn_fwd_split_workspace_size(1, 1, 1 << 24, 0, ctypes.byref(n)) == ea.ATTN_E_INVALID
     import torch
     if not torch.cuda.is_available():
         assert split() == ea.ATTN_E_DEVICE
-        assert lib.attn_fwd_split_workspace_size(ctypes.byref(n)) == ea.ATTN_E_DEVICE
-        assert n.value == 7  # untouched on error
+        assert split(ws=None) == ea.ATTN_E_DEVICE
+        assert lib.attn_fwd_split_workspace_size(1, 16, 38400, 0, ctypes.byref(n)) == ea.ATTN_E_DEVICE
+    assert n.value == 7  # untouched on error

@@ -28,6 +28,7 @@ from workloads import Workload, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+DEV_INDEX = 0
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -70,7 +71,7 @@ def run_split(q, k, v, ws=None, key_len=None, key_bits=None, layouts=None, out=N
     zeroed) workspace; returns O, LSE, the workspace."""
     B, H, N, d = q.shape
     if ws is None:
-        ws = torch.zeros(ea.attn_fwd_split_workspace_size(), dtype=torch.uint8, device=DEV)
+        ws = torch.zeros(ea.attn_fwd_split_workspace_size(B, H, N, False), dtype=torch.uint8, device=DEV)
     o = torch.empty((B, H, N, d), dtype=q.dtype, device=DEV) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
     lays = layouts or (None, None, None, None)
@@ -137,7 +138,8 @@ def test_forward_uses_the_split_path_and_its_workspace():
     torch.cuda.synchronize()
     o_s, l_s, _ = run_split(q, k, v)
     assert torch.equal(o_f, o_s) and torch.equal(l_f, l_s)
-    ws = ea.split_workspace(q.device, torch.cuda.current_stream().cuda_stream)
+    ws = ea.split_workspace(q.device, torch.cuda.current_stream().cuda_stream,
+                            ea.attn_fwd_split_workspace_size(B, H, N, False))
     assert int(ws[:count_bytes()].count_nonzero()) == 0
 
 
@@ -242,7 +244,9 @@ def test_split_workspace_validation():
     q, k, v = (t.to(DEV) for t in inputs(B, H, N, seed=4800))
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
-    need = ea.attn_fwd_split_workspace_size()
+    need = ea.attn_fwd_split_workspace_size(B, H, N, False)
+    assert ea.attn_fwd_split_workspace_size(B, H, N, True) == 0      # causal: never split
+    assert ea.attn_fwd_split_workspace_size(1, 16, 11616, False) == 0  # a 7/8-full last round: not split
     c = cus() // 8
     # the counters (8*C ints, padded to 256 bytes), then 2 slots of 69,632 bytes per range
     assert need == (8 * c * 4 + 255) // 256 * 256 + 16 * c * 69632
@@ -259,3 +263,23 @@ def test_split_workspace_validation():
     assert call(ws.data_ptr(), need) == ea.ATTN_OK
     torch.cuda.synchronize()
     assert int(ws[:count_bytes()].count_nonzero()) == 0
+
+
+def test_unsplit_calls_take_no_workspace():
+    """A call attn_fwd_split does not split runs with a NULL workspace and
+    gives attn_fwd's bits; forward() then makes no workspace."""
+    B, H, N = 1, 16, 2000
+    assert not splits(B, H, N) and ea.attn_fwd_split_workspace_size(B, H, N, False) == 0
+    q, k, v = (t.to(DEV) for t in inputs(B, H, N, seed=4900))
+    o, lse = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        assert ea.load_library().attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                lse.data_ptr(), B, H, N, 64, 0.125, 0, None, None, None, None,
+                                                None, None, None, 0, stream.cuda_stream) == ea.ATTN_OK
+        o_f, l_f = ea.forward(q, k, v, scale=0.125)
+    torch.cuda.synchronize()
+    o0, l0 = ea.forward(q, k, v, scale=0.125, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0) and torch.equal(lse, l0) and torch.equal(o_f, o0)
+    assert (DEV_INDEX, stream.cuda_stream) not in ea._SPLIT_WS
