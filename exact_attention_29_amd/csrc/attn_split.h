@@ -104,8 +104,8 @@ __host__ __device__ inline size_t split_workspace_bytes(int cus) {
 // applies (no XCD's leftover is a whole round, rem_x < C; some leftover;
 // every leftover tile has at least C key tiles, so each range is at least
 // one key tile long; C * C * n_kt < 2^31 for the device's 32-bit range
-// arithmetic; C <= 64, one range per lane when ranking).  `on`: valid and
-// worth it --
+// arithmetic; C <= 64, i.e. up to 512 CUs and a workspace of at most 72 MB).
+// `on`: valid and worth it --
 //   * the leftover fills at most half of a round (sum rem_x <= 4C).  The
 //     part is power-limited: with a few CUs idle the busy ones clock higher
 //     and make up most of the idle time, so a nearly full last round (3 MP
