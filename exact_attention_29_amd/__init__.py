@@ -9,9 +9,9 @@ arguments
 of the C entry points declared in include/attn.h and only marshal arguments;
 every step of the computation runs in the HIP kernels.
 ``forward`` is a convenience wrapper that allocates the outputs (and the
-split workspace, once per device and stream) with torch and launches on
-torch's current stream.  There is no CPU fallback: without
-the built library (or without a gfx950 device) every call raises.
+split workspace: once per device and stream, or per captured call) with
+torch and launches on torch's current stream.  There is no CPU fallback:
+without the built library (or without a gfx950 device) every call raises.
 """
 
 import ctypes
@@ -227,8 +227,8 @@ def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-# forward()'s split workspaces: one per (device index, stream handle), so
-# that calls on different streams never share one
+# forward()'s split workspaces for eager calls: one per (device index,
+# stream handle), so that calls on different streams never share one
 _SPLIT_WS = {}
 # the first bytes of a workspace hold the arrival counters (at most 64 ints
 # per XCD, 8 XCDs); attn_fwd_split needs them zero at the start of a call
@@ -239,18 +239,25 @@ def split_workspace(device, stream, n):
     """The workspace forward() hands attn_fwd_split on (device, stream): a
     uint8 tensor of n bytes (what attn_fwd_split_workspace_size reports for
     a split call; the same for every split call on a device) whose counters
-    start at zero; every completed call leaves them zero.  Made on first
-    use; under graph capture it comes from the graph's memory pool and only
-    its counter block is cleared, by a fill kernel captured with it."""
+    are zero when the call starts.
+
+    Eager calls share one per stream, made zeroed on first use; every
+    completed call leaves its counters zero again.  A call under graph
+    capture gets one of its own from the graph's memory pool, its counter
+    block cleared by a fill kernel captured just before the call, so every
+    replay starts from zero whatever ran before it, and a replay (on
+    whatever stream) shares no workspace with eager calls or other graphs.
+    It is released when forward() returns; the pool can hand the same
+    block to the capture's next split call on that stream, which runs after
+    this one in every replay."""
+    if torch.cuda.is_current_stream_capturing():
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        ws[:_SPLIT_COUNT_BYTES].zero_()
+        return ws
     key = (device.index, stream)
     ws = _SPLIT_WS.get(key)
     if ws is None or ws.numel() < n:
-        with torch.cuda.device(device):
-            if torch.cuda.is_current_stream_capturing():
-                ws = torch.empty(n, dtype=torch.uint8, device=device)
-                ws[:_SPLIT_COUNT_BYTES].zero_()
-            else:
-                ws = torch.zeros(n, dtype=torch.uint8, device=device)
+        ws = torch.zeros(n, dtype=torch.uint8, device=device)
         _SPLIT_WS[key] = ws
     return ws
 
@@ -285,9 +292,7 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, key_len=None,
     Non-causal bf16 calls without a block mask that attn_fwd_split would
     split (a mostly empty last round of workgroups; unless ``split=False``)
     go through it, with the workspace split_workspace() keeps for the device
-    and stream.  (A graph captured with it uses the
-    capture stream's workspace: do not replay it while other forward calls
-    run on that stream.)
+    and stream (under graph capture, one of the graph's own).
     Launches on torch's current stream and returns without synchronising.
     """
     if q.dtype != k.dtype or q.dtype != v.dtype:

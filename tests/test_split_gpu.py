@@ -224,7 +224,7 @@ def test_split_replays_in_a_graph():
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph):
-            for _ in range(3):  # several calls per replay share the capture's workspace
+            for _ in range(3):  # several split calls per replay, each clearing its counters
                 ea.forward(q, k, v, scale=0.125, out=o, lse=lse)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
@@ -237,6 +237,55 @@ def test_split_replays_in_a_graph():
         torch.cuda.synchronize()
         assert torch.isfinite(filler)
         assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {replay} differs"
+
+
+def test_split_graphs_and_eager_calls_keep_their_own_workspaces():
+    """Two graphs captured back to back on one stream, an eager call on that
+    stream before any replay, then the graphs replayed in the other order
+    and at once on two streams: each captured call has a workspace of its
+    own (cleared by its own captured fill), so none of these shares arrival
+    counters or partial slots with another, and every result has the eager
+    bits."""
+    B, H, N = SHAPES[2]
+    q, k, v = (t.to(DEV) for t in inputs(B, H, N, seed=4750))
+    o_ref, l_ref = ea.forward(q, k, v, scale=0.125)
+    torch.cuda.synchronize()
+    outs = [(torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=DEV)) for _ in range(2)]
+    graphs = [torch.cuda.CUDAGraph() for _ in range(2)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for g, (o, lse) in zip(graphs, outs):
+            with torch.cuda.graph(g, stream=side):
+                ea.forward(q, k, v, scale=0.125, out=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert (DEV_INDEX, side.cuda_stream) not in ea._SPLIT_WS  # captures keep no eager workspace
+    with torch.cuda.stream(side):
+        o_e, l_e = ea.forward(q, k, v, scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o_e, o_ref) and torch.equal(l_e, l_ref), "eager call after the captures"
+    for o, lse in outs:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    torch.cuda.synchronize()
+    graphs[1].replay()
+    torch.cuda.synchronize()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    for i, (o, lse) in enumerate(outs):
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"graph {i}, replayed in reverse order"
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    for g, st in zip(graphs, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            g.replay()
+    torch.cuda.synchronize()
+    for i, (o, lse) in enumerate(outs):
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"graph {i}, replayed beside the other"
 
 
 def test_split_workspace_validation():
