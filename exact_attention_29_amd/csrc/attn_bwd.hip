@@ -926,7 +926,7 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
   void* pargs[] = {&a, &rows};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_kernel),
                                  dim3((unsigned)((rows + 255) / 256)), dim3(256), pargs, 0, s);
-  if (e != hipSuccess) return ATTN_E_LAUNCH;
+  if (e != hipSuccess) return launch_status(e);
 
   if (causal) {
     e = launch_main<kWavesCausal>(reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal>), a, B, H, N, s);
@@ -937,7 +937,7 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
     if (e == hipSuccess)
       e = launch_main<kWavesDq>(reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq>), a, B, H, N, s);
   }
-  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  return launch_status(e);
 }
 
 // The workspace of attn_bwd_noalloc: a static device array, one copy per

@@ -131,6 +131,15 @@ __attribute__((visibility("hidden"))) attn_status check_device(int* cus = nullpt
 
 inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
+// The status of a kernel launch.  A rejected launch's error is also taken
+// out of the runtime's last-error state: the caller has it as the return
+// value, and the next unrelated launch check must not report it again.
+inline attn_status launch_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  (void)hipGetLastError();
+  return ATTN_E_LAUNCH;
+}
+
 // Sizes every kernel handles: tile, row-block and workgroup counts are ints
 // (B*H*ceil(N/32) bounds them all), and one head's rows are addressed with
 // 32-bit byte offsets (N rows of 128 bytes).  Offsets between heads and

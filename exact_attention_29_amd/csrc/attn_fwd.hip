@@ -1425,7 +1425,7 @@ attn_status launch_bf16(const void* q, const void* k, const void* v, void* o, fl
                  : reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<false, kWavesFull, false, false, false>);
   const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(waves * 64), args, 0,
                                        static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  return launch_status(e);
 }
 
 attn_status launch_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -1454,7 +1454,7 @@ attn_status launch_fp32(const float* q, const float* k, const float* v, float* o
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_f32_kernel),
                                        dim3(B * H * a.q_tiles), dim3(64), args, 0,
                                        static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  return launch_status(e);
 }
 
 }  // namespace
@@ -1544,7 +1544,7 @@ extern "C" attn_status attn_pack_key_mask(const unsigned char* key_valid, unsign
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_pack_key_mask_kernel),
                                        dim3(blocks), dim3(256), args, 0,
                                        static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  return launch_status(e);
 }
 
 extern "C" const char* attn_strerror(attn_status s) {

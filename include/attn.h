@@ -46,7 +46,9 @@
  *     non-finite V value of a hidden key can still reach the rows that visit
  *     its block (0 * NaN); the fp32 paths skip hidden keys.
  *   - Errors are reported synchronously, before anything is enqueued; on an
- *     error the outputs are untouched.  A fault inside the kernel surfaces at
+ *     error the outputs are untouched (except ATTN_E_LAUNCH from a later
+ *     kernel of attn_bwd, whose earlier kernels are then enqueued and leave
+ *     dq, dk, dv undefined).  A fault inside the kernel surfaces at
  *     the caller's next synchronisation (HIP convention).  No C++ exception
  *     crosses this interface.
  */
@@ -72,7 +74,8 @@ typedef enum attn_status {
     ATTN_E_ALIGN = 2,
     /* No HIP device is current, or the current device is not gfx950. */
     ATTN_E_DEVICE = 3,
-    /* The kernel launch was rejected by the runtime. */
+    /* The kernel launch was rejected by the runtime (its error is also
+     * cleared from the runtime's last-error state). */
     ATTN_E_LAUNCH = 4,
     /* attn_bwd_noalloc only: the call needs more workspace than the
      * library's static scratch holds (ATTN_BWD_NOALLOC_SCRATCH_BYTES). */
