@@ -40,11 +40,15 @@
  *     fp32 (the fp32 entry points form scores in fp64).  Non-finite inputs
  *     are not scrubbed: a NaN in the K row of a key a query sees, or in that
  *     query, makes the query's O row and LSE NaN; a NaN in feature f of a
- *     seen key's V row makes feature f of O NaN.  A hidden key's score never
- *     enters the softmax.  The bf16 paths multiply whole 32-key blocks of V
- *     by their probabilities, a hidden key's being exactly 0, so a
- *     non-finite V value of a hidden key can still reach the rows that visit
- *     its block (0 * NaN); the fp32 paths skip hidden keys.
+ *     seen key's V row makes feature f of O NaN (an infinite one, +-inf).
+ *     A hidden key's score never enters the softmax.  The bf16 paths
+ *     multiply whole 32-key blocks of V by their probabilities, a hidden
+ *     key's being exactly 0, so a non-finite V value of a hidden key can
+ *     still reach the rows that visit its block, as NaN (0 * NaN, 0 * inf);
+ *     and when N is not a multiple of 32 the slots past N of the last block
+ *     hold copies of key N-1's V row, so a non-finite V value of key N-1
+ *     reaches every row that visits that block as NaN (an infinite value
+ *     then gives NaN, not +-inf).  The fp32 paths skip hidden keys.
  *   - Errors are reported synchronously, before anything is enqueued; on an
  *     error the outputs are untouched (except ATTN_E_LAUNCH from a later
  *     kernel of attn_bwd, whose earlier kernels are then enqueued and leave

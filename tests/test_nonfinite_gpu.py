@@ -5,14 +5,21 @@ a NaN in a K row makes the score of every query that sees that key NaN, so
 those rows are NaN in O and LSE, while rows that never see the key (causal
 rows before it) are untouched; a NaN in feature f of a V row makes column f
 of O NaN in every row that sees the key, and leaves the other features and
-LSE alone.  The NaN positions must match the oracle's, and every finite
-element must meet the usual bars.
+LSE alone.  An infinite K element gives a query +inf, -inf or NaN as
+score by the sign of its matching Q feature: +inf makes the row NaN (the
+max is +inf and exp(inf - inf) is NaN), -inf takes the key out; an infinite
+V value makes that column of O infinite in the rows that see the key.  The
+NaN and infinity positions must match the oracle's, and every finite element
+must meet the usual bars.
 
 One documented difference on the bf16 path: a wave multiplies a whole
 32-key block of V by its probabilities, and a hidden key's probability is
-an exact 0, so a NaN value of a hidden key reaches column f of the rows that
-share its block (causal rows 32*floor(j/32) .. j-1 here).  The fp32 path
-skips hidden keys and matches the oracle exactly.
+an exact 0, so a non-finite value of a hidden key reaches column f of the
+rows that share its block as NaN (0 * NaN, 0 * inf: causal rows
+32*floor(j/32) .. j-1 here).  The key slots past N of a ragged length hold
+copies of key N-1's V row, so a non-finite V[N-1] reaches every row that
+visits that last block likewise (an infinite value gives NaN there, not
++-inf).  The fp32 path skips hidden keys and matches the oracle exactly.
 """
 
 import numpy as np
@@ -111,6 +118,79 @@ def test_nan_query_row(dtype):
     assert np.array_equal(np.isnan(o), np.isnan(o_ref)) and np.isnan(o_ref[0, 0, 77]).all()
     assert np.array_equal(np.isnan(lse), np.isnan(lse_ref)) and np.isnan(lse[0, 0, 77])
     _finite_parts_agree(o, lse, o_ref, lse_ref, FP32 if dtype == "fp32" else BF16, "other rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("j", [5, 128, 298])
+def test_inf_key_element(j, causal, dtype):
+    """K[j, F] = +inf: a query with q[F] > 0 scores +inf against key j (the
+    definition's max is +inf and exp(inf - inf) is NaN: the row is NaN), one
+    with q[F] < 0 scores -inf (key j takes no part: a finite row), and one
+    with q[F] = 0 scores 0 * inf = NaN.  Key j sits in the first key tile,
+    on a tile edge and in the ragged last tile, so both the exact first
+    step and the steady state (with its exact-max fallback) meet it."""
+    w = Workload("inf_k", 1, 2, N, 64, dtype, 1.0, 0.125, causal, 1010 + j, "")
+    q, k, v = make_inputs(w)
+    k[:, 1, j, F] = float("inf")
+    mag = q[:, 1, :, F].abs() + 0.25
+    rows = torch.arange(N)
+    q[:, 1, :, F] = torch.where(rows % 3 == 0, torch.zeros_like(mag), torch.where(rows % 3 == 1, mag, -mag))
+    print(f"[case] +inf in K[{j}, {F}] of head 1, causal={causal}, {dtype}", flush=True)
+    o, lse = _run(q, k, v, causal, dtype)
+    with np.errstate(invalid="ignore"):
+        o_ref, lse_ref = oracle_attention(to_f64(q), to_f64(k), to_f64(v), 0.125, causal=causal)
+    first = j if causal else 0
+    sees = np.zeros(N, dtype=bool)
+    sees[first:] = True
+    r = np.arange(N)
+    assert np.isnan(lse_ref[0, 1, sees & (r % 3 != 2)]).all(), "oracle: +inf or NaN score rows"
+    assert np.isfinite(lse_ref[0, 1, ~sees | (r % 3 == 2)]).all(), "oracle: -inf score rows and rows before j"
+    assert np.array_equal(np.isnan(o), np.isnan(o_ref)), "NaN positions of O"
+    assert np.array_equal(np.isnan(lse), np.isnan(lse_ref)), "NaN positions of LSE"
+    _finite_parts_agree(o, lse, o_ref, lse_ref, FP32 if dtype == "fp32" else BF16, "finite rows")
+
+
+def _block_band(j, causal):
+    """bf16 path: the (row, column F) elements of O that a non-finite V[j, F]
+    may turn NaN beyond the definition -- rows that visit key j's 32-key
+    block without seeing key j (causal rows 32*floor(j/32) .. j-1), and, for
+    the last key of a ragged length, every row that visits that block: its
+    key slots past N hold copies of key N-1's V row with probability 0."""
+    band = np.zeros((1, 2, N, 64), dtype=bool)
+    b0 = 32 * (j // 32)
+    if causal:
+        band[0, 1, b0:j, F] = True
+    if j == N - 1 and N % 32:
+        band[0, 1, b0 if causal else 0:, F] = True
+    return band
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("j", [100, 298, 299])
+def test_inf_value(j, causal, dtype):
+    """V[j, F] = -inf: column F of O is -inf in every row that sees key j,
+    nothing else changes.  On the bf16 path the elements of the 32-key block
+    band may be NaN instead (0 * inf, as with a NaN value); key 299 is the
+    last key of the ragged length 300."""
+    w = Workload("inf_v", 1, 2, N, 64, dtype, 1.0, 0.125, causal, 1060 + j, "")
+    q, k, v = make_inputs(w)
+    v[:, 1, j, F] = float("-inf")
+    print(f"[case] -inf in V[{j}, {F}] of head 1, causal={causal}, {dtype}", flush=True)
+    o, lse = _run(q, k, v, causal, dtype)
+    with np.errstate(invalid="ignore"):
+        o_ref, lse_ref = oracle_attention(to_f64(q), to_f64(k), to_f64(v), 0.125, causal=causal)
+    first = j if causal else 0
+    assert np.isneginf(o_ref[0, 1, first:, F]).all() and np.isfinite(o_ref[0, 1, :first]).all()
+    assert not np.isnan(o_ref).any()
+    if dtype == "bf16":
+        band = _block_band(j, causal)
+        assert not np.isnan(np.where(band, 0.0, o)).any(), "NaN outside the band of key j's block"
+        o = np.where(band & np.isnan(o), o_ref, o)
+    assert np.array_equal(np.isneginf(o), np.isneginf(o_ref)), "-inf positions of O"
+    assert not np.isnan(o).any() and np.isfinite(lse).all()
+    _finite_parts_agree(o, lse, o_ref, lse_ref, FP32 if dtype == "fp32" else BF16, "finite elements")
 
 
 def test_padded_nan_key_fp32_takes_no_part():

@@ -12,9 +12,9 @@ shapes that exercise each case of the decomposition:
   * no whole round, long rows: every tile cut into several pieces;
   * a ragged last key tile (N not a multiple of 64) inside a piece;
 plus key-padding masks (pieces that see no key at all), strided head views,
-NaN inputs, determinism, the arrival counters left at zero, and replays of a
-captured graph.  The decomposition is deterministic (pieces merge in a fixed
-order), so repeated calls give the same bits.
+NaN and infinite inputs, determinism, the arrival counters left at zero,
+and replays of captured graphs.  The decomposition is deterministic (pieces
+merge in a fixed order), so repeated calls give the same bits.
 """
 
 import numpy as np
@@ -203,6 +203,37 @@ def test_split_nan_rows_follow_the_definition():
     assert np.array_equal(np.isnan(lse_h), np.isnan(lse_ref)), "NaN positions of LSE"
     ok = ~np.isnan(o_ref)
     assert np.isnan(o_ref[0, 0]).all() and np.isnan(o_ref[0, 1, :, 5]).all() and ok[0, 2:].all()
+    e = errors(np.where(ok, o_h, 0), np.where(np.isnan(lse_ref), 0, lse_h),
+               np.where(ok, o_ref, 0), np.where(np.isnan(lse_ref), 0, lse_ref))
+    assert_within(e, {kk: vv for kk, vv in BF16.items() if kk != "o_mean"}, "finite parts")
+
+
+def test_split_infinite_inputs_follow_the_definition():
+    """Head 2's last query tile is split (1 x 24 x 2816: one leftover tile
+    per XCD).  K[2000, 5] = +inf there: rows with q[5] > 0 score +inf (NaN
+    rows: some piece's reference max is +inf and the merge takes
+    2^(inf - inf)), rows with q[5] < 0 score -inf (the key takes no part),
+    rows with q[5] = 0 score NaN.  V[1234, 5] = -inf in head 5 (also split):
+    column 5 of O is -inf in every row."""
+    B, H, N, F = 1, 24, 2816, 5
+    assert splits(B, H, N)
+    q, k, v = inputs(B, H, N, seed=4650)
+    k[0, 2, 2000, F] = float("inf")
+    mag = q[0, 2, :, F].abs() + 0.25
+    r = torch.arange(N)
+    q[0, 2, :, F] = torch.where(r % 3 == 0, torch.zeros_like(mag), torch.where(r % 3 == 1, mag, -mag))
+    v[0, 5, 1234, F] = float("-inf")
+    o, lse, _ = run_split(*(t.to(DEV) for t in (q, k, v)))
+    with np.errstate(invalid="ignore"):
+        o_ref, lse_ref = oracle_attention(to_f64(q), to_f64(k), to_f64(v), 0.125)
+    o_h, lse_h = to_f64(o), to_f64(lse)
+    rr = np.arange(N)
+    assert np.isnan(lse_ref[0, 2, rr % 3 != 2]).all() and np.isfinite(lse_ref[0, 2, rr % 3 == 2]).all()
+    assert np.isneginf(o_ref[0, 5, :, F]).all()
+    assert np.array_equal(np.isnan(o_h), np.isnan(o_ref)), "NaN positions of O"
+    assert np.array_equal(np.isnan(lse_h), np.isnan(lse_ref)), "NaN positions of LSE"
+    assert np.array_equal(np.isneginf(o_h), np.isneginf(o_ref)), "-inf positions of O"
+    ok = np.isfinite(o_ref)
     e = errors(np.where(ok, o_h, 0), np.where(np.isnan(lse_ref), 0, lse_h),
                np.where(ok, o_ref, 0), np.where(np.isnan(lse_ref), 0, lse_ref))
     assert_within(e, {kk: vv for kk, vv in BF16.items() if kk != "o_mean"}, "finite parts")
