@@ -43,7 +43,15 @@
 //     recomputes its rows with the exact max on every tile (a rare path that
 //     reads K and V straight from global memory);
 //   * causal: key tiles past a wave's last query are skipped, only the
-//     diagonal and ragged half tiles pay for masking.
+//     diagonal and ragged half tiles pay for masking;
+//   * key masks (a valid length per batch entry, or a bit per key) hide keys
+//     by select, like the causal mask; block-sparse calls walk a list of the
+//     key tiles set for their 128-row query block instead of every tile;
+//   * split calls (attn_fwd_split): when the last round of workgroups would
+//     leave most CUs idle, its tiles' key ranges are cut into pieces spread
+//     over every CU; each workgroup runs its one or two pieces in a loop,
+//     hands each partial (unnormalised O^T, m, l) to a workspace slot, and
+//     the last piece of a tile to arrive merges them in piece order.
 // fp32 kernel: one thread per query row on the vector ALU (scores in fp64,
 // exp2 and sums in fp32), 8-key K/V tiles broadcast from LDS, hidden keys
 // skipped; same online softmax.  Used for fp32 I/O.
