@@ -264,15 +264,26 @@ def pin_backward_torch_autograd():
     rng = _rng(26)
     B, H, N, d = 2, 2, 33, 16
     q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    # a key-padding mask per batch entry (key 0 always valid, so no row of
+    # torch's SDPA is empty)
+    key_valid = rng.random((B, N)) < 0.7
+    key_valid[:, 0] = True
+    key_valid[1, N // 2:] = False
     for causal in (False, True):
-        tq, tk, tv = (torch.tensor(t, requires_grad=True) for t in (q, k, v))
-        mask = torch.ones(N, N, dtype=torch.bool).tril() if causal else None
-        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3)
-        out.backward(torch.tensor(do))
-        dq, dk, dv = attention_backward(q, k, v, do, 0.3, causal=causal)
-        _close(dq, tq.grad.numpy(), 1e-11, f"dQ vs torch autograd (causal={causal})")
-        _close(dk, tk.grad.numpy(), 1e-11, f"dK vs torch autograd (causal={causal})")
-        _close(dv, tv.grad.numpy(), 1e-11, f"dV vs torch autograd (causal={causal})")
+        for kv in (None, key_valid):
+            tq, tk, tv = (torch.tensor(t, requires_grad=True) for t in (q, k, v))
+            mask = torch.ones(1, 1, N, N, dtype=torch.bool)
+            if causal:
+                mask = mask & torch.ones(N, N, dtype=torch.bool).tril()
+            if kv is not None:
+                mask = mask & torch.tensor(kv)[:, None, None, :]
+            out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3)
+            out.backward(torch.tensor(do))
+            dq, dk, dv = attention_backward(q, k, v, do, 0.3, causal=causal, key_valid=kv)
+            what = f"causal={causal}, key mask={kv is not None}"
+            _close(dq, tq.grad.numpy(), 1e-11, f"dQ vs torch autograd ({what})")
+            _close(dk, tk.grad.numpy(), 1e-11, f"dK vs torch autograd ({what})")
+            _close(dv, tv.grad.numpy(), 1e-11, f"dV vs torch autograd ({what})")
 
 
 def pin_materialised_brute_force():
@@ -328,19 +339,26 @@ def pin_row_sampling():
 def pin_backward_row_sampling():
     """The sampled gradients (dQ at some query rows, dK and dV at some keys,
     from the forward oracle's O and LSE) are those rows of the full backward
-    oracle, for ragged, causal and single-key shapes."""
+    oracle, for ragged, causal and single-key shapes, and under key-padding
+    masks (hidden sampled keys, an entry with no valid key)."""
     from oracle.backward import attention_backward, attention_backward_sampled
     rng = _rng(13)
-    for n, causal in ((70, False), (70, True), (37, True), (1, False)):
-        q, k, v, do = rng.standard_normal((4, 1, 2, n, 8))
+    for n, causal, masked in ((70, False, False), (70, True, False), (37, True, False), (1, False, False),
+                              (70, False, True), (37, True, True)):
+        q, k, v, do = rng.standard_normal((4, 2, 2, n, 8))
         rows = np.array(sorted({0, n // 3, n - 1}))
         keys = np.array(sorted({0, n // 2, n - 1}))
-        dq, dk, dv = attention_backward(q, k, v, do, 0.4, causal=causal)
-        sq, sk, sv = attention_backward_sampled(q, k, v, do, 0.4, causal, rows, keys)
+        kv = None
+        if masked:
+            kv = np.ones((2, n), dtype=bool)
+            kv[0, n // 2:] = False
+            kv[1, :] = False
+        dq, dk, dv = attention_backward(q, k, v, do, 0.4, causal=causal, key_valid=kv)
+        sq, sk, sv = attention_backward_sampled(q, k, v, do, 0.4, causal, rows, keys, key_valid=kv)
         # absolute: with one key the gradients of Q and K cancel to zero
         for got, ref, what in ((sq, dq[:, :, rows], "dQ"), (sk, dk[:, :, keys], "dK"),
                                (sv, dv[:, :, keys], "dV")):
-            assert np.abs(got - ref).max() <= 1e-12, f"sampled {what} (n={n}, causal={causal})"
+            assert np.abs(got - ref).max() <= 1e-12, f"sampled {what} (n={n}, causal={causal}, masked={masked})"
 
 
 def _merge(o1, l1, o2, l2):
@@ -449,17 +467,22 @@ def pin_block_sparse():
 def pin_backward_finite_differences():
     """The gradients of L = sum(dO * O) against central finite differences of
     the forward oracle (step 1e-6, float64): every entry of dQ, dK and dV,
-    causal or not, on a tiny problem."""
+    causal or not, with and without a key-padding mask (one batch entry with
+    two hidden keys, one with every key hidden: its output is the constant
+    0, so all its gradients are 0), on a tiny problem."""
     from oracle.backward import attention_backward
     rng = _rng(24)
-    B, H, N, d = 1, 2, 6, 4
+    B, H, N, d = 2, 2, 6, 4
     q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
     scale, h = 0.7, 1e-6
-    for causal in (False, True):
-        dq, dk, dv = attention_backward(q, k, v, do, scale, causal=causal)
+    key_valid = np.ones((B, N), dtype=bool)
+    key_valid[0, [1, 4]] = False
+    key_valid[1, :] = False
+    for causal, kv in ((False, None), (True, None), (False, key_valid), (True, key_valid)):
+        dq, dk, dv = attention_backward(q, k, v, do, scale, causal=causal, key_valid=kv)
 
         def loss(qq, kk, vv):
-            return float((O.attention(qq, kk, vv, scale, causal=causal)[0] * do).sum())
+            return float((O.attention(qq, kk, vv, scale, causal=causal, key_valid=kv)[0] * do).sum())
 
         for name, x, g in (("dQ", q, dq), ("dK", k, dk), ("dV", v, dv)):
             num = np.zeros_like(x)
@@ -470,7 +493,7 @@ def pin_backward_finite_differences():
                 args_p = [xp if t is x else t for t in (q, k, v)]
                 args_m = [xm if t is x else t for t in (q, k, v)]
                 num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
-            _close(g, num, 1e-7, f"{name} vs finite differences (causal={causal})")
+            _close(g, num, 1e-7, f"{name} vs finite differences (causal={causal}, key mask={kv is not None})")
 
 
 def pin_backward_invariants():
@@ -495,6 +518,37 @@ def pin_backward_invariants():
     dq2, dk2, dv2 = attention_backward(q, k + u, v, do, 0.6)
     _close(dv2, dv, 1e-12, "dV under a shared key shift")
     _close(dk2, dk, 1e-12, "dK under a shared key shift")
+
+
+def pin_backward_hidden_keys():
+    """A key-padding mask in the gradients: the hidden keys' K and V can be
+    anything (every gradient stays the same bits), their own dK and dV are
+    exactly 0, a batch entry with no valid key gets all-zero gradients, and
+    the column sums of dV equal those of dO over the rows that see a key
+    (each such row of P sums to one)."""
+    from oracle.backward import attention_backward
+    rng = _rng(27)
+    B, H, N, d = 3, 2, 11, 5
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    key_valid = np.ones((B, N), dtype=bool)
+    key_valid[0, 7:] = False            # right padding
+    key_valid[1, [0, 3, 4, 9]] = False  # scattered
+    key_valid[2, :] = False             # nothing valid
+    for causal in (False, True):
+        dq, dk, dv = attention_backward(q, k, v, do, 0.45, causal=causal, key_valid=key_valid)
+        k2, v2 = k.copy(), v.copy()
+        hid = ~key_valid[:, None, :, None] & np.ones((B, H, N, d), dtype=bool)
+        k2[hid] = 40.0 * rng.standard_normal(int(hid.sum()))
+        v2[hid] = -7.0
+        dq2, dk2, dv2 = attention_backward(q, k2, v2, do, 0.45, causal=causal, key_valid=key_valid)
+        for name, a, b in (("dQ", dq, dq2), ("dK", dk, dk2), ("dV", dv, dv2)):
+            assert np.array_equal(a, b), f"{name} depends on hidden keys (causal={causal})"
+        assert not dk[hid].any() and not dv[hid].any(), f"hidden keys get a gradient (causal={causal})"
+        assert not dq[2].any() and not dk[2].any() and not dv[2].any(), "entry with no valid key"
+        sees = np.array([[(key_valid[b] & ((np.arange(N) <= i) if causal else True)).any() for i in range(N)]
+                         for b in range(B)])
+        want = (do * sees[:, None, :, None]).sum(axis=2)
+        _close(dv.sum(axis=2), want, 1e-12, f"column sums of dV under a key mask (causal={causal})")
 
 
 def pin_nonfinite_inputs():
@@ -550,6 +604,7 @@ INDEPENDENT_PINS = [
     pin_block_sparse,
     pin_backward_finite_differences,
     pin_backward_invariants,
+    pin_backward_hidden_keys,
     pin_nonfinite_inputs,
 ]
 

@@ -73,8 +73,30 @@ def test_independent_pins_catch_mutant(name, monkeypatch):
     assert caught, f"mutant {name} passed every independent pin"
 
 
+def _p_ignoring_key_mask(q, k, scale, causal, rows, key_valid=None):
+    """Probabilities that forget the key-padding mask."""
+    s = O._scores(q[rows], k, scale)
+    s = np.where(O._visible(rows, k.shape[0], causal, None), s, -np.inf)
+    e = np.exp(s - s.max(axis=1)[:, None])
+    return e / e.sum(axis=1)[:, None]
+
+
+def _p_empty_rows_uniform(q, k, scale, causal, rows, key_valid=None):
+    """Probabilities that spread a row with no visible key uniformly over
+    every key instead of leaving it at 0."""
+    s = O._scores(q[rows], k, scale)
+    vis = O._visible(rows, k.shape[0], causal, key_valid)
+    s = np.where(vis, s, -np.inf)
+    empty = ~vis.any(axis=1)
+    s[empty] = 0.0
+    e = np.exp(s - s.max(axis=1)[:, None])
+    return e / e.sum(axis=1)[:, None]
+
+
 # mistakes in the gradient steps (oracle.backward)
 BACKWARD_MUTANTS = {
+    "probabilities_ignore_key_mask": ("_probabilities", _p_ignoring_key_mask),
+    "probabilities_empty_rows_uniform": ("_probabilities", _p_empty_rows_uniform),
     "dv_not_transposed": ("_dv", lambda p, do: p @ do),
     "dp_uses_values_untransposed": ("_dp", lambda do, v: do @ v[::-1].T),
     "delta_sums_dp_only": ("_delta", lambda p, dp: dp.sum(axis=1)),
@@ -106,12 +128,15 @@ def test_independent_pins_catch_backward_mutant(name, monkeypatch):
 SAMPLED_MUTANTS = {
     "delta_from_output_dropped": ("_delta_from_output", lambda do, o: np.zeros(do.shape[0])),
     "delta_from_output_values": ("_delta_from_output", lambda do, o: do.sum(axis=1)),
-    "columns_without_lse": ("_probability_columns", lambda q, kc, lse, scale, causal, cols: (
+    "columns_without_lse": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None: (
         np.exp(scale * (q @ kc.T)))),
-    "columns_causal_reversed": ("_probability_columns", lambda q, kc, lse, scale, causal, cols: np.where(
+    "columns_causal_reversed": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None: np.where(
         (cols[None, :] >= np.arange(q.shape[0])[:, None]) if causal else True,
         np.exp(scale * (q @ kc.T) - lse[:, None]), 0.0)),
-    "columns_scale_dropped": ("_probability_columns", lambda q, kc, lse, scale, causal, cols: np.where(
+    "columns_ignore_key_mask": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None: (
+        np.where((cols[None, :] <= np.arange(q.shape[0])[:, None]) if causal else True,
+                 np.exp(scale * (q @ kc.T) - lse[:, None]), 0.0))),
+    "columns_scale_dropped": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None: np.where(
         (cols[None, :] <= np.arange(q.shape[0])[:, None]) if causal else True,
         np.exp(q @ kc.T - lse[:, None]), 0.0)),
 }
