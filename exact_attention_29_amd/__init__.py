@@ -3,7 +3,7 @@
 The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
 ``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_fwd_split``,
 ``attn_fwd_split_workspace_size``, ``attn_fwd_block_sparse``,
-``attn_bwd``, ``attn_bwd_noalloc``, ``attn_bwd_workspace_size``,
+``attn_bwd``, ``attn_bwd_masked``, ``attn_bwd_noalloc``, ``attn_bwd_workspace_size``,
 ``attn_pack_key_mask`` and ``attn_strerror`` carry the names and
 arguments
 of the C entry points declared in include/attn.h and only marshal arguments;
@@ -20,7 +20,7 @@ import os
 import torch  # imported first: the library then binds to torch's HIP runtime
 
 __all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-           "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_size",
+           "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_masked", "attn_bwd_noalloc", "attn_bwd_workspace_size",
            "attn_pack_key_mask", "AttnLayout",
            "backward", "attn_strerror", "forward", "pack_key_mask", "AttnError",
            "library_path", "load_library", "split_workspace"]
@@ -32,7 +32,7 @@ _lib = None
 ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH, ATTN_E_SCRATCH = range(6)
 # the static scratch of attn_bwd_noalloc (ATTN_BWD_NOALLOC_SCRATCH_BYTES in attn.h)
 BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
-EXPORTED = ("attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
+EXPORTED = ("attn_bwd", "attn_bwd_masked", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
             "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse",
             "attn_pack_key_mask", "attn_strerror")
 SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 128, 64
@@ -87,6 +87,8 @@ def load_library():
     lib.attn_fwd_block_sparse.restype = i32
     lib.attn_bwd.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_masked.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr, ptr]
+    lib.attn_bwd_masked.restype = i32
     lib.attn_bwd_noalloc.argtypes = [ptr] * 9 + [i32, i32, i32, i32, f32, i32, ptr]
     lib.attn_bwd_noalloc.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
@@ -168,6 +170,13 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, ca
                                    int(bool(causal)), stream))
 
 
+def attn_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, key_len, stream):
+    """C entry point attn_bwd_masked: attn_bwd plus the device address of
+    the int32 [B] valid key lengths (0 = none)."""
+    _check(load_library().attn_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, float(scale),
+                                          int(bool(causal)), key_len, stream))
+
+
 def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream):
     """C entry point attn_bwd_noalloc: attn_bwd without a workspace argument
     (the library's static device scratch; allocates nothing)."""
@@ -180,11 +189,13 @@ def attn_bwd_workspace_size(B, H, N):
     return int(load_library().attn_bwd_workspace_size(B, H, N))
 
 
-def backward(q, k, v, o, lse, dout, scale=None, causal=False):
+def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None):
     """dQ, dK, dV (bf16 [B, H, N, d]) of attention for upstream gradient dout,
-    from forward's o and lse (same q, k, v, scale, causal).  Contiguous bf16
-    tensors on one GPU; the workspace (attn_bwd_workspace_size bytes) is
-    allocated here.  Launches on torch's current stream."""
+    from forward's o and lse (same q, k, v, scale, causal and key_len).
+    key_len: optional int32 [B] valid key lengths (attn_bwd_masked: hidden
+    keys get dK = dV = 0).  Contiguous bf16 tensors on one GPU; the
+    workspace (attn_bwd_workspace_size bytes) is allocated here.  Launches
+    on torch's current stream."""
     ts = (q, k, v, o, dout)
     if any(t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous() or t.device != q.device
            for t in ts) or q.dim() != 4 or not q.is_cuda:
@@ -197,11 +208,17 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False):
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     if B * H * N == 0 and d == 64:
         return dq, dk, dv  # nothing to compute (the C entry points take B, H, N >= 1)
+    if key_len is not None and (key_len.dtype != torch.int32 or key_len.shape != (B,)
+                                or not key_len.is_contiguous() or key_len.device != q.device):
+        raise ValueError("key_len must be a contiguous int32 [B] tensor on q's device")
     ws = torch.empty(attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=q.device)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
     with torch.cuda.device(q.device):
-        attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, N, d, scale, causal,
-                 _stream_handle(q.device))
+        if key_len is None:
+            attn_bwd(*ptrs, B, H, N, d, scale, causal, _stream_handle(q.device))
+        else:
+            attn_bwd_masked(*ptrs, B, H, N, d, scale, causal, key_len.data_ptr(), _stream_handle(q.device))
     return dq, dk, dv
 
 

@@ -74,10 +74,18 @@ struct BwdArgs {
   int total;     // B * H * blocks
   float c;       // scale * log2(e)
   float scale;
+  const int* key_len;  // [B] or null: keys j >= key_len[b] are hidden (the forward's key mask)
+  int heads;           // H: batch entry of head bh is bh / H
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Keys of head bh that take part: key_len[b] clamped to [0, n], uniform in
+// the workgroup (loaded where needed rather than kept live across a loop).
+__device__ __forceinline__ int valid_keys(const BwdArgs& a, int bh) {
+  return __builtin_amdgcn_readfirstlane(min(max(a.key_len[bh / a.heads], 0), a.n));
+}
 
 // Per row of every head: L2 = LSE * log2(e) and -D = -sum_f dO_f O_f; rows
 // of the padding get L2 = +inf and -D = 0.
@@ -261,7 +269,10 @@ struct TileDma {
 
 // ------------------------------------------------------------------ dK, dV
 
-template <bool kCausal, int kWaves>
+// kKeyLen: keys at or past the batch entry's valid length are hidden from
+// every query; they get dK = dV = 0 (a workgroup whose keys are all hidden
+// only writes those zeros).
+template <bool kCausal, int kWaves, bool kKeyLen>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
   constexpr int kStages = kWaves == 8 ? 5 : 4;
@@ -291,6 +302,19 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int key0 = kb * kRows + wave_s * 32;  // this wave's first key
   const int key = key0 + l32;                 // this lane's key
+  if constexpr (kKeyLen) {
+    if (kb * kRows >= valid_keys(a, bh)) {  // uniform: before any barrier
+      if (key < n) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int f = 32 * hi; f < 32 * hi + 32; f += 8) {
+          *(u32x4*)(a.dk + head + (size_t)key * kD + f) = z;
+          *(u32x4*)(a.dv + head + (size_t)key * kD + f) = z;
+        }
+      }
+      return;
+    }
+  }
 
   // K^T and V^T operands (B operands of S = Q K^T and dP = dO V^T)
   bf16x8 kop[4], vop[4];
@@ -564,15 +588,20 @@ bwd_dkdv_kernel(BwdArgs a) {
     uint16_t* dkrow = a.dk + head + (size_t)key_e * kD;
     uint16_t* dvrow = a.dv + head + (size_t)key_e * kD;
     const float scale = a.scale;
+    bool hidden = false;  // kKeyLen: a key past the valid length (whatever its accumulators hold)
+    if constexpr (kKeyLen) hidden = key_e >= valid_keys(a, bh);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int f0 = 32 * db + 8 * r4 + 4 * hi_e;
-        const unsigned k01 = pack_bf16(acc_dk[db][4 * r4] * scale, acc_dk[db][4 * r4 + 1] * scale);
-        const unsigned k23 = pack_bf16(acc_dk[db][4 * r4 + 2] * scale, acc_dk[db][4 * r4 + 3] * scale);
-        const unsigned v01 = pack_bf16(acc_dv[db][4 * r4], acc_dv[db][4 * r4 + 1]);
-        const unsigned v23 = pack_bf16(acc_dv[db][4 * r4 + 2], acc_dv[db][4 * r4 + 3]);
+        unsigned k01 = pack_bf16(acc_dk[db][4 * r4] * scale, acc_dk[db][4 * r4 + 1] * scale);
+        unsigned k23 = pack_bf16(acc_dk[db][4 * r4 + 2] * scale, acc_dk[db][4 * r4 + 3] * scale);
+        unsigned v01 = pack_bf16(acc_dv[db][4 * r4], acc_dv[db][4 * r4 + 1]);
+        unsigned v23 = pack_bf16(acc_dv[db][4 * r4 + 2], acc_dv[db][4 * r4 + 3]);
+        if constexpr (kKeyLen) {
+          if (hidden) k01 = k23 = v01 = v23 = 0u;
+        }
         *(u32x2*)(dkrow + f0) = u32x2{k01, k23};
         *(u32x2*)(dvrow + f0) = u32x2{v01, v23};
       }
@@ -581,7 +610,10 @@ bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------- dQ
 
-template <bool kCausal, int kWaves>
+// kKeyLen: only the keys below the batch entry's valid length are visited
+// (the half holding the last one masked per element); an entry with no
+// valid key gets dQ = 0.
+template <bool kCausal, int kWaves, bool kKeyLen>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a) {
   constexpr int kStages = kWaves == 8 ? 6 : 5;
@@ -612,6 +644,19 @@ bwd_dq_kernel(BwdArgs a) {
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int q0w = qb * kRows + wave_s * 32;  // this wave's first query
   const int qi = q0w + l32;                  // this lane's query (< n_pad)
+  // keys that take part: all n, or (kKeyLen) the entry's valid length
+  int n_k = n;
+  if constexpr (kKeyLen) {
+    n_k = valid_keys(a, bh);
+    if (n_k == 0) {  // uniform: before any barrier
+      if (qi < n) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int f = 32 * hi; f < 32 * hi + 32; f += 8) *(u32x4*)(a.dq + head + (size_t)qi * kD + f) = z;
+      }
+      return;
+    }
+  }
 
   // Q^T and dO^T operands (B operands of S^T = K Q^T and dP^T = V dO^T)
   bf16x8 qop[4], dop[4];
@@ -633,11 +678,12 @@ bwd_dq_kernel(BwdArgs a) {
 
   // 32-key halves this wave works on: [0, jl].  Causal: up to the half that
   // starts at the wave's first query (the diagonal).  The last half is
-  // masked per element when it is the diagonal or holds keys past N.
+  // masked per element when it is the diagonal or holds keys past N (past
+  // the valid length with kKeyLen).
   // (A wave whose queries all lie past N runs like the others: its L2 is
   // +inf, so its probabilities are 0, and nothing of it is written.)
   const int q_last = min(n - 1, qb * kRows + kRows - 1);
-  const int kv_end = kCausal ? q_last + 1 : n;
+  const int kv_end = kCausal ? (kKeyLen ? min(q_last + 1, n_k) : q_last + 1) : n_k;
   const int t_end = (kv_end + kBwdTile - 1) / kBwdTile;
   const int jl = kCausal ? min(q0w / 32, 2 * t_end - 1) : 2 * t_end - 1;
   // Tile 0 runs on the general path; then tiles whose two steps are fast in
@@ -711,15 +757,15 @@ bwd_dq_kernel(BwdArgs a) {
     if (j >= 0 && j <= jl) {
       const int k0 = 32 * j;
       const bool diag = kCausal && k0 == q0w;
-      const bool ragged = k0 + 32 > n;
+      const bool ragged = k0 + 32 > n_k;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], c, -lse2));
         float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r + 1], c, -lse2));
         if (diag || ragged) {
           const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);  // key - k0
-          if ((diag && kr > l32) || k0 + kr >= n) p0 = 0.f;
-          if ((diag && kr + 1 > l32) || k0 + kr + 1 >= n) p1 = 0.f;
+          if ((diag && kr > l32) || k0 + kr >= n_k) p0 = 0.f;
+          if ((diag && kr + 1 > l32) || k0 + kr + 1 >= n_k) p1 = 0.f;
         }
         set_word(ds_cur[r >> 3], (r & 7) >> 1, pack_bf16(p0 * dp_cur[r], p1 * dp_cur[r + 1]));
       }
@@ -900,7 +946,7 @@ attn_status bwd_validate(const void* q, const void* k, const void* v, const void
 
 attn_status bwd_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N,
-                       float scale, int causal, void* stream) {
+                       float scale, int causal, const int* key_len, void* stream) {
   BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -915,6 +961,8 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
   a.n = N;
   a.n_pad = (N + kPadRows - 1) / kPadRows * kPadRows;
   a.bh_count = B * H;
+  a.heads = H;
+  a.key_len = key_len;
   a.blocks = a.total = 0;
   a.c = scale * kLog2e;
   a.scale = scale;
@@ -928,14 +976,22 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
                                  dim3((unsigned)((rows + 255) / 256)), dim3(256), pargs, 0, s);
   if (e != hipSuccess) return launch_status(e);
 
+  const void* k_dkdv;
+  const void* k_dq;
   if (causal) {
-    e = launch_main<kWavesCausal>(reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal>), a, B, H, N, s);
-    if (e == hipSuccess)
-      e = launch_main<kWavesCausal>(reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal>), a, B, H, N, s);
+    k_dkdv = key_len ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal, true>)
+                     : reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal, false>);
+    k_dq = key_len ? reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, true>)
+                   : reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, false>);
+    e = launch_main<kWavesCausal>(k_dkdv, a, B, H, N, s);
+    if (e == hipSuccess) e = launch_main<kWavesCausal>(k_dq, a, B, H, N, s);
   } else {
-    e = launch_main<kWavesDkdv>(reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv>), a, B, H, N, s);
-    if (e == hipSuccess)
-      e = launch_main<kWavesDq>(reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq>), a, B, H, N, s);
+    k_dkdv = key_len ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, true>)
+                     : reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, false>);
+    k_dq = key_len ? reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, true>)
+                   : reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, false>);
+    e = launch_main<kWavesDkdv>(k_dkdv, a, B, H, N, s);
+    if (e == hipSuccess) e = launch_main<kWavesDq>(k_dq, a, B, H, N, s);
   }
   return launch_status(e);
 }
@@ -981,7 +1037,21 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
   st = check_device();
   if (st != ATTN_OK) return st;
   return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
-                    stream);
+                    nullptr, stream);
+}
+
+extern "C" attn_status attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                       const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
+                                       int H, int N, int d, float scale, int causal, const int* key_len,
+                                       void* stream) {
+  if (!workspace) return ATTN_E_INVALID;
+  attn_status st = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (misaligned(workspace, 16) || misaligned(key_len, 4)) return ATTN_E_ALIGN;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
+                    key_len, stream);
 }
 
 extern "C" attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
@@ -995,5 +1065,5 @@ extern "C" attn_status attn_bwd_noalloc(const void* q, const void* k, const void
   float* ws = nullptr;
   st = scratch_address(&ws);
   if (st != ATTN_OK) return st;
-  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, scale, causal, stream);
+  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, scale, causal, nullptr, stream);
 }

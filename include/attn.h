@@ -314,6 +314,30 @@ attn_status attn_bwd(const void *q, const void *k, const void *v,
                      void *stream);
 
 /*
+ * attn_bwd_masked: attn_bwd for a forward that hid keys by valid length
+ * (attn_fwd_masked with key_len, key_bits NULL) -- the padded batches the
+ * Qiita page's layer passes a key_padding_mask for, in training.  Keys
+ * j >= key_len[b] of batch entry b take no part in any query's softmax, so
+ * by the same recomputation (FlashAttention reading notes, section
+ * "recomputation") their probabilities are 0 in every row:
+ *   - dK and dV of a hidden key are exactly 0, and it adds nothing to dQ;
+ *   - an entry with key_len 0 has the constant output O = 0 (empty rows):
+ *     every dQ, dK, dV of that entry is 0.
+ *   key_len : const int [B] device array, 4-byte aligned, or NULL (then
+ *             exactly attn_bwd); values are clamped to [0, N].  O and LSE
+ *             must come from the forward with the same key_len.
+ * Other arguments, layout, ownership, workspace and errors as attn_bwd
+ * (ATTN_E_ALIGN also for a misaligned key_len).  A bit mask (key_bits) has
+ * no backward here.
+ */
+attn_status attn_bwd_masked(const void *q, const void *k, const void *v,
+                            const void *o, const float *lse,
+                            const void *dout, void *dq, void *dk, void *dv,
+                            void *workspace, int B, int H, int N, int d,
+                            float scale, int causal, const int *key_len,
+                            void *stream);
+
+/*
  * Bytes of workspace attn_bwd needs: 8 * B * H * ceil(N / 256) * 256 (two
  * fp32 values per padded row of every head); 0 when B, H or N is below 1.
  */

@@ -79,10 +79,10 @@ def assert_within(err, bar, what=""):
 GRAD = dict(rel_fro=1e-2, rel_max=2e-2)
 
 
-def grad_magnitudes(q, k, v, do, scale, causal):
+def grad_magnitudes(q, k, v, do, scale, causal, key_valid=None):
     """The gradients with every cancelling difference replaced by its
     magnitude: dS -> P * (|dP| + |D|), dO -> |dO| (float64, from the oracle's
-    own steps)."""
+    own steps; key_valid: optional bool [B, N] key mask)."""
     from oracle import backward as ob
     from workloads import to_f64
     q, k, v, do = (to_f64(t) for t in (q, k, v, do))
@@ -91,7 +91,8 @@ def grad_magnitudes(q, k, v, do, scale, causal):
     rows = np.arange(N)
     for b in range(B):
         for h in range(H):
-            p = ob._probabilities(q[b, h], k[b, h], scale, causal, rows)
+            p = ob._probabilities(q[b, h], k[b, h], scale, causal, rows,
+                                  None if key_valid is None else np.asarray(key_valid, dtype=bool)[b])
             dp = ob._dp(do[b, h], v[b, h])
             delta = ob._delta(p, dp)
             mds = p * (np.abs(dp) + np.abs(delta)[:, None])
@@ -113,7 +114,7 @@ def assert_grad_within(name, got, ref, mag):
     assert mx <= GRAD["rel_max"], f"{name}: max error {mx:.3e} of max|ref| > {GRAD['rel_max']}"
 
 
-def grad_magnitudes_sampled(q, k, v, do, scale, causal, rows, keys):
+def grad_magnitudes_sampled(q, k, v, do, scale, causal, rows, keys, key_valid=None):
     """grad_magnitudes at query rows `rows` (dQ) and keys `keys` (dK, dV),
     from rows and columns of P as in the oracle's sampled backward."""
     from oracle import attention
@@ -127,12 +128,15 @@ def grad_magnitudes_sampled(q, k, v, do, scale, causal, rows, keys):
     for b in range(B):
         for h in range(H):
             qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
-            o, lse = attention(qh[None, None], kh[None, None], vh[None, None], scale, causal=causal)
+            kvb = None if key_valid is None else np.asarray(key_valid, dtype=bool)[b]
+            o, lse = attention(qh[None, None], kh[None, None], vh[None, None], scale, causal=causal,
+                               key_valid=None if kvb is None else kvb[None])
             delta = np.abs(ob._delta_from_output(doh, o[0, 0]))
-            p_r = ob._probabilities(qh, kh, scale, causal, rows)
+            p_r = ob._probabilities(qh, kh, scale, causal, rows, kvb)
             mds_r = p_r * (np.abs(ob._dp(doh[rows], vh)) + delta[rows][:, None])
             mq[b, h] = abs(scale) * (mds_r @ np.abs(kh))
-            p_c = ob._probability_columns(qh, kh[keys], lse[0, 0], scale, causal, keys)
+            p_c = ob._probability_columns(qh, kh[keys], lse[0, 0], scale, causal, keys,
+                                          None if kvb is None else kvb[keys])
             mds_c = p_c * (np.abs(ob._dp(doh, vh[keys])) + delta[:, None])
             mk[b, h] = abs(scale) * (mds_c.T @ np.abs(qh))
             mv[b, h] = p_c.T @ np.abs(doh)
