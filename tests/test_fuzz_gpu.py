@@ -2,7 +2,8 @@
 GPU against the fp64 oracle: shapes (lengths near and between tile
 boundaries), causal or not, both key-mask forms (with entries that hide every
 key), packed strided views, fp32 I/O, negative and unusual scales, random
-block-sparse masks, and the backward.  Each
+block-sparse masks, and the backward (with and without valid key
+lengths).  Each
 feature has its own tests; these check that they combine.  The cases are
 drawn once from a fixed seed, so every run sees the same list.  Inputs are
 standard normal and scales reach 1 (eight times the workloads'), so rows
@@ -127,6 +128,45 @@ def test_random_backward(case):
     mags = grad_magnitudes(q, k, v, do, case["scale"], case["causal"])
     for name, g, r, m in zip(("dQ", "dK", "dV"), grads, ref, mags):
         assert_grad_within(f"{name} case {case['i']}", g, r, m)
+
+
+def _masked_backward_cases(count=12, seed=4049):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        B, N = int(rng.integers(1, 4)), _length(rng) // 2 + 1
+        lens = rng.integers(0, N + 1, size=B)
+        if B > 1 and rng.random() < 0.3:
+            lens[0] = 0  # an entry that hides every key
+        cases.append(dict(i=i, B=B, H=int(rng.integers(1, 4)), N=N, causal=bool(rng.random() < 0.5),
+                          scale=float(0.125 if rng.random() < 0.6 else rng.uniform(-0.4, 0.6)),
+                          lens=[int(x) for x in lens], seed=int(rng.integers(0, 2**31))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _masked_backward_cases(), ids=lambda c: "m%02d_N%d%s_B%dH%d" % (
+    c["i"], c["N"], "_causal" if c["causal"] else "", c["B"], c["H"]))
+def test_random_masked_backward(case):
+    """The backward after a forward with valid key lengths (attn_bwd_masked)."""
+    B, H, N = case["B"], case["H"], case["N"]
+    print(f"[fuzz] {case}", flush=True)
+    w = Workload("fuzz_mbwd", B, H, N, 64, "bf16", 1.0, case["scale"], case["causal"], case["seed"], "")
+    q, k, v = make_inputs(w)
+    do = make_inputs(Workload("fuzz_mdo", B, H, N, 64, "bf16", 1.0, case["scale"], case["causal"],
+                              case["seed"] + 1, ""))[0]
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    kl = torch.tensor(case["lens"], dtype=torch.int32, device=DEV)
+    o, lse = ea.forward(qd, kd, vd, scale=case["scale"], causal=case["causal"], key_len=kl)
+    grads = ea.backward(qd, kd, vd, o, lse, dod, scale=case["scale"], causal=case["causal"], key_len=kl)
+    torch.cuda.synchronize()
+    valid = np.arange(N)[None, :] < np.asarray(case["lens"])[:, None]
+    ref = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), case["scale"], causal=case["causal"],
+                             key_valid=valid)
+    mags = grad_magnitudes(q, k, v, do, case["scale"], case["causal"], key_valid=valid)
+    for name, g, r, m in zip(("dQ", "dK", "dV"), grads, ref, mags):
+        assert_grad_within(f"{name} case {case['i']}", g, r, m)
+    hidden = torch.tensor(~valid, device=DEV)[:, None, :, None]
+    assert not (grads[1].float() * hidden).any() and not (grads[2].float() * hidden).any(), "hidden keys"
 
 
 def _sparse_cases(count=12, seed=6072):
