@@ -22,12 +22,16 @@ def _inputs(N, seed, causal):
     return q, k, v, do
 
 
+@pytest.mark.parametrize("masked", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_and_backward_replay_in_a_graph(causal):
+def test_forward_and_backward_replay_in_a_graph(causal, masked):
+    """masked: both passes with valid key lengths (attn_fwd_masked's key_len,
+    attn_bwd_masked), one entry cut inside a tile."""
     q, k, v, do = _inputs(777, 9500 + causal, causal)
+    kl = torch.tensor([777, 300], dtype=torch.int32, device=DEV) if masked else None
     # eager results (also warms the library's per-device state up before capture)
-    o_ref, lse_ref = ea.forward(q, k, v, scale=0.125, causal=causal)
-    g_ref = ea.backward(q, k, v, o_ref, lse_ref, do, scale=0.125, causal=causal)
+    o_ref, lse_ref = ea.forward(q, k, v, scale=0.125, causal=causal, key_len=kl)
+    g_ref = ea.backward(q, k, v, o_ref, lse_ref, do, scale=0.125, causal=causal, key_len=kl)
     torch.cuda.synchronize()
 
     o = torch.empty_like(q)
@@ -37,8 +41,8 @@ def test_forward_and_backward_replay_in_a_graph(causal):
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph):
-            ea.forward(q, k, v, scale=0.125, causal=causal, out=o, lse=lse)
-            grads = ea.backward(q, k, v, o, lse, do, scale=0.125, causal=causal)
+            ea.forward(q, k, v, scale=0.125, causal=causal, out=o, lse=lse, key_len=kl)
+            grads = ea.backward(q, k, v, o, lse, do, scale=0.125, causal=causal, key_len=kl)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
