@@ -553,7 +553,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
 
 
 def bench_backward(w, steps, warmup, key_len=None):
-    """attn_bwd (three kernels: D, dK/dV, dQ) on the workload, inputs and
+    """attn_bwd (two kernels: dQ with the per-row terms, then dK/dV) on the workload, inputs and
     the forward's O, LSE resident.  FLOPs: the algorithmic 10*B*H*N^2*d of
     the recomputing backward pass (recompute S, then dV, dP, dQ, dK: five
     N x N x d products), halved when causal; this implementation recomputes S
@@ -607,7 +607,7 @@ def bench_backward(w, steps, warmup, key_len=None):
         "timing": {"ms_mean": round(kern * 1e3, 4), "ms_median": round(median(per) * 1e3, 4),
                    "ms_min": round(min(per) * 1e3, 4),
                    "method": TIMER["method"],
-                   "note": "the three kernels of one call, between events on the launch stream"},
+                   "note": "the two kernels of one call, between events on the launch stream"},
         "workspace": {"bytes": int(ws.numel()),
                       "note": "caller-owned attn_bwd_workspace_size(B, H, N): LSE*log2(e) and -D per padded row"},
     }

@@ -10,21 +10,23 @@
 // statistics (here LSE), and P = exp(S - LSE) is rebuilt tile by tile from Q
 // and K, never stored.
 //
-// Three kernels on the caller's stream:
-//   1. bwd_prep: per row, L2 = LSE * log2(e) and -D = -sum_f dO_if O_if into
-//      the caller's workspace (rows padded to a multiple of 256 with
-//      L2 = +inf and -D = 0, so a padding row has probability exactly 0);
+// Two kernels on the caller's stream:
+//   1. bwd_dq (query-parallel): each wave keeps Q and dO of its 32 queries
+//      in registers, first forms each query's L2 = LSE * log2(e) and
+//      -D = -sum_f dO_if O_if (from its dO and the matching O features; a
+//      lane exchange completes the row) and leaves them in the caller's
+//      workspace (rows padded to a multiple of 256; rows past N get
+//      L2 = +inf and -D = 0, so a padding query has probability exactly 0),
+//      then streams 64-key tiles of K and V: S^T = K Q^T and dP^T = V dO^T
+//      (a lane per query), dS^T, then dQ^T += K^T dS^T;
 //   2. bwd_dkdv (key-parallel): each wave keeps K and V of its 32 keys in
 //      registers as MFMA operands; 64-query tiles of Q, dO, L2 and -D stream
 //      through an LDS ring filled by DMA.  S = Q K^T is computed in the layout
 //      where each lane holds one key and 16 queries: P and dS then feed
 //      dV^T += dO^T P and dK^T += Q^T dS directly as MFMA operands, and the
 //      transposed Q / dO operands come from the row-major tiles with
-//      ds_read_b64_tr_b16;
-//   3. bwd_dq (query-parallel): each wave keeps Q and dO of its 32 queries
-//      in registers and streams 64-key tiles of K and V: S^T = K Q^T and
-//      dP^T = V dO^T (a lane per query), dS^T, then dQ^T += K^T dS^T.
-// Both main kernels run a software pipeline over 32-row steps: step j
+//      ds_read_b64_tr_b16.
+// Both kernels run a software pipeline over 32-row steps: step j
 // issues the MFMAs of S and dP for step j+1 and of the accumulating products
 // of step j-1, one by one, each beside a slice of the vector work of step j
 // (exp2, dS, bf16 packing), and reads its MFMA operands from LDS four MFMAs
@@ -85,36 +87,6 @@ __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast
 // the workgroup (loaded where needed rather than kept live across a loop).
 __device__ __forceinline__ int valid_keys(const BwdArgs& a, int bh) {
   return __builtin_amdgcn_readfirstlane(min(max(a.key_len[bh / a.heads], 0), a.n));
-}
-
-// Per row of every head: L2 = LSE * log2(e) and -D = -sum_f dO_f O_f; rows
-// of the padding get L2 = +inf and -D = 0.
-__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a, long long rows) {
-  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const int bh = (int)(r / a.n_pad);
-  const int row = (int)(r - (long long)bh * a.n_pad);
-  float l2 = INFINITY, nd = 0.f;
-  if (row < a.n) {
-    const size_t g = (size_t)bh * a.n + row;
-    const u32x4* po = (const u32x4*)(a.o + g * kD);
-    const u32x4* pd = (const u32x4*)(a.dout + g * kD);
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 wo = po[i], wd = pd[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = __builtin_fmaf(bf16_lo(wo[e]), bf16_lo(wd[e]), acc);
-        acc = __builtin_fmaf(bf16_hi(wo[e]), bf16_hi(wd[e]), acc);
-      }
-    }
-    l2 = a.lse[g] * kLog2e;
-    nd = -acc;
-  }
-  float* const hs = a.ws + (size_t)bh * 2 * a.n_pad;  // this head's L2, then -D
-  hs[row] = l2;
-  hs[a.n_pad + row] = nd;
 }
 
 // 16-byte chunk `ch` of row `row` of a [n][64] bf16 matrix, zero past row n.
@@ -665,9 +637,36 @@ bwd_dq_kernel(BwdArgs a) {
     qop[ks] = row_operand(qg, qi, ks, hi, n);
     dop[ks] = row_operand(dog, qi, ks, hi, n);
   }
-  const float* const hs = a.ws + (size_t)bh * 2 * a.n_pad;  // this head's L2, then -D
-  const float lse2 = hs[qi];
-  const float ndl = hs[a.n_pad + qi];
+  // L2 = LSE * log2(e) and -D = -sum_f dO_f O_f of this lane's query, formed
+  // here from the 32 features of dO already in dop and the matching 32 of O
+  // (lane l ^ 32 holds the other half of the row), and left in the
+  // workspace for the dK/dV kernel, which runs after this one.  Queries past
+  // N get L2 = +inf and -D = 0: their probabilities there are exactly 0.
+  float* const hs = a.ws + (size_t)bh * 2 * a.n_pad;  // this head's L2, then -D
+  float lse2 = INFINITY, ndl = 0.f;
+  {
+    const uint16_t* og = a.o + head;
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 ow = load_chunk(og, qi, 2 * ks + hi, n);
+      const u32x4 dw = __builtin_bit_cast(u32x4, dop[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum = __builtin_fmaf(bf16_lo(ow[e]), bf16_lo(dw[e]), dsum);
+        dsum = __builtin_fmaf(bf16_hi(ow[e]), bf16_hi(dw[e]), dsum);
+      }
+    }
+    dsum = half_swap_sum(dsum);
+    if (qi < n) {
+      lse2 = a.lse[(size_t)bh * n + qi] * kLog2e;
+      ndl = -dsum;
+    }
+    if (hi == 0) {
+      hs[qi] = lse2;
+      hs[a.n_pad + qi] = ndl;
+    }
+  }
   f32x16 nd16;  // -D of this lane's query in every register: dP^T starts there
 #pragma unroll
   for (int r = 0; r < 16; ++r) nd16[r] = ndl;
@@ -968,14 +967,10 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
   a.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  // bwd_prep writes every entry of the workspace (padding rows included)
-  // before the main kernels read it: nothing has to start at zero
-  long long rows = (long long)B * H * a.n_pad;
-  void* pargs[] = {&a, &rows};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_kernel),
-                                 dim3((unsigned)((rows + 255) / 256)), dim3(256), pargs, 0, s);
-  if (e != hipSuccess) return launch_status(e);
-
+  // The dQ kernel runs first: it writes every workspace entry the dK/dV
+  // kernel reads (L2 and -D of each query row up to its row blocks' end,
+  // padding rows +inf and 0), so nothing has to start at zero.
+  hipError_t e;
   const void* k_dkdv;
   const void* k_dq;
   if (causal) {
@@ -983,15 +978,15 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
                      : reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal, false>);
     k_dq = key_len ? reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, true>)
                    : reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, false>);
-    e = launch_main<kWavesCausal>(k_dkdv, a, B, H, N, s);
-    if (e == hipSuccess) e = launch_main<kWavesCausal>(k_dq, a, B, H, N, s);
+    e = launch_main<kWavesCausal>(k_dq, a, B, H, N, s);
+    if (e == hipSuccess) e = launch_main<kWavesCausal>(k_dkdv, a, B, H, N, s);
   } else {
     k_dkdv = key_len ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, true>)
                      : reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, false>);
     k_dq = key_len ? reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, true>)
                    : reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, false>);
-    e = launch_main<kWavesDkdv>(k_dkdv, a, B, H, N, s);
-    if (e == hipSuccess) e = launch_main<kWavesDq>(k_dq, a, B, H, N, s);
+    e = launch_main<kWavesDq>(k_dq, a, B, H, N, s);
+    if (e == hipSuccess) e = launch_main<kWavesDkdv>(k_dkdv, a, B, H, N, s);
   }
   return launch_status(e);
 }

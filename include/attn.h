@@ -303,8 +303,9 @@ attn_status attn_pack_key_mask(const unsigned char *key_valid,
  *                      aligned; overwritten (it holds LSE * log2(e) and -D
  *                      per row, rows padded to a multiple of 256), so calls
  *                      that overlap in time need separate workspaces.
- * Three kernels are enqueued on `stream` (the per-row terms, then dK and dV,
- * then dQ); no atomics, so the result is deterministic.  Errors as attn_fwd
+ * Two kernels are enqueued on `stream` (dQ, which also leaves the per-row
+ * terms in the workspace, then dK and dV); no atomics, so the result is
+ * deterministic.  Errors as attn_fwd
  * (every bf16 pointer and workspace 16-byte aligned, lse 4-byte aligned).
  */
 attn_status attn_bwd(const void *q, const void *k, const void *v,

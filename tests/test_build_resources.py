@@ -37,7 +37,7 @@ def test_report_lists_every_kernel():
     fwd = [n for n in names if "attn_fwd_bf16_kernel" in n]
     # {non-causal 8 and 4 waves, non-causal split, causal} x {key mask or not}, 2 block-sparse
     assert len(fwd) == 10, fwd
-    for kind in ("attn_fwd_f32_kernel", "attn_pack_key_mask_kernel", "bwd_prep_kernel"):
+    for kind in ("attn_fwd_f32_kernel", "attn_pack_key_mask_kernel"):
         assert sum(kind in n for n in names) == 1, kind
     assert sum("bwd_dkdv_kernel" in n for n in names) == 4  # causal or not, with or without key lengths
     assert sum("bwd_dq_kernel" in n for n in names) == 4
