@@ -680,7 +680,7 @@ bwd_dq_kernel(BwdArgs a) {
   // masked per element when it is the diagonal or holds keys past N (past
   // the valid length with kKeyLen).
   // (A wave whose queries all lie past N runs like the others: its L2 is
-  // +inf, so its probabilities are 0, and nothing of it is written.)
+  // +inf, so its probabilities are 0, and no dQ row of it is written.)
   const int q_last = min(n - 1, qb * kRows + kRows - 1);
   const int kv_end = kCausal ? (kKeyLen ? min(q_last + 1, n_k) : q_last + 1) : n_k;
   const int t_end = (kv_end + kBwdTile - 1) / kBwdTile;
