@@ -552,15 +552,17 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     return line
 
 
-def bench_backward(w, steps, warmup, key_len=None):
+def bench_backward(w, steps, warmup, key_len=None, key_density=None):
     """attn_bwd (two kernels: dQ with the per-row terms, then dK/dV) on the workload, inputs and
     the forward's O, LSE resident.  FLOPs: the algorithmic 10*B*H*N^2*d of
     the recomputing backward pass (recompute S, then dV, dP, dQ, dK: five
     N x N x d products), halved when causal; this implementation recomputes S
     and dP in both the key-parallel and the query-parallel kernel (14*N^2*d
-    executed).  key_len: every entry keeps this many valid keys
-    (attn_bwd_masked, after the forward with the same lengths); FLOPs then
-    count the visible (query, key) pairs only: 10*d per pair."""
+    executed).  key_len: every entry keeps this many valid keys; key_density:
+    a random key bit mask (seed 1001) keeps about this fraction of each
+    entry's keys (attn_bwd_masked, after the forward with the same masks);
+    FLOPs then count the visible (query, key) pairs only: 10*d per pair."""
+    import numpy as np
     import torch
     import exact_attention_29_amd as ea
     from workloads import make_inputs, Workload
@@ -570,7 +572,13 @@ def bench_backward(w, steps, warmup, key_len=None):
     q, k, v = (t.to(dev) for t in make_inputs(w))
     do = make_inputs(Workload("do", B, H, N, d, "bf16", 1.0, w.scale, w.causal, w.seed + 50, ""))[0].to(dev)
     kl = None if key_len is None else torch.full((B,), key_len, dtype=torch.int32, device=dev)
-    o, lse = ea.forward(q, k, v, scale=w.scale, causal=w.causal, key_len=kl)
+    kvalid = None
+    if key_density is not None:
+        kvalid = np.random.default_rng(1001).random((B, N)) < key_density
+        if key_len is not None:
+            kvalid &= np.arange(N)[None, :] < key_len
+    kbits = None if kvalid is None else ea.pack_key_mask(torch.tensor(kvalid, device=dev))
+    o, lse = ea.forward(q, k, v, scale=w.scale, causal=w.causal, key_len=kl, key_bits=kbits)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = torch.empty(ea.attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -580,28 +588,35 @@ def bench_backward(w, steps, warmup, key_len=None):
     def step():
         # the current stream at call time (a capture stream while recording a graph)
         s = torch.cuda.current_stream(dev).cuda_stream
-        if kl is None:
+        if kl is None and kbits is None:
             ea.attn_bwd(*ptrs, B, H, N, d, w.scale, w.causal, s)
         else:
-            ea.attn_bwd_masked(*ptrs, B, H, N, d, w.scale, w.causal, kl.data_ptr(), s)
+            ea.attn_bwd_masked(*ptrs, B, H, N, d, w.scale, w.causal, 0 if kl is None else kl.data_ptr(),
+                               0 if kbits is None else kbits.data_ptr(), s)
 
     wall, kern, per = TIMER["fn"](step, steps, warmup, stream)
     warm_run = WARMUP_RUN["launches"]
-    if kl is None:
+    if kl is None and kvalid is None:
         flops = 10.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
         counted = "10*B*H*N^2*d (x0.5 causal)"
-    else:
+    elif kvalid is None:
         lk = max(0, min(key_len, N))
         pairs = sum(min(i + 1, lk) for i in range(N)) if w.causal else N * lk
         flops = 10.0 * B * H * pairs * d
         counted = f"10*d per visible (query, key) pair: {pairs} pairs per head (key_len {lk})"
+    else:
+        # visible pairs per entry: row i sees the valid keys j (j <= i when causal)
+        per_entry = [int(np.cumsum(kv).sum()) if w.causal else int(kv.sum()) * N for kv in kvalid]
+        pairs = sum(per_entry)
+        flops = 10.0 * H * pairs * d
+        counted = f"10*d per visible (query, key) pair: {pairs} pairs over the {B} entries (key density {key_density})"
     return {
         "metric": "attention backward (dQ, dK, dV) TFLOP/s",
         "value": round(flops / wall / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.what}", "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
-                   "scale": w.scale, "key_len": key_len, "flops_counted": counted},
+                   "scale": w.scale, "key_len": key_len, "key_density": key_density, "flops_counted": counted},
         "pct_of_bf16_peak": round(100.0 * flops / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
         "warmup_launches_run": warm_run,
         "timing": {"ms_mean": round(kern * 1e3, 4), "ms_median": round(median(per) * 1e3, 4),
@@ -680,6 +695,8 @@ def main():
                     help="time attn_bwd (dQ, dK, dV) instead of the forward pass")
     ap.add_argument("--key-len", type=int, default=None,
                     help="with --backward: every batch entry has this many valid keys (attn_bwd_masked)")
+    ap.add_argument("--key-density", type=float, default=None,
+                    help="with --backward: a random key bit mask keeping this fraction of keys (attn_bwd_masked)")
     ap.add_argument("--block-density", type=float, default=None,
                     help="time attn_fwd_block_sparse with this fraction of random blocks set")
     ap.add_argument("--layout", choices=["contiguous", "packed"], default="contiguous",
@@ -730,7 +747,7 @@ def main():
         if args.causal:
             from dataclasses import replace
             w = replace(w, causal=args.causal == "yes")
-        print(json.dumps(bench_backward(w, args.steps, args.warmup, args.key_len)), flush=True)
+        print(json.dumps(bench_backward(w, args.steps, args.warmup, args.key_len, args.key_density)), flush=True)
         return
 
     if args.workspace_sweep:

@@ -87,7 +87,7 @@ def load_library():
     lib.attn_fwd_block_sparse.restype = i32
     lib.attn_bwd.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr]
     lib.attn_bwd.restype = i32
-    lib.attn_bwd_masked.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr, ptr]
+    lib.attn_bwd_masked.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr, ptr, ptr]
     lib.attn_bwd_masked.restype = i32
     lib.attn_bwd_noalloc.argtypes = [ptr] * 9 + [i32, i32, i32, i32, f32, i32, ptr]
     lib.attn_bwd_noalloc.restype = i32
@@ -170,11 +170,13 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, ca
                                    int(bool(causal)), stream))
 
 
-def attn_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, key_len, stream):
-    """C entry point attn_bwd_masked: attn_bwd plus the device address of
-    the int32 [B] valid key lengths (0 = none)."""
+def attn_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, key_len, key_bits,
+                    stream):
+    """C entry point attn_bwd_masked: attn_bwd plus the device addresses of
+    the int32 [B] valid key lengths and the [B, ceil(N/32)] key bit words
+    (0 = none)."""
     _check(load_library().attn_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, float(scale),
-                                          int(bool(causal)), key_len, stream))
+                                          int(bool(causal)), key_len, key_bits, stream))
 
 
 def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream):
@@ -189,11 +191,12 @@ def attn_bwd_workspace_size(B, H, N):
     return int(load_library().attn_bwd_workspace_size(B, H, N))
 
 
-def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None):
+def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None, key_valid=None, key_bits=None):
     """dQ, dK, dV (bf16 [B, H, N, d]) of attention for upstream gradient dout,
-    from forward's o and lse (same q, k, v, scale, causal and key_len).
-    key_len: optional int32 [B] valid key lengths (attn_bwd_masked: hidden
-    keys get dK = dV = 0).  Contiguous bf16 tensors on one GPU; the
+    from forward's o and lse (same q, k, v, scale, causal and key masks).
+    Key masks as in forward (int32 [B] key_len, bool [B, N] key_valid packed
+    here, or int32 [B, ceil(N/32)] key_bits), through attn_bwd_masked:
+    hidden keys get dK = dV = 0.  Contiguous bf16 tensors on one GPU; the
     workspace (attn_bwd_workspace_size bytes) is allocated here.  Launches
     on torch's current stream."""
     ts = (q, k, v, o, dout)
@@ -211,14 +214,24 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None):
     if key_len is not None and (key_len.dtype != torch.int32 or key_len.shape != (B,)
                                 or not key_len.is_contiguous() or key_len.device != q.device):
         raise ValueError("key_len must be a contiguous int32 [B] tensor on q's device")
+    if key_valid is not None:
+        if key_bits is not None:
+            raise ValueError("give key_valid or key_bits, not both")
+        if key_valid.shape != (B, N) or key_valid.device != q.device:
+            raise ValueError("key_valid must be a [B, N] tensor on q's device")
+        key_bits = pack_key_mask(key_valid)
+    if key_bits is not None and (key_bits.dtype != torch.int32 or key_bits.shape != (B, (N + 31) // 32)
+                                 or not key_bits.is_contiguous() or key_bits.device != q.device):
+        raise ValueError("key_bits must be a contiguous int32 [B, ceil(N/32)] tensor on q's device")
     ws = torch.empty(attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
     with torch.cuda.device(q.device):
-        if key_len is None:
+        if key_len is None and key_bits is None:
             attn_bwd(*ptrs, B, H, N, d, scale, causal, _stream_handle(q.device))
         else:
-            attn_bwd_masked(*ptrs, B, H, N, d, scale, causal, key_len.data_ptr(), _stream_handle(q.device))
+            attn_bwd_masked(*ptrs, B, H, N, d, scale, causal, 0 if key_len is None else key_len.data_ptr(),
+                            0 if key_bits is None else key_bits.data_ptr(), _stream_handle(q.device))
     return dq, dk, dv
 
 

@@ -78,15 +78,30 @@ struct BwdArgs {
   float scale;
   const int* key_len;  // [B] or null: keys j >= key_len[b] are hidden (the forward's key mask)
   int heads;           // H: batch entry of head bh is bh / H
+  const uint32_t* key_bits;  // [B][words] or null: bit j%32 of word j/32 clear hides key j
+  int words;                 // ceil(n / 32)
 };
+
+// Which keys take part, as a kernel template argument: all of them, those
+// below each entry's valid length, or (kKeysBits) those whose bit is set
+// and, when lengths are given too, below the length.
+constexpr int kKeysAll = 0, kKeysLen = 1, kKeysBits = 2;
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Keys of head bh that take part: key_len[b] clamped to [0, n], uniform in
-// the workgroup (loaded where needed rather than kept live across a loop).
+// Keys of head bh that take part: key_len[b] clamped to [0, n] (n when a
+// bit-mask call has no lengths), uniform in the workgroup (loaded where
+// needed rather than kept live across a loop).
+template <int kKeys>
 __device__ __forceinline__ int valid_keys(const BwdArgs& a, int bh) {
+  if (kKeys == kKeysBits && !a.key_len) return a.n;
   return __builtin_amdgcn_readfirstlane(min(max(a.key_len[bh / a.heads], 0), a.n));
+}
+
+// Bit word w (keys 32w .. 32w+31) of head bh's batch entry.
+__device__ __forceinline__ uint32_t key_word(const BwdArgs& a, int bh, int w) {
+  return a.key_bits[(size_t)(bh / a.heads) * a.words + w];
 }
 
 // 16-byte chunk `ch` of row `row` of a [n][64] bf16 matrix, zero past row n.
@@ -241,10 +256,12 @@ struct TileDma {
 
 // ------------------------------------------------------------------ dK, dV
 
-// kKeyLen: keys at or past the batch entry's valid length are hidden from
-// every query; they get dK = dV = 0 (a workgroup whose keys are all hidden
-// only writes those zeros).
-template <bool kCausal, int kWaves, bool kKeyLen>
+// kKeys (kKeysAll, kKeysLen, kKeysBits): hidden keys (past the batch
+// entry's valid length, or with a clear bit) are hidden from every query;
+// they get dK = dV = 0 (each output column is one key, so zeroing it at the
+// end is exact whatever its accumulators hold).  A workgroup whose keys all
+// lie past the valid length only writes those zeros.
+template <bool kCausal, int kWaves, int kKeys>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
   constexpr int kStages = kWaves == 8 ? 5 : 4;
@@ -274,8 +291,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int key0 = kb * kRows + wave_s * 32;  // this wave's first key
   const int key = key0 + l32;                 // this lane's key
-  if constexpr (kKeyLen) {
-    if (kb * kRows >= valid_keys(a, bh)) {  // uniform: before any barrier
+  if constexpr (kKeys != kKeysAll) {
+    if (kb * kRows >= valid_keys<kKeys>(a, bh)) {  // uniform: before any barrier
       if (key < n) {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -560,8 +577,9 @@ bwd_dkdv_kernel(BwdArgs a) {
     uint16_t* dkrow = a.dk + head + (size_t)key_e * kD;
     uint16_t* dvrow = a.dv + head + (size_t)key_e * kD;
     const float scale = a.scale;
-    bool hidden = false;  // kKeyLen: a key past the valid length (whatever its accumulators hold)
-    if constexpr (kKeyLen) hidden = key_e >= valid_keys(a, bh);
+    bool hidden = false;  // a key past the valid length or with a clear bit
+    if constexpr (kKeys != kKeysAll) hidden = key_e >= valid_keys<kKeys>(a, bh);
+    if constexpr (kKeys == kKeysBits) hidden = hidden || !((key_word(a, bh, key_e >> 5) >> (key_e & 31)) & 1u);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -571,7 +589,7 @@ bwd_dkdv_kernel(BwdArgs a) {
         unsigned k23 = pack_bf16(acc_dk[db][4 * r4 + 2] * scale, acc_dk[db][4 * r4 + 3] * scale);
         unsigned v01 = pack_bf16(acc_dv[db][4 * r4], acc_dv[db][4 * r4 + 1]);
         unsigned v23 = pack_bf16(acc_dv[db][4 * r4 + 2], acc_dv[db][4 * r4 + 3]);
-        if constexpr (kKeyLen) {
+        if constexpr (kKeys != kKeysAll) {
           if (hidden) k01 = k23 = v01 = v23 = 0u;
         }
         *(u32x2*)(dkrow + f0) = u32x2{k01, k23};
@@ -582,10 +600,12 @@ bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------- dQ
 
-// kKeyLen: only the keys below the batch entry's valid length are visited
-// (the half holding the last one masked per element); an entry with no
-// valid key gets dQ = 0.
-template <bool kCausal, int kWaves, bool kKeyLen>
+// kKeys: with kKeysLen / kKeysBits only the keys below the batch entry's
+// valid length are visited (the half holding the last one masked per
+// element), and an entry with no valid key gets dQ = 0; with kKeysBits every
+// step runs on the general path, which also drops the keys whose bit is
+// clear (one mask word per 32-key half, a select per score).
+template <bool kCausal, int kWaves, int kKeys>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a) {
   constexpr int kStages = kWaves == 8 ? 6 : 5;
@@ -616,10 +636,10 @@ bwd_dq_kernel(BwdArgs a) {
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int q0w = qb * kRows + wave_s * 32;  // this wave's first query
   const int qi = q0w + l32;                  // this lane's query (< n_pad)
-  // keys that take part: all n, or (kKeyLen) the entry's valid length
+  // keys that take part: all n, or the entry's valid length
   int n_k = n;
-  if constexpr (kKeyLen) {
-    n_k = valid_keys(a, bh);
+  if constexpr (kKeys != kKeysAll) {
+    n_k = valid_keys<kKeys>(a, bh);
     if (n_k == 0) {  // uniform: before any barrier
       if (qi < n) {
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -678,11 +698,11 @@ bwd_dq_kernel(BwdArgs a) {
   // 32-key halves this wave works on: [0, jl].  Causal: up to the half that
   // starts at the wave's first query (the diagonal).  The last half is
   // masked per element when it is the diagonal or holds keys past N (past
-  // the valid length with kKeyLen).
+  // the valid length), and every half that holds a hidden key (kKeysBits).
   // (A wave whose queries all lie past N runs like the others: its L2 is
   // +inf, so its probabilities are 0, and no dQ row of it is written.)
   const int q_last = min(n - 1, qb * kRows + kRows - 1);
-  const int kv_end = kCausal ? (kKeyLen ? min(q_last + 1, n_k) : q_last + 1) : n_k;
+  const int kv_end = kCausal ? (kKeys != kKeysAll ? min(q_last + 1, n_k) : q_last + 1) : n_k;
   const int t_end = (kv_end + kBwdTile - 1) / kBwdTile;
   const int jl = kCausal ? min(q0w / 32, 2 * t_end - 1) : 2 * t_end - 1;
   // Tile 0 runs on the general path; then tiles whose two steps are fast in
@@ -690,10 +710,10 @@ bwd_dq_kernel(BwdArgs a) {
   // rest on the general path again.
   constexpr int kHead = 1;
   const int jl_min = kCausal ? min(qb * kWaves, 2 * t_end - 1) : 2 * t_end - 1;
-  const int t_fast_end = jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
+  const int t_fast_end = kKeys == kKeysBits ? 0 : jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
   const Dma dma(kg, vg, n, wave, lane, nullptr, 0);
 
-  auto fast = [&](int j) { return j >= 1 && j <= jl - 1; };
+  auto fast = [&](int j) { return kKeys != kKeysBits && j >= 1 && j <= jl - 1; };
   auto half_stage = [&](int j) { return stage((j / 2) % kStages); };
   auto k_row = [&](const char* sb, int h, int ks) { return lds_read_b128(sb, h * 32 * kRow + row_off[ks]); };
   auto v_row = [&](const char* sb, int h, int ks) {
@@ -757,6 +777,8 @@ bwd_dq_kernel(BwdArgs a) {
       const int k0 = 32 * j;
       const bool diag = kCausal && k0 == q0w;
       const bool ragged = k0 + 32 > n_k;
+      uint32_t kept = ~0u;  // kKeysBits: bit kr set = key k0 + kr takes part
+      if constexpr (kKeys == kKeysBits) kept = k0 < n ? key_word(a, bh, j) >> (4 * hi) : 0u;  // words: keys < n
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], c, -lse2));
@@ -765,6 +787,11 @@ bwd_dq_kernel(BwdArgs a) {
           const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);  // key - k0
           if ((diag && kr > l32) || k0 + kr >= n_k) p0 = 0.f;
           if ((diag && kr + 1 > l32) || k0 + kr + 1 >= n_k) p1 = 0.f;
+        }
+        if constexpr (kKeys == kKeysBits) {
+          const int kb0 = 8 * (r >> 2) + (r & 3);  // key - k0 - 4 * hi
+          if (!((kept >> kb0) & 1u)) p0 = 0.f;
+          if (!((kept >> (kb0 + 1)) & 1u)) p1 = 0.f;
         }
         set_word(ds_cur[r >> 3], (r & 7) >> 1, pack_bf16(p0 * dp_cur[r], p1 * dp_cur[r + 1]));
       }
@@ -945,7 +972,8 @@ attn_status bwd_validate(const void* q, const void* k, const void* v, const void
 
 attn_status bwd_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N,
-                       float scale, int causal, const int* key_len, void* stream) {
+                       float scale, int causal, const int* key_len, const uint32_t* key_bits,
+                       void* stream) {
   BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -962,6 +990,8 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
   a.bh_count = B * H;
   a.heads = H;
   a.key_len = key_len;
+  a.key_bits = key_bits;
+  a.words = (N + 31) / 32;
   a.blocks = a.total = 0;
   a.c = scale * kLog2e;
   a.scale = scale;
@@ -971,22 +1001,25 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
   // kernel reads (L2 and -D of each query row up to its row blocks' end,
   // padding rows +inf and 0), so nothing has to start at zero.
   hipError_t e;
-  const void* k_dkdv;
-  const void* k_dq;
+  const int keys = key_bits ? kKeysBits : key_len ? kKeysLen : kKeysAll;
   if (causal) {
-    k_dkdv = key_len ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal, true>)
-                     : reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal, false>);
-    k_dq = key_len ? reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, true>)
-                   : reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, false>);
-    e = launch_main<kWavesCausal>(k_dq, a, B, H, N, s);
-    if (e == hipSuccess) e = launch_main<kWavesCausal>(k_dkdv, a, B, H, N, s);
+    const void* const k_dq[3] = {reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, kKeysAll>),
+                                 reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, kKeysLen>),
+                                 reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, kKeysBits>)};
+    const void* const k_dkdv[3] = {reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal, kKeysAll>),
+                                   reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal, kKeysLen>),
+                                   reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, kWavesCausal, kKeysBits>)};
+    e = launch_main<kWavesCausal>(k_dq[keys], a, B, H, N, s);
+    if (e == hipSuccess) e = launch_main<kWavesCausal>(k_dkdv[keys], a, B, H, N, s);
   } else {
-    k_dkdv = key_len ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, true>)
-                     : reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, false>);
-    k_dq = key_len ? reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, true>)
-                   : reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, false>);
-    e = launch_main<kWavesDq>(k_dq, a, B, H, N, s);
-    if (e == hipSuccess) e = launch_main<kWavesDkdv>(k_dkdv, a, B, H, N, s);
+    const void* const k_dq[3] = {reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, kKeysAll>),
+                                 reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, kKeysLen>),
+                                 reinterpret_cast<const void*>(&bwd_dq_kernel<false, kWavesDq, kKeysBits>)};
+    const void* const k_dkdv[3] = {reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, kKeysAll>),
+                                   reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, kKeysLen>),
+                                   reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, kWavesDkdv, kKeysBits>)};
+    e = launch_main<kWavesDq>(k_dq[keys], a, B, H, N, s);
+    if (e == hipSuccess) e = launch_main<kWavesDkdv>(k_dkdv[keys], a, B, H, N, s);
   }
   return launch_status(e);
 }
@@ -1032,21 +1065,21 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
   st = check_device();
   if (st != ATTN_OK) return st;
   return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
-                    nullptr, stream);
+                    nullptr, nullptr, stream);
 }
 
 extern "C" attn_status attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                        const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
                                        int H, int N, int d, float scale, int causal, const int* key_len,
-                                       void* stream) {
+                                       const unsigned* key_bits, void* stream) {
   if (!workspace) return ATTN_E_INVALID;
   attn_status st = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale);
   if (st != ATTN_OK) return st;
-  if (misaligned(workspace, 16) || misaligned(key_len, 4)) return ATTN_E_ALIGN;
+  if (misaligned(workspace, 16) || misaligned(key_len, 4) || misaligned(key_bits, 4)) return ATTN_E_ALIGN;
   st = check_device();
   if (st != ATTN_OK) return st;
   return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
-                    key_len, stream);
+                    key_len, key_bits, stream);
 }
 
 extern "C" attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
@@ -1060,5 +1093,5 @@ extern "C" attn_status attn_bwd_noalloc(const void* q, const void* k, const void
   float* ws = nullptr;
   st = scratch_address(&ws);
   if (st != ATTN_OK) return st;
-  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, scale, causal, nullptr, stream);
+  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, scale, causal, nullptr, nullptr, stream);
 }

@@ -315,28 +315,32 @@ attn_status attn_bwd(const void *q, const void *k, const void *v,
                      void *stream);
 
 /*
- * attn_bwd_masked: attn_bwd for a forward that hid keys by valid length
- * (attn_fwd_masked with key_len, key_bits NULL) -- the padded batches the
- * Qiita page's layer passes a key_padding_mask for, in training.  Keys
- * j >= key_len[b] of batch entry b take no part in any query's softmax, so
- * by the same recomputation (FlashAttention reading notes, section
- * "recomputation") their probabilities are 0 in every row:
+ * attn_bwd_masked: attn_bwd for a forward that hid keys (attn_fwd_masked
+ * with the same key_len and key_bits) -- the padded batches the Qiita page's
+ * layer passes a key_padding_mask for, in training.  A hidden key takes no
+ * part in any query's softmax, so by the same recomputation (FlashAttention
+ * reading notes, section "recomputation") its probabilities are 0 in every
+ * row:
  *   - dK and dV of a hidden key are exactly 0, and it adds nothing to dQ;
- *   - an entry with key_len 0 has the constant output O = 0 (empty rows):
- *     every dQ, dK, dV of that entry is 0.
- *   key_len : const int [B] device array, 4-byte aligned, or NULL (then
- *             exactly attn_bwd); values are clamped to [0, N].  O and LSE
- *             must come from the forward with the same key_len.
- * Other arguments, layout, ownership, workspace and errors as attn_bwd
- * (ATTN_E_ALIGN also for a misaligned key_len).  A bit mask (key_bits) has
- * no backward here.
+ *   - a query that sees no key has the constant output O = 0 (LSE = -inf):
+ *     its dQ is 0 and it adds nothing to any dK or dV.
+ *   key_len  : const int [B] device array or NULL, as attn_fwd_masked (keys
+ *              j >= key_len[b] hidden; clamped to [0, N]);
+ *   key_bits : const unsigned [B][ceil(N/32)] device array or NULL, as
+ *              attn_fwd_masked (bit j%32 of word j/32 clear hides key j);
+ *              both NULL is exactly attn_bwd.
+ * O and LSE must come from the forward with the same masks.  With key_bits
+ * the dQ kernel runs without its pipelined fast path (a select per score
+ * on every step), so bit masks cost more than lengths.  Other arguments,
+ * layout, ownership, workspace and errors as attn_bwd (ATTN_E_ALIGN also
+ * for a key_len or key_bits not 4-byte aligned).
  */
 attn_status attn_bwd_masked(const void *q, const void *k, const void *v,
                             const void *o, const float *lse,
                             const void *dout, void *dq, void *dk, void *dv,
                             void *workspace, int B, int H, int N, int d,
                             float scale, int causal, const int *key_len,
-                            void *stream);
+                            const unsigned *key_bits, void *stream);
 
 /*
  * Bytes of workspace attn_bwd needs: 8 * B * H * ceil(N / 256) * 256 (two

@@ -135,24 +135,27 @@ def test_backward_validation():
 
 
 def test_backward_masked_validation():
-    """attn_bwd_masked: attn_bwd's checks plus a 4-byte aligned key_len
-    (NULL allowed: then it is attn_bwd), all before any device call."""
+    """attn_bwd_masked: attn_bwd's checks plus 4-byte aligned key_len and
+    key_bits (NULL allowed: both NULL is attn_bwd), all before any device
+    call."""
     lib = ea.load_library()
 
     def bwd(**kw):
         ptrs = [kw.get(n, ALIGNED) for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws")]
         return lib.attn_bwd_masked(*ptrs, kw.get("B", 1), 1, kw.get("N", 100), kw.get("d", 64), 0.125, 0,
-                                   kw.get("key_len", ALIGNED), None)
+                                   kw.get("key_len", ALIGNED), kw.get("key_bits", ALIGNED), None)
     assert bwd(ws=None) == ea.ATTN_E_INVALID
     assert bwd(dk=None) == ea.ATTN_E_INVALID
     assert bwd(d=32) == ea.ATTN_E_INVALID
     assert bwd(N=1 << 24) == ea.ATTN_E_INVALID
     assert bwd(key_len=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    assert bwd(key_bits=ALIGNED + 2) == ea.ATTN_E_ALIGN
     assert bwd(ws=ALIGNED + 4) == ea.ATTN_E_ALIGN
     import torch
     if not torch.cuda.is_available():
         assert bwd() == ea.ATTN_E_DEVICE
         assert bwd(key_len=None) == ea.ATTN_E_DEVICE
+        assert bwd(key_len=None, key_bits=None) == ea.ATTN_E_DEVICE
 
 
 def test_backward_noalloc_validation():

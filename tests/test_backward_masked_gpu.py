@@ -31,11 +31,17 @@ def inputs(B, H, N, seed, sigma=1.0):
     return q, k, v, do
 
 
-def grads_gpu(q, k, v, do, scale, causal, lengths):
+def grads_gpu(q, k, v, do, scale, causal, lengths, valid=None):
+    """Forward and backward with valid lengths, or (valid: bool [B, N]) a key
+    bit mask, and lengths too unless lengths is None."""
     q, k, v, do = (t.to(DEV) for t in (q, k, v, do))
-    kl = torch.tensor(lengths, dtype=torch.int32, device=DEV)
-    o, lse = ea.forward(q, k, v, scale=scale, causal=causal, key_len=kl)
-    dq, dk, dv = ea.backward(q, k, v, o, lse, do, scale=scale, causal=causal, key_len=kl)
+    masks = {}
+    if lengths is not None:
+        masks["key_len"] = torch.tensor(lengths, dtype=torch.int32, device=DEV)
+    if valid is not None:
+        masks["key_valid"] = torch.tensor(valid, device=DEV)
+    o, lse = ea.forward(q, k, v, scale=scale, causal=causal, **masks)
+    dq, dk, dv = ea.backward(q, k, v, o, lse, do, scale=scale, causal=causal, **masks)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -44,28 +50,30 @@ def key_valid(lengths, n):
     return np.arange(n)[None, :] < np.clip(np.asarray(lengths), 0, n)[:, None]
 
 
-def check_exact_zeros(dq, dk, dv, lengths, n, what):
+def check_exact_zeros(dq, dk, dv, valid, what):
     """Hidden keys' dK and dV, and every gradient of an entry with no valid
-    key, are exactly 0."""
-    kv = torch.tensor(key_valid(lengths, n), device=dk.device)
+    key, are exactly 0 (valid: bool [B, N])."""
+    kv = torch.tensor(valid, device=dk.device)
     hidden = ~kv[:, None, :, None]
     assert not (dk.float() * hidden).any() and not (dv.float() * hidden).any(), f"{what}: hidden keys' dK/dV"
-    for b, length in enumerate(lengths):
-        if length <= 0:
+    for b in range(valid.shape[0]):
+        if not valid[b].any():
             assert not dq[b].float().any() and not dk[b].float().any() and not dv[b].float().any(), \
                 f"{what}: entry {b} has no valid key"
 
 
-def compare_full(q, k, v, do, causal, lengths, what):
+def compare_full(q, k, v, do, causal, lengths, what, valid=None):
     n = q.shape[2]
     print(f"[case] {what}", flush=True)
-    dq, dk, dv = grads_gpu(q, k, v, do, 0.125, causal, lengths)
-    kv = key_valid(lengths, n)
+    dq, dk, dv = grads_gpu(q, k, v, do, 0.125, causal, lengths, valid)
+    kv = np.ones((q.shape[0], n), dtype=bool) if lengths is None else key_valid(lengths, n)
+    if valid is not None:
+        kv = kv & valid
     ref = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), 0.125, causal=causal, key_valid=kv)
     mags = grad_magnitudes(q, k, v, do, 0.125, causal, key_valid=kv)
     for name, g, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref, mags):
         assert_grad_within(f"{name} {what}", g, r, m)
-    check_exact_zeros(dq, dk, dv, lengths, n, what)
+    check_exact_zeros(dq, dk, dv, kv, what)
 
 
 @pytest.mark.parametrize("n", [65, 200, 513])
@@ -83,6 +91,36 @@ def test_backward_key_len_pipeline_lengths(causal):
     inside the pipelined stretch, on a tile edge and in the last tile."""
     q, k, v, do = inputs(4, 1, 2100, seed=5200)
     compare_full(q, k, v, do, causal, [700, 1337, 2048, 2099], f"n=2100 causal={causal}")
+
+
+def _bits(B, n, seed, density=0.7):
+    """A random key mask [B, n]: entry 0 at the given density (key 0 kept),
+    entry 1 with no valid key, entry 2 with every key valid."""
+    rng = np.random.default_rng(seed)
+    valid = rng.random((B, n)) < density
+    valid[0, 0] = True
+    valid[1] = False
+    valid[2] = True
+    return valid
+
+
+@pytest.mark.parametrize("n", [65, 300, 1337])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_key_bits(n, causal):
+    """A key bit mask (the forward's key_valid, packed): a random pattern,
+    an entry with no valid key, an entry with all keys valid; the dQ kernel
+    then runs every step on its general path."""
+    q, k, v, do = inputs(3, 2, n, seed=5600 + n)
+    compare_full(q, k, v, do, causal, None, f"bits n={n} causal={causal}", valid=_bits(3, n, 5650 + n))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_key_bits_and_lengths(causal):
+    """Both masks at once: a key is hidden when past the length or when its
+    bit is clear."""
+    q, k, v, do = inputs(3, 2, 700, seed=5700)
+    compare_full(q, k, v, do, causal, [500, 700, 333], f"bits and lengths causal={causal}",
+                 valid=_bits(3, 700, 5750, density=0.5))
 
 
 def test_backward_full_lengths_match_unmasked_bitwise():
@@ -135,4 +173,4 @@ def test_backward_key_len_patch_3mp_sampled(causal):
     got = (dq[:, :, rows], dk[:, :, keys], dv[:, :, keys])
     for name, g, r, m in zip(("dQ", "dK", "dV"), got, ref, mags):
         assert_grad_within(f"{name} 3 MP key_len causal={causal}", g, r, m)
-    check_exact_zeros(dq, dk, dv, lengths, w.N, "3 MP")
+    check_exact_zeros(dq, dk, dv, kv, "3 MP")

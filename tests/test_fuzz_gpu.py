@@ -141,13 +141,18 @@ def _masked_backward_cases(count=12, seed=4049):
         cases.append(dict(i=i, B=B, H=int(rng.integers(1, 4)), N=N, causal=bool(rng.random() < 0.5),
                           scale=float(0.125 if rng.random() < 0.6 else rng.uniform(-0.4, 0.6)),
                           lens=[int(x) for x in lens], seed=int(rng.integers(0, 2**31))))
+    # the same cases with a key bit mask instead of (or with) the lengths
+    for c in list(cases):
+        cases.append(dict(c, i=c["i"] + count, bits=float(rng.uniform(0.2, 0.95)),
+                          lens=c["lens"] if rng.random() < 0.5 else None))
     return cases
 
 
-@pytest.mark.parametrize("case", _masked_backward_cases(), ids=lambda c: "m%02d_N%d%s_B%dH%d" % (
-    c["i"], c["N"], "_causal" if c["causal"] else "", c["B"], c["H"]))
+@pytest.mark.parametrize("case", _masked_backward_cases(), ids=lambda c: "m%02d_N%d%s_B%dH%d%s" % (
+    c["i"], c["N"], "_causal" if c["causal"] else "", c["B"], c["H"], "_bits" if "bits" in c else ""))
 def test_random_masked_backward(case):
-    """The backward after a forward with valid key lengths (attn_bwd_masked)."""
+    """The backward after a forward with valid key lengths, a key bit mask,
+    or both (attn_bwd_masked)."""
     B, H, N = case["B"], case["H"], case["N"]
     print(f"[fuzz] {case}", flush=True)
     w = Workload("fuzz_mbwd", B, H, N, 64, "bf16", 1.0, case["scale"], case["causal"], case["seed"], "")
@@ -155,11 +160,18 @@ def test_random_masked_backward(case):
     do = make_inputs(Workload("fuzz_mdo", B, H, N, 64, "bf16", 1.0, case["scale"], case["causal"],
                               case["seed"] + 1, ""))[0]
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
-    kl = torch.tensor(case["lens"], dtype=torch.int32, device=DEV)
-    o, lse = ea.forward(qd, kd, vd, scale=case["scale"], causal=case["causal"], key_len=kl)
-    grads = ea.backward(qd, kd, vd, o, lse, dod, scale=case["scale"], causal=case["causal"], key_len=kl)
+    masks = {}
+    valid = np.ones((B, N), dtype=bool)
+    if case["lens"] is not None:
+        masks["key_len"] = torch.tensor(case["lens"], dtype=torch.int32, device=DEV)
+        valid &= np.arange(N)[None, :] < np.asarray(case["lens"])[:, None]
+    if "bits" in case:
+        bits = np.random.default_rng(case["seed"] + 2).random((B, N)) < case["bits"]
+        masks["key_valid"] = torch.tensor(bits, device=DEV)
+        valid &= bits
+    o, lse = ea.forward(qd, kd, vd, scale=case["scale"], causal=case["causal"], **masks)
+    grads = ea.backward(qd, kd, vd, o, lse, dod, scale=case["scale"], causal=case["causal"], **masks)
     torch.cuda.synchronize()
-    valid = np.arange(N)[None, :] < np.asarray(case["lens"])[:, None]
     ref = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), case["scale"], causal=case["causal"],
                              key_valid=valid)
     mags = grad_magnitudes(q, k, v, do, case["scale"], case["causal"], key_valid=valid)
