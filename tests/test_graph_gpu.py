@@ -22,16 +22,20 @@ def _inputs(N, seed, causal):
     return q, k, v, do
 
 
-@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("masked", ["none", "len", "bits"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_and_backward_replay_in_a_graph(causal, masked):
-    """masked: both passes with valid key lengths (attn_fwd_masked's key_len,
-    attn_bwd_masked), one entry cut inside a tile."""
+    """masked: both passes with valid key lengths (one entry cut inside a
+    tile) or with a random key bit mask (attn_fwd_masked, attn_bwd_masked)."""
     q, k, v, do = _inputs(777, 9500 + causal, causal)
-    kl = torch.tensor([777, 300], dtype=torch.int32, device=DEV) if masked else None
+    masks = {}
+    if masked == "len":
+        masks["key_len"] = torch.tensor([777, 300], dtype=torch.int32, device=DEV)
+    elif masked == "bits":
+        masks["key_bits"] = ea.pack_key_mask(torch.rand(2, 777, device=DEV) < 0.6)
     # eager results (also warms the library's per-device state up before capture)
-    o_ref, lse_ref = ea.forward(q, k, v, scale=0.125, causal=causal, key_len=kl)
-    g_ref = ea.backward(q, k, v, o_ref, lse_ref, do, scale=0.125, causal=causal, key_len=kl)
+    o_ref, lse_ref = ea.forward(q, k, v, scale=0.125, causal=causal, **masks)
+    g_ref = ea.backward(q, k, v, o_ref, lse_ref, do, scale=0.125, causal=causal, **masks)
     torch.cuda.synchronize()
 
     o = torch.empty_like(q)
@@ -41,8 +45,8 @@ def test_forward_and_backward_replay_in_a_graph(causal, masked):
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph):
-            ea.forward(q, k, v, scale=0.125, causal=causal, out=o, lse=lse, key_len=kl)
-            grads = ea.backward(q, k, v, o, lse, do, scale=0.125, causal=causal, key_len=kl)
+            ea.forward(q, k, v, scale=0.125, causal=causal, out=o, lse=lse, **masks)
+            grads = ea.backward(q, k, v, o, lse, do, scale=0.125, causal=causal, **masks)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
