@@ -76,7 +76,7 @@ def compare_full(q, k, v, do, causal, lengths, what, valid=None):
     check_exact_zeros(dq, dk, dv, kv, what)
 
 
-@pytest.mark.parametrize("n", [65, 200, 513])
+@pytest.mark.parametrize("n", [1, 17, 65, 200, 513])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_key_len_sizes(n, causal):
     """Four entries: every key valid, a single key, a ragged middle length,
@@ -104,7 +104,7 @@ def _bits(B, n, seed, density=0.7):
     return valid
 
 
-@pytest.mark.parametrize("n", [65, 300, 1337])
+@pytest.mark.parametrize("n", [1, 33, 65, 300, 1337])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_key_bits(n, causal):
     """A key bit mask (the forward's key_valid, packed): a random pattern,
