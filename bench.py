@@ -10,6 +10,7 @@ to stderr.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--n N]
   python bench.py --sweep FILE   # one JSON line per workload into FILE
   python bench.py --workspace-sweep   # device memory beyond O and LSE vs P, with fits
+  python bench.py --backward [--key-len L | --key-density D]   # dQ, dK, dV instead
 
 Besides the contract fields, the line carries per-launch kernel time (mean,
 median, min) from HIP events on the launch stream, a cold-cache variant
