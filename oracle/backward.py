@@ -18,7 +18,9 @@ P = softmax(S), S = scale * Q K^T (masked):
 
 A key hidden by a key-padding mask (``key_valid`` False; the forward
 oracle's key mask) has probability 0 in every row, so it receives dK = dV = 0
-and adds nothing to dQ.  A row that sees no key at all has the constant
+and adds nothing to dQ; a (query, key) pair hidden by a block mask
+(``block_mask``, as in the forward oracle) has probability 0 and passes no
+gradient between them.  A row that sees no key at all has the constant
 output O = 0 (the forward oracle's empty row): its probabilities are all 0,
 so it passes no gradient anywhere and its dQ is 0.
 
@@ -32,11 +34,14 @@ import numpy as np
 from . import fp64
 
 
-def _probabilities(q, k, scale, causal, rows, key_valid=None):
+def _probabilities(q, k, scale, causal, rows, key_valid=None, block_mask=None):
     """P [R, N] for query rows `rows` of one head (masked keys give 0; a row
-    that sees no key is all 0).  key_valid: bool [N] or None."""
+    that sees no key is all 0).  key_valid: bool [N] or None; block_mask:
+    (M, bq, bk) or None, as in the forward oracle."""
     s = fp64._scores(q[rows], k, scale)
     vis = fp64._visible(rows, k.shape[0], causal, key_valid)
+    if block_mask is not None:
+        vis &= fp64._block_visible(rows, k.shape[0], block_mask)
     s = np.where(vis, s, -np.inf)
     empty = fp64._empty_rows(vis)
     m = np.where(empty, 0.0, fp64._row_max(s))
@@ -75,11 +80,12 @@ def _dk(ds, q, scale):
     return scale * (ds.T @ q)
 
 
-def attention_backward(q, k, v, do, scale, causal=False, key_valid=None):
+def attention_backward(q, k, v, do, scale, causal=False, key_valid=None, block_mask=None):
     """dQ, dK, dV (float64, [B, H, N, d]) of exact attention for upstream
     gradient dO.  Inputs of any real dtype are converted exactly to f64.
-    key_valid: optional bool [B, N], False hides that key from every query
-    (as in the forward oracle)."""
+    key_valid: optional bool [B, N], False hides that key from every query;
+    block_mask: optional (M, bq, bk), key j hidden from query i when
+    M[i // bq][j // bk] == 0 (both as in the forward oracle)."""
     q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
     B, H, N, d = q.shape
     kv = None if key_valid is None else np.asarray(key_valid, dtype=bool)
@@ -87,7 +93,7 @@ def attention_backward(q, k, v, do, scale, causal=False, key_valid=None):
     rows = np.arange(N)
     for b in range(B):
         for h in range(H):
-            p = _probabilities(q[b, h], k[b, h], scale, causal, rows, None if kv is None else kv[b])
+            p = _probabilities(q[b, h], k[b, h], scale, causal, rows, None if kv is None else kv[b], block_mask)
             dp = _dp(do[b, h], v[b, h])
             delta = _delta(p, dp)
             ds = _ds(p, dp, delta)

@@ -520,6 +520,41 @@ def pin_backward_invariants():
     _close(dk2, dk, 1e-12, "dK under a shared key shift")
 
 
+def pin_backward_block_mask():
+    """A block mask in the gradients: against central finite differences of
+    the forward oracle with that block mask (every entry, causal or not, a
+    mask with a query block that sees no key block), and all-ones M gives the
+    unmasked gradients bit for bit."""
+    from oracle.backward import attention_backward
+    rng = _rng(28)
+    B, H, N, d = 1, 2, 8, 4
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    scale, h = 0.6, 1e-6
+    m = np.array([[1, 0, 1, 0], [0, 1, 1, 0], [0, 0, 0, 0], [1, 1, 0, 1]], dtype=np.uint8)  # 2-row, 2-key blocks
+    for causal in (False, True):
+        bm = (m, 2, 2)
+        dq, dk, dv = attention_backward(q, k, v, do, scale, causal=causal, block_mask=bm)
+
+        def loss(qq, kk, vv):
+            return float((O.attention(qq, kk, vv, scale, causal=causal, block_mask=bm)[0] * do).sum())
+
+        for name, x, g in (("dQ", q, dq), ("dK", k, dk), ("dV", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [xp if t is x else t for t in (q, k, v)]
+                args_m = [xm if t is x else t for t in (q, k, v)]
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(g, num, 1e-7, f"{name} vs finite differences (block mask, causal={causal})")
+        assert not dq[:, :, 4:6].any(), "a query block that sees no key block has dQ = 0"
+        ones = (np.ones_like(m), 2, 2)
+        full = attention_backward(q, k, v, do, scale, causal=causal)
+        for a, b in zip(attention_backward(q, k, v, do, scale, causal=causal, block_mask=ones), full):
+            assert np.array_equal(a, b), f"all-ones block mask (causal={causal})"
+
+
 def pin_backward_hidden_keys():
     """A key-padding mask in the gradients: the hidden keys' K and V can be
     anything (every gradient stays the same bits), their own dK and dV are
@@ -605,6 +640,7 @@ INDEPENDENT_PINS = [
     pin_backward_finite_differences,
     pin_backward_invariants,
     pin_backward_hidden_keys,
+    pin_backward_block_mask,
     pin_nonfinite_inputs,
 ]
 

@@ -73,7 +73,7 @@ def test_independent_pins_catch_mutant(name, monkeypatch):
     assert caught, f"mutant {name} passed every independent pin"
 
 
-def _p_ignoring_key_mask(q, k, scale, causal, rows, key_valid=None):
+def _p_ignoring_key_mask(q, k, scale, causal, rows, key_valid=None, block_mask=None):
     """Probabilities that forget the key-padding mask."""
     s = O._scores(q[rows], k, scale)
     s = np.where(O._visible(rows, k.shape[0], causal, None), s, -np.inf)
@@ -81,11 +81,38 @@ def _p_ignoring_key_mask(q, k, scale, causal, rows, key_valid=None):
     return e / e.sum(axis=1)[:, None]
 
 
-def _p_empty_rows_uniform(q, k, scale, causal, rows, key_valid=None):
+def _p_ignoring_block_mask(q, k, scale, causal, rows, key_valid=None, block_mask=None):
+    """Probabilities that forget the block mask."""
+    s = O._scores(q[rows], k, scale)
+    s = np.where(O._visible(rows, k.shape[0], causal, key_valid), s, -np.inf)
+    empty = ~np.isfinite(s).any(axis=1)
+    s[empty] = 0.0
+    e = np.where(np.isfinite(s), np.exp(s - s.max(axis=1)[:, None]), 0.0)
+    return np.where(empty[:, None], 0.0, e / np.where(empty, 1.0, e.sum(axis=1))[:, None])
+
+
+def _p_block_mask_transposed(q, k, scale, causal, rows, key_valid=None, block_mask=None):
+    """Probabilities that read the block mask with query and key blocks swapped."""
+    s = O._scores(q[rows], k, scale)
+    vis = O._visible(rows, k.shape[0], causal, key_valid)
+    if block_mask is not None:
+        m, bq, bk = block_mask
+        m = np.asarray(m, dtype=bool)
+        vis &= m[(np.arange(k.shape[0])[None, :] // bk) % m.shape[0], (rows[:, None] // bq) % m.shape[1]]
+    s = np.where(vis, s, -np.inf)
+    empty = ~vis.any(axis=1)
+    s[empty] = 0.0
+    e = np.where(vis, np.exp(s - s.max(axis=1)[:, None]), 0.0)
+    return e / np.where(empty, 1.0, e.sum(axis=1))[:, None]
+
+
+def _p_empty_rows_uniform(q, k, scale, causal, rows, key_valid=None, block_mask=None):
     """Probabilities that spread a row with no visible key uniformly over
     every key instead of leaving it at 0."""
     s = O._scores(q[rows], k, scale)
     vis = O._visible(rows, k.shape[0], causal, key_valid)
+    if block_mask is not None:
+        vis &= O._block_visible(rows, k.shape[0], block_mask)
     s = np.where(vis, s, -np.inf)
     empty = ~vis.any(axis=1)
     s[empty] = 0.0
@@ -97,6 +124,8 @@ def _p_empty_rows_uniform(q, k, scale, causal, rows, key_valid=None):
 BACKWARD_MUTANTS = {
     "probabilities_ignore_key_mask": ("_probabilities", _p_ignoring_key_mask),
     "probabilities_empty_rows_uniform": ("_probabilities", _p_empty_rows_uniform),
+    "probabilities_ignore_block_mask": ("_probabilities", _p_ignoring_block_mask),
+    "probabilities_block_mask_transposed": ("_probabilities", _p_block_mask_transposed),
     "dv_not_transposed": ("_dv", lambda p, do: p @ do),
     "dp_uses_values_untransposed": ("_dp", lambda do, v: do @ v[::-1].T),
     "delta_sums_dp_only": ("_delta", lambda p, dp: dp.sum(axis=1)),
