@@ -3,7 +3,8 @@
 The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
 ``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_fwd_split``,
 ``attn_fwd_split_workspace_size``, ``attn_fwd_block_sparse``,
-``attn_bwd``, ``attn_bwd_masked``, ``attn_bwd_noalloc``, ``attn_bwd_workspace_size``,
+``attn_bwd``, ``attn_bwd_masked``, ``attn_bwd_block_sparse``, ``attn_bwd_noalloc``,
+``attn_bwd_workspace_size``,
 ``attn_pack_key_mask`` and ``attn_strerror`` carry the names and
 arguments
 of the C entry points declared in include/attn.h and only marshal arguments;
@@ -20,7 +21,7 @@ import os
 import torch  # imported first: the library then binds to torch's HIP runtime
 
 __all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-           "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_masked", "attn_bwd_noalloc", "attn_bwd_workspace_size",
+           "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_masked", "attn_bwd_block_sparse", "attn_bwd_noalloc", "attn_bwd_workspace_size",
            "attn_pack_key_mask", "AttnLayout",
            "backward", "attn_strerror", "forward", "pack_key_mask", "AttnError",
            "library_path", "load_library", "split_workspace"]
@@ -32,7 +33,7 @@ _lib = None
 ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH, ATTN_E_SCRATCH = range(6)
 # the static scratch of attn_bwd_noalloc (ATTN_BWD_NOALLOC_SCRATCH_BYTES in attn.h)
 BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
-EXPORTED = ("attn_bwd", "attn_bwd_masked", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
+EXPORTED = ("attn_bwd", "attn_bwd_masked", "attn_bwd_block_sparse", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
             "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse",
             "attn_pack_key_mask", "attn_strerror")
 SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 128, 64
@@ -89,6 +90,8 @@ def load_library():
     lib.attn_bwd.restype = i32
     lib.attn_bwd_masked.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr, ptr, ptr]
     lib.attn_bwd_masked.restype = i32
+    lib.attn_bwd_block_sparse.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr, ptr]
+    lib.attn_bwd_block_sparse.restype = i32
     lib.attn_bwd_noalloc.argtypes = [ptr] * 9 + [i32, i32, i32, i32, f32, i32, ptr]
     lib.attn_bwd_noalloc.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
@@ -179,6 +182,14 @@ def attn_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, sc
                                           int(bool(causal)), key_len, key_bits, stream))
 
 
+def attn_bwd_block_sparse(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, block_mask,
+                          stream):
+    """C entry point attn_bwd_block_sparse: attn_bwd plus the device address
+    of the [ceil(N/128)][ceil(N/64)] block mask bytes."""
+    _check(load_library().attn_bwd_block_sparse(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d,
+                                                float(scale), int(bool(causal)), block_mask, stream))
+
+
 def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream):
     """C entry point attn_bwd_noalloc: attn_bwd without a workspace argument
     (the library's static device scratch; allocates nothing)."""
@@ -191,14 +202,17 @@ def attn_bwd_workspace_size(B, H, N):
     return int(load_library().attn_bwd_workspace_size(B, H, N))
 
 
-def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None, key_valid=None, key_bits=None):
+def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None, key_valid=None, key_bits=None,
+             block_mask=None):
     """dQ, dK, dV (bf16 [B, H, N, d]) of attention for upstream gradient dout,
-    from forward's o and lse (same q, k, v, scale, causal and key masks).
+    from forward's o and lse (same q, k, v, scale, causal and masks).
     Key masks as in forward (int32 [B] key_len, bool [B, N] key_valid packed
     here, or int32 [B, ceil(N/32)] key_bits), through attn_bwd_masked:
-    hidden keys get dK = dV = 0.  Contiguous bf16 tensors on one GPU; the
-    workspace (attn_bwd_workspace_size bytes) is allocated here.  Launches
-    on torch's current stream."""
+    hidden keys get dK = dV = 0.  block_mask as in forward (bool or uint8
+    [ceil(N/128), ceil(N/64)], no key mask), through attn_bwd_block_sparse.
+    Contiguous bf16 tensors on one GPU; the workspace
+    (attn_bwd_workspace_size bytes) is allocated here.  Launches on torch's
+    current stream."""
     ts = (q, k, v, o, dout)
     if any(t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous() or t.device != q.device
            for t in ts) or q.dim() != 4 or not q.is_cuda:
@@ -223,11 +237,20 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None, key_
     if key_bits is not None and (key_bits.dtype != torch.int32 or key_bits.shape != (B, (N + 31) // 32)
                                  or not key_bits.is_contiguous() or key_bits.device != q.device):
         raise ValueError("key_bits must be a contiguous int32 [B, ceil(N/32)] tensor on q's device")
+    if block_mask is not None:
+        nbq, nbk = (N + 127) // 128, (N + 63) // 64
+        if block_mask.dtype not in (torch.bool, torch.uint8) or block_mask.shape != (nbq, nbk) \
+                or not block_mask.is_contiguous() or block_mask.device != q.device:
+            raise ValueError(f"block_mask must be a contiguous bool or uint8 [{nbq}, {nbk}] tensor on q's device")
+        if key_len is not None or key_bits is not None:
+            raise ValueError("block_mask takes no key mask")
     ws = torch.empty(attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
     with torch.cuda.device(q.device):
-        if key_len is None and key_bits is None:
+        if block_mask is not None:
+            attn_bwd_block_sparse(*ptrs, B, H, N, d, scale, causal, block_mask.data_ptr(), _stream_handle(q.device))
+        elif key_len is None and key_bits is None:
             attn_bwd(*ptrs, B, H, N, d, scale, causal, _stream_handle(q.device))
         else:
             attn_bwd_masked(*ptrs, B, H, N, d, scale, causal, 0 if key_len is None else key_len.data_ptr(),

@@ -80,12 +80,18 @@ struct BwdArgs {
   int heads;           // H: batch entry of head bh is bh / H
   const uint32_t* key_bits;  // [B][words] or null: bit j%32 of word j/32 clear hides key j
   int words;                 // ceil(n / 32)
+  const uint8_t* block_mask;  // block-sparse: [ceil(n/128)][mask_cols], 0 hides that block
+  int mask_cols;              // ceil(n / 64)
 };
 
-// Which keys take part, as a kernel template argument: all of them, those
-// below each entry's valid length, or (kKeysBits) those whose bit is set
-// and, when lengths are given too, below the length.
-constexpr int kKeysAll = 0, kKeysLen = 1, kKeysBits = 2;
+// Which (query, key) pairs take part, as a kernel template argument: all of
+// them, keys below each entry's valid length, (kKeysBits) keys whose bit is
+// set and, when lengths are given too, below the length, or (kKeysBlocks)
+// pairs whose 128-query x 64-key block of the block mask is set.
+constexpr int kKeysAll = 0, kKeysLen = 1, kKeysBits = 2, kKeysBlocks = 3;
+// The block mask's granularity (the forward's block-sparse tiles) and the
+// longest list of 64-row tiles a workgroup keeps in LDS (N <= 262,144).
+constexpr int kBlockQ = 128, kBlockK = 64, kMaxBlockTiles = 4096;
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -95,8 +101,12 @@ __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast
 // needed rather than kept live across a loop).
 template <int kKeys>
 __device__ __forceinline__ int valid_keys(const BwdArgs& a, int bh) {
-  if (kKeys == kKeysBits && !a.key_len) return a.n;
-  return __builtin_amdgcn_readfirstlane(min(max(a.key_len[bh / a.heads], 0), a.n));
+  if constexpr (kKeys == kKeysLen || kKeys == kKeysBits) {
+    if (kKeys == kKeysBits && !a.key_len) return a.n;
+    return __builtin_amdgcn_readfirstlane(min(max(a.key_len[bh / a.heads], 0), a.n));
+  } else {
+    return a.n;
+  }
 }
 
 // Bit word w (keys 32w .. 32w+31) of head bh's batch entry.
@@ -260,7 +270,10 @@ struct TileDma {
 // entry's valid length, or with a clear bit) are hidden from every query;
 // they get dK = dV = 0 (each output column is one key, so zeroing it at the
 // end is exact whatever its accumulators hold).  A workgroup whose keys all
-// lie past the valid length only writes those zeros.
+// lie past the valid length only writes those zeros.  kKeysBlocks: the
+// workgroup visits only the query tiles whose block is set in one of its two
+// key columns of the block mask, every step on the general path, and a wave
+// drops (P = dS = 0) the halves its own column, or the causal mask, hides.
 template <bool kCausal, int kWaves, int kKeys>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
@@ -291,7 +304,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int key0 = kb * kRows + wave_s * 32;  // this wave's first key
   const int key = key0 + l32;                 // this lane's key
-  if constexpr (kKeys != kKeysAll) {
+  if constexpr (kKeys == kKeysLen || kKeys == kKeysBits) {
     if (kb * kRows >= valid_keys<kKeys>(a, bh)) {  // uniform: before any barrier
       if (key < n) {
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -305,6 +318,37 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
+  // kKeysBlocks: the 64-query tiles whose query block has either of this
+  // workgroup's two key columns set (causal: none before its first key),
+  // compacted into blk_list (wave 0 writes, every wave counts); from here on
+  // a tile index is a position in that list.
+  __shared__ uint16_t blk_list[kKeys == kKeysBlocks ? kMaxBlockTiles : 1];
+  int n_listed = 0;
+  if constexpr (kKeys == kKeysBlocks) {
+    static_assert(kRows == 2 * kBlockK, "a workgroup spans two key columns of the block mask");
+    const int tq_end = (n + kBwdTile - 1) / kBwdTile;
+    const int c0 = 2 * kb;
+    const bool c1_in = c0 + 1 < a.mask_cols;
+    for (int base = kCausal ? (kb * kRows) / kBwdTile : 0; base < tq_end; base += 64) {
+      const int t = base + lane;
+      bool act = false;
+      if (t < tq_end) {
+        const uint8_t* mrow = a.block_mask + (size_t)(t * kBwdTile / kBlockQ) * a.mask_cols;
+        act = mrow[c0] != 0 || (c1_in && mrow[c0 + 1] != 0);
+      }
+      const uint64_t bal = __ballot(act);
+      const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+      if (wave == 0 && act) blk_list[n_listed + below] = (uint16_t)t;
+      n_listed += __popcll(bal);
+    }
+    __syncthreads();
+  }
+  // the query tile at list position t (kKeysBlocks), else tile t itself
+  auto tile_of = [&](int t) -> int {
+    if constexpr (kKeys == kKeysBlocks) return __builtin_amdgcn_readfirstlane((int)blk_list[t]);
+    else return t;
+  };
+
   // K^T and V^T operands (B operands of S = Q K^T and dP = dO V^T)
   bf16x8 kop[4], vop[4];
 #pragma unroll
@@ -317,26 +361,27 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) row_off[ks] = tile_off(l32, 2 * ks + hi);
 
-  // 64-query tiles of the workgroup
-  const int t0 = kCausal ? (kb * kRows) / kBwdTile : 0;
-  const int t_end = (n + kBwdTile - 1) / kBwdTile;
+  // 64-query tiles of the workgroup (kKeysBlocks: list positions)
+  const int t0 = kKeys == kKeysBlocks ? 0 : kCausal ? (kb * kRows) / kBwdTile : 0;
+  const int t_end = kKeys == kKeysBlocks ? n_listed : (n + kBwdTile - 1) / kBwdTile;
   // 32-query halves this wave works on: [jf, jl], every half of the tiles.
   // Causal: from the half that starts at the wave's first key (the
   // diagonal, masked per element).  Queries past N have L2 = +inf, so their
   // probabilities are exactly 0.  (A wave whose keys all lie past N runs
   // like the others; nothing of it is written.)
   const int jl = 2 * t_end - 1;
-  const int jf = kCausal ? key0 / 32 : 0;
+  const int jf = kCausal && kKeys != kKeysBlocks ? key0 / 32 : 0;
   // Tiles t0 .. t0+kHead-1 run on the general path; then tiles whose two
   // steps are fast in every wave (2t > the last wave's first half, 2t+1 <
   // jl) run pipelined, in whole turns of the ring and a last partial one;
   // the rest on the general path again.
   constexpr int kHead = kCausal ? (kWaves + 1) / 2 : 1;
-  const int t_fast_end = jl >= 2 ? (jl - 2) / 2 + 1 : 0;
+  const int t_fast_end = kKeys == kKeysBlocks ? 0 : jl >= 2 ? (jl - 2) / 2 + 1 : 0;
   const Dma dma(qg, dog, n, wave, lane, a.ws + (size_t)bh * 2 * a.n_pad, a.n_pad);
+  auto dma_issue = [&](int t, char* sb) { dma.issue(tile_of(t), sb); };
 
   // a step is fast (pipelined, unmasked) when it has a step on each side
-  auto fast = [&](int j) { return j >= jf + 1 && j <= jl - 1; };
+  auto fast = [&](int j) { return kKeys != kKeysBlocks && j >= jf + 1 && j <= jl - 1; };
   // stage of half j (tile j/2; the half's rows start at 32*(j&1))
   auto half_stage = [&](int j) { return stage((j / 2 - t0) % kStages); };
   (void)half_stage;
@@ -423,7 +468,16 @@ bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     if (j >= jf && j <= jl) {
-      const bool diag = kCausal && j == jf;  // key > query hidden
+      bool diag = kCausal && j == jf;  // key > query hidden
+      bool none = false;               // kKeysBlocks: the whole half is hidden from this wave
+      if constexpr (kKeys == kKeysBlocks) {
+        const int tq = tile_of(j >> 1);
+        const int rh = 2 * tq + (j & 1);  // the half's query rows start at 32 * rh
+        const int col = key0 / kBlockK;
+        diag = kCausal && rh == key0 / 32;
+        none = (kCausal && rh < key0 / 32) || col >= a.mask_cols ||
+               a.block_mask[(size_t)(tq * kBwdTile / kBlockQ) * a.mask_cols + col] == 0;
+      }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 l4 = l2_group(cb, hc, g4);
@@ -434,6 +488,9 @@ bwd_dkdv_kernel(BwdArgs a) {
           float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r + 1], c, -l4[e + 1]));
           if (diag && l32 > 8 * g4 + 4 * hi + e) p0 = 0.f;
           if (diag && l32 > 8 * g4 + 4 * hi + e + 1) p1 = 0.f;
+          if constexpr (kKeys == kKeysBlocks) {
+            if (none) p0 = p1 = 0.f;
+          }
           set_word(p_cur[r >> 3], (r & 7) >> 1, pack_bf16(p0, p1));
           set_word(ds_cur[r >> 3], (r & 7) >> 1, pack_bf16(p0 * dp_cur[r], p1 * dp_cur[r + 1]));
         }
@@ -521,7 +578,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
     vm_wait_barrier_tiles<Dma::kPerTile, kStages - 4>(
         max(0, min(min(t_end - 1, t + kStages - 2) - (t + 2), kStages - 4)));
-    if (t + kStages - 1 < t_end) dma.issue(t + kStages - 1, stage(sp));
+    if (t + kStages - 1 < t_end) dma_issue(t + kStages - 1, stage(sp));
   };
   using kGeneral = std::false_type;
   using kFast = std::true_type;
@@ -530,7 +587,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   // S and dP of the first half
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
-    if (t0 + i < t_end) dma.issue(t0 + i, stage(i));
+    if (t0 + i < t_end) dma_issue(t0 + i, stage(i));
   vm_wait_barrier_tiles<Dma::kPerTile, kStages - 3>(max(0, min(t_end - t0, kStages - 1) - 2));
   step_general(2 * t0 - 1, stage(0), 0, stage(kStages - 1), 1, stage(kStages - 1), 0, stage(0), sB, dpB, sA, dpA,
                pA, dsA, pB, dsB);
@@ -578,7 +635,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     uint16_t* dvrow = a.dv + head + (size_t)key_e * kD;
     const float scale = a.scale;
     bool hidden = false;  // a key past the valid length or with a clear bit
-    if constexpr (kKeys != kKeysAll) hidden = key_e >= valid_keys<kKeys>(a, bh);
+    if constexpr (kKeys == kKeysLen || kKeys == kKeysBits) hidden = key_e >= valid_keys<kKeys>(a, bh);
     if constexpr (kKeys == kKeysBits) hidden = hidden || !((key_word(a, bh, key_e >> 5) >> (key_e & 31)) & 1u);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -589,7 +646,7 @@ bwd_dkdv_kernel(BwdArgs a) {
         unsigned k23 = pack_bf16(acc_dk[db][4 * r4 + 2] * scale, acc_dk[db][4 * r4 + 3] * scale);
         unsigned v01 = pack_bf16(acc_dv[db][4 * r4], acc_dv[db][4 * r4 + 1]);
         unsigned v23 = pack_bf16(acc_dv[db][4 * r4 + 2], acc_dv[db][4 * r4 + 3]);
-        if constexpr (kKeys != kKeysAll) {
+        if constexpr (kKeys == kKeysLen || kKeys == kKeysBits) {
           if (hidden) k01 = k23 = v01 = v23 = 0u;
         }
         *(u32x2*)(dkrow + f0) = u32x2{k01, k23};
@@ -604,11 +661,14 @@ bwd_dkdv_kernel(BwdArgs a) {
 // valid length are visited (the half holding the last one masked per
 // element), and an entry with no valid key gets dQ = 0; with kKeysBits every
 // step runs on the general path, which also drops the keys whose bit is
-// clear (one mask word per 32-key half, a select per score).
+// clear (one mask word per 32-key half, a select per score).  kKeysBlocks:
+// the workgroup (one 128-query block) visits only the key tiles its row of
+// the block mask sets, every step on the general path; the ring is one
+// stage shorter so that two workgroups with their tile lists share a CU.
 template <bool kCausal, int kWaves, int kKeys>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a) {
-  constexpr int kStages = kWaves == 8 ? 6 : 5;
+  constexpr int kStages = kKeys == kKeysBlocks ? 4 : kWaves == 8 ? 6 : 5;
   constexpr int kRows = 32 * kWaves;  // queries per workgroup
   constexpr int kStageBytes = 2 * kTileBytes;
   using Dma = TileDma<kWaves, false>;
@@ -638,7 +698,7 @@ bwd_dq_kernel(BwdArgs a) {
   const int qi = q0w + l32;                  // this lane's query (< n_pad)
   // keys that take part: all n, or the entry's valid length
   int n_k = n;
-  if constexpr (kKeys != kKeysAll) {
+  if constexpr (kKeys == kKeysLen || kKeys == kKeysBits) {
     n_k = valid_keys<kKeys>(a, bh);
     if (n_k == 0) {  // uniform: before any barrier
       if (qi < n) {
@@ -703,17 +763,42 @@ bwd_dq_kernel(BwdArgs a) {
   // +inf, so its probabilities are 0, and no dQ row of it is written.)
   const int q_last = min(n - 1, qb * kRows + kRows - 1);
   const int kv_end = kCausal ? (kKeys != kKeysAll ? min(q_last + 1, n_k) : q_last + 1) : n_k;
-  const int t_end = (kv_end + kBwdTile - 1) / kBwdTile;
-  const int jl = kCausal ? min(q0w / 32, 2 * t_end - 1) : 2 * t_end - 1;
+  // kKeysBlocks: the key tiles below kv_end that this query block's row of
+  // the block mask sets, compacted into blk_list (wave 0 writes, every wave
+  // counts); from here on a tile index is a position in that list, and each
+  // wave masks its halves by their real key offsets.
+  __shared__ uint16_t blk_list[kKeys == kKeysBlocks ? kMaxBlockTiles : 1];
+  int n_listed = 0;
+  if constexpr (kKeys == kKeysBlocks) {
+    static_assert(kRows == kBlockQ, "a workgroup is one query block of the block mask");
+    const int kt_end = (kv_end + kBwdTile - 1) / kBwdTile;
+    const uint8_t* mrow = a.block_mask + (size_t)qb * a.mask_cols;
+    for (int base = 0; base < kt_end; base += 64) {
+      const int kt = base + lane;
+      const bool act = kt < kt_end && mrow[kt] != 0;
+      const uint64_t bal = __ballot(act);
+      const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+      if (wave == 0 && act) blk_list[n_listed + below] = (uint16_t)kt;
+      n_listed += __popcll(bal);
+    }
+    __syncthreads();
+  }
+  auto tile_of = [&](int t) -> int {
+    if constexpr (kKeys == kKeysBlocks) return __builtin_amdgcn_readfirstlane((int)blk_list[t]);
+    else return t;
+  };
+  const int t_end = kKeys == kKeysBlocks ? n_listed : (kv_end + kBwdTile - 1) / kBwdTile;
+  const int jl = kCausal && kKeys != kKeysBlocks ? min(q0w / 32, 2 * t_end - 1) : 2 * t_end - 1;
   // Tile 0 runs on the general path; then tiles whose two steps are fast in
   // every wave (2t+1 < the first wave's jl), in whole turns of the ring; the
   // rest on the general path again.
   constexpr int kHead = 1;
   const int jl_min = kCausal ? min(qb * kWaves, 2 * t_end - 1) : 2 * t_end - 1;
-  const int t_fast_end = kKeys == kKeysBits ? 0 : jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
+  const int t_fast_end = kKeys == kKeysBits || kKeys == kKeysBlocks ? 0 : jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
   const Dma dma(kg, vg, n, wave, lane, nullptr, 0);
+  auto dma_issue = [&](int t, char* sb) { dma.issue(tile_of(t), sb); };
 
-  auto fast = [&](int j) { return kKeys != kKeysBits && j >= 1 && j <= jl - 1; };
+  auto fast = [&](int j) { return kKeys != kKeysBits && kKeys != kKeysBlocks && j >= 1 && j <= jl - 1; };
   auto half_stage = [&](int j) { return stage((j / 2) % kStages); };
   auto k_row = [&](const char* sb, int h, int ks) { return lds_read_b128(sb, h * 32 * kRow + row_off[ks]); };
   auto v_row = [&](const char* sb, int h, int ks) {
@@ -774,9 +859,10 @@ bwd_dq_kernel(BwdArgs a) {
       }
     }
     if (j >= 0 && j <= jl) {
-      const int k0 = 32 * j;
+      const int k0 = 32 * (kKeys == kKeysBlocks ? 2 * tile_of(j >> 1) + (j & 1) : j);  // the half's first key
       const bool diag = kCausal && k0 == q0w;
       const bool ragged = k0 + 32 > n_k;
+      const bool none = kKeys == kKeysBlocks && kCausal && k0 > q0w;  // every key after the wave's queries
       uint32_t kept = ~0u;  // kKeysBits: bit kr set = key k0 + kr takes part
       if constexpr (kKeys == kKeysBits) kept = k0 < n ? key_word(a, bh, j) >> (4 * hi) : 0u;  // words: keys < n
 #pragma unroll
@@ -792,6 +878,9 @@ bwd_dq_kernel(BwdArgs a) {
           const int kb0 = 8 * (r >> 2) + (r & 3);  // key - k0 - 4 * hi
           if (!((kept >> kb0) & 1u)) p0 = 0.f;
           if (!((kept >> (kb0 + 1)) & 1u)) p1 = 0.f;
+        }
+        if constexpr (kKeys == kKeysBlocks) {
+          if (none) p0 = p1 = 0.f;
         }
         set_word(ds_cur[r >> 3], (r & 7) >> 1, pack_bf16(p0 * dp_cur[r], p1 * dp_cur[r + 1]));
       }
@@ -860,7 +949,7 @@ bwd_dq_kernel(BwdArgs a) {
     }
     vm_wait_barrier_tiles<Dma::kPerTile, kStages - 4>(
         max(0, min(min(t_end - 1, t + kStages - 2) - (t + 2), kStages - 4)));
-    if (t + kStages - 1 < t_end) dma.issue(t + kStages - 1, stage(sp));
+    if (t + kStages - 1 < t_end) dma_issue(t + kStages - 1, stage(sp));
   };
   using kGeneral = std::false_type;
   using kFast = std::true_type;
@@ -868,7 +957,7 @@ bwd_dq_kernel(BwdArgs a) {
   // ---- prologue
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
-    if (i < t_end) dma.issue(i, stage(i));
+    if (i < t_end) dma_issue(i, stage(i));
   vm_wait_barrier_tiles<Dma::kPerTile, kStages - 3>(max(0, min(t_end, kStages - 1) - 2));
   step_general(-1, stage(0), 0, stage(kStages - 1), 1, stage(kStages - 1), 0, stage(0), sB, dpB, sA, dpA, dsA,
                dsB);
@@ -893,7 +982,7 @@ bwd_dq_kernel(BwdArgs a) {
              kGeneral());
     });
   // dQ of the last half (every DMA has landed)
-  if (2 * t_end - 1 <= jl) {
+  if ((kKeys != kKeysBlocks || t_end > 0) && 2 * t_end - 1 <= jl) {  // (an empty block list has no last half)
     const char* pb = half_stage(2 * t_end - 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i & 1] = mfma(k_tr(pb, 1, i), dsB[i >> 1], acc[i & 1]);
@@ -973,7 +1062,7 @@ attn_status bwd_validate(const void* q, const void* k, const void* v, const void
 attn_status bwd_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N,
                        float scale, int causal, const int* key_len, const uint32_t* key_bits,
-                       void* stream) {
+                       const uint8_t* block_mask, void* stream) {
   BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -992,6 +1081,8 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
   a.key_len = key_len;
   a.key_bits = key_bits;
   a.words = (N + 31) / 32;
+  a.block_mask = block_mask;
+  a.mask_cols = (N + kBlockK - 1) / kBlockK;
   a.blocks = a.total = 0;
   a.c = scale * kLog2e;
   a.scale = scale;
@@ -1001,6 +1092,15 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
   // kernel reads (L2 and -D of each query row up to its row blocks' end,
   // padding rows +inf and 0), so nothing has to start at zero.
   hipError_t e;
+  if (block_mask) {  // 4-wave workgroups: one 128-query block (dQ), two 64-key columns (dK/dV)
+    const void* k_dq = causal ? reinterpret_cast<const void*>(&bwd_dq_kernel<true, 4, kKeysBlocks>)
+                              : reinterpret_cast<const void*>(&bwd_dq_kernel<false, 4, kKeysBlocks>);
+    const void* k_dkdv = causal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, 4, kKeysBlocks>)
+                                : reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, 4, kKeysBlocks>);
+    e = launch_main<4>(k_dq, a, B, H, N, s);
+    if (e == hipSuccess) e = launch_main<4>(k_dkdv, a, B, H, N, s);
+    return launch_status(e);
+  }
   const int keys = key_bits ? kKeysBits : key_len ? kKeysLen : kKeysAll;
   if (causal) {
     const void* const k_dq[3] = {reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, kKeysAll>),
@@ -1065,7 +1165,7 @@ extern "C" attn_status attn_bwd(const void* q, const void* k, const void* v, con
   st = check_device();
   if (st != ATTN_OK) return st;
   return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
-                    nullptr, nullptr, stream);
+                    nullptr, nullptr, nullptr, stream);
 }
 
 extern "C" attn_status attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -1079,7 +1179,22 @@ extern "C" attn_status attn_bwd_masked(const void* q, const void* k, const void*
   st = check_device();
   if (st != ATTN_OK) return st;
   return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
-                    key_len, key_bits, stream);
+                    key_len, key_bits, nullptr, stream);
+}
+
+extern "C" attn_status attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                             void* workspace, int B, int H, int N, int d, float scale, int causal,
+                                             const unsigned char* block_mask, void* stream) {
+  if (!workspace || !block_mask) return ATTN_E_INVALID;
+  attn_status st = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (N > kBlockK * kMaxBlockTiles) return ATTN_E_INVALID;
+  if (misaligned(workspace, 16)) return ATTN_E_ALIGN;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
+                    nullptr, nullptr, block_mask, stream);
 }
 
 extern "C" attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
@@ -1093,5 +1208,6 @@ extern "C" attn_status attn_bwd_noalloc(const void* q, const void* k, const void
   float* ws = nullptr;
   st = scratch_address(&ws);
   if (st != ATTN_OK) return st;
-  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, scale, causal, nullptr, nullptr, stream);
+  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, scale, causal, nullptr, nullptr, nullptr,
+                    stream);
 }

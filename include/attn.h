@@ -343,6 +343,30 @@ attn_status attn_bwd_masked(const void *q, const void *k, const void *v,
                             const unsigned *key_bits, void *stream);
 
 /*
+ * attn_bwd_block_sparse: attn_bwd for a forward run by
+ * attn_fwd_block_sparse with the same block_mask (FlashAttention reading
+ * notes, section on block-sparse FlashAttention: the backward skips the
+ * same zero blocks).  A (query, key) pair whose block of M is 0 has
+ * probability 0, so it passes no gradient between them; a query whose row
+ * of M (with the causal mask) leaves no key has dQ = 0.
+ *   block_mask : const unsigned char [ceil(N/128)][ceil(N/64)] device array,
+ *                as attn_fwd_block_sparse (one M for every batch entry and
+ *                head; query block i / 128, key block j / 64).
+ * Work follows M: the dQ kernel visits only the key tiles its query block's
+ * row sets, the dK/dV kernel only the query tiles whose blocks set its key
+ * columns; both run every step on their general path (no pipelined fast
+ * path), so a dense M costs more than attn_bwd.  Other arguments and errors
+ * as attn_bwd, plus ATTN_E_INVALID for a NULL block_mask or N > 262144.
+ */
+attn_status attn_bwd_block_sparse(const void *q, const void *k, const void *v,
+                                  const void *o, const float *lse,
+                                  const void *dout, void *dq, void *dk,
+                                  void *dv, void *workspace, int B, int H,
+                                  int N, int d, float scale, int causal,
+                                  const unsigned char *block_mask,
+                                  void *stream);
+
+/*
  * Bytes of workspace attn_bwd needs: 8 * B * H * ceil(N / 256) * 256 (two
  * fp32 values per padded row of every head); 0 when B, H or N is below 1.
  */

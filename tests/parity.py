@@ -102,6 +102,26 @@ def grad_magnitudes(q, k, v, do, scale, causal, key_valid=None):
     return mq, mk, mv
 
 
+def grad_magnitudes_blocks(q, k, v, do, scale, causal, block_mask):
+    """grad_magnitudes under a block mask (M, bq, bk)."""
+    from oracle import backward as ob
+    from workloads import to_f64
+    q, k, v, do = (to_f64(t) for t in (q, k, v, do))
+    B, H, N, d = q.shape
+    mq, mk, mv = (np.zeros((B, H, N, d)) for _ in range(3))
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            p = ob._probabilities(q[b, h], k[b, h], scale, causal, rows, None, block_mask)
+            dp = ob._dp(do[b, h], v[b, h])
+            delta = ob._delta(p, dp)
+            mds = p * (np.abs(dp) + np.abs(delta)[:, None])
+            mq[b, h] = abs(scale) * (mds @ np.abs(k[b, h]))
+            mk[b, h] = abs(scale) * (mds.T @ np.abs(q[b, h]))
+            mv[b, h] = p.T @ np.abs(do[b, h])
+    return mq, mk, mv
+
+
 def assert_grad_within(name, got, ref, mag):
     from workloads import to_f64
     got = to_f64(got)

@@ -158,6 +158,27 @@ def test_backward_masked_validation():
         assert bwd(key_len=None, key_bits=None) == ea.ATTN_E_DEVICE
 
 
+def test_backward_block_sparse_validation():
+    """attn_bwd_block_sparse: attn_bwd's checks, a block mask, N <= 262,144,
+    all before any device call."""
+    lib = ea.load_library()
+
+    def bwd(**kw):
+        ptrs = [kw.get(n, ALIGNED) for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws")]
+        return lib.attn_bwd_block_sparse(*ptrs, kw.get("B", 1), 1, kw.get("N", 100), kw.get("d", 64), 0.125, 0,
+                                         kw.get("mask", ALIGNED), None)
+    assert bwd(mask=None) == ea.ATTN_E_INVALID
+    assert bwd(ws=None) == ea.ATTN_E_INVALID
+    assert bwd(d=32) == ea.ATTN_E_INVALID
+    assert bwd(N=64 * 4096 + 1) == ea.ATTN_E_INVALID
+    assert bwd(q=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    assert bwd(ws=ALIGNED + 4) == ea.ATTN_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd() == ea.ATTN_E_DEVICE
+        assert bwd(N=64 * 4096) == ea.ATTN_E_DEVICE
+
+
 def test_backward_noalloc_validation():
     """attn_bwd_noalloc: attn_bwd's checks, then the static scratch limit
     (16 MiB = 8 * B * H * ceil(N/256) * 256 bytes), all before any device
