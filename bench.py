@@ -10,7 +10,7 @@ to stderr.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--n N]
   python bench.py --sweep FILE   # one JSON line per workload into FILE
   python bench.py --workspace-sweep   # device memory beyond O and LSE vs P, with fits
-  python bench.py --backward [--key-len L | --key-density D]   # dQ, dK, dV instead
+  python bench.py --backward [--key-len L | --key-density D | --block-density D]   # dQ, dK, dV instead
 
 Besides the contract fields, the line carries per-launch kernel time (mean,
 median, min) from HIP events on the launch stream, a cold-cache variant
@@ -553,7 +553,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     return line
 
 
-def bench_backward(w, steps, warmup, key_len=None, key_density=None):
+def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_density=None):
     """attn_bwd (two kernels: dQ with the per-row terms, then dK/dV) on the workload, inputs and
     the forward's O, LSE resident.  FLOPs: the algorithmic 10*B*H*N^2*d of
     the recomputing backward pass (recompute S, then dV, dP, dQ, dK: five
@@ -562,7 +562,10 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None):
     executed).  key_len: every entry keeps this many valid keys; key_density:
     a random key bit mask (seed 1001) keeps about this fraction of each
     entry's keys (attn_bwd_masked, after the forward with the same masks);
-    FLOPs then count the visible (query, key) pairs only: 10*d per pair."""
+    FLOPs then count the visible (query, key) pairs only: 10*d per pair.
+    block_density: a random block mask as in the forward's block-sparse
+    lines (seed 1000; attn_bwd_block_sparse), FLOPs over the set blocks
+    (non-causal)."""
     import numpy as np
     import torch
     import exact_attention_29_amd as ea
@@ -579,7 +582,11 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None):
         if key_len is not None:
             kvalid &= np.arange(N)[None, :] < key_len
     kbits = None if kvalid is None else ea.pack_key_mask(torch.tensor(kvalid, device=dev))
-    o, lse = ea.forward(q, k, v, scale=w.scale, causal=w.causal, key_len=kl, key_bits=kbits)
+    bmask = None
+    if block_density is not None:
+        bm_np = np.random.default_rng(1000).random((-(-N // 128), -(-N // 64))) < block_density
+        bmask = torch.from_numpy(bm_np).to(dev)
+    o, lse = ea.forward(q, k, v, scale=w.scale, causal=w.causal, key_len=kl, key_bits=kbits, block_mask=bmask)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = torch.empty(ea.attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -589,7 +596,9 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None):
     def step():
         # the current stream at call time (a capture stream while recording a graph)
         s = torch.cuda.current_stream(dev).cuda_stream
-        if kl is None and kbits is None:
+        if bmask is not None:
+            ea.attn_bwd_block_sparse(*ptrs, B, H, N, d, w.scale, w.causal, bmask.data_ptr(), s)
+        elif kl is None and kbits is None:
             ea.attn_bwd(*ptrs, B, H, N, d, w.scale, w.causal, s)
         else:
             ea.attn_bwd_masked(*ptrs, B, H, N, d, w.scale, w.causal, 0 if kl is None else kl.data_ptr(),
@@ -597,7 +606,10 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None):
 
     wall, kern, per = TIMER["fn"](step, steps, warmup, stream)
     warm_run = WARMUP_RUN["launches"]
-    if kl is None and kvalid is None:
+    if bmask is not None:
+        flops = 2.5 * sparse_flops(w, bm_np)
+        counted = f"10*d per (query, key) pair of the set blocks ({int(bm_np.sum())} of {bm_np.size})"
+    elif kl is None and kvalid is None:
         flops = 10.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
         counted = "10*B*H*N^2*d (x0.5 causal)"
     elif kvalid is None:
@@ -617,7 +629,8 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None):
         "warmup": warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.what}", "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
-                   "scale": w.scale, "key_len": key_len, "key_density": key_density, "flops_counted": counted},
+                   "scale": w.scale, "key_len": key_len, "key_density": key_density,
+                   "block_density": block_density, "flops_counted": counted},
         "pct_of_bf16_peak": round(100.0 * flops / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
         "warmup_launches_run": warm_run,
         "timing": {"ms_mean": round(kern * 1e3, 4), "ms_median": round(median(per) * 1e3, 4),
@@ -748,7 +761,8 @@ def main():
         if args.causal:
             from dataclasses import replace
             w = replace(w, causal=args.causal == "yes")
-        print(json.dumps(bench_backward(w, args.steps, args.warmup, args.key_len, args.key_density)), flush=True)
+        print(json.dumps(bench_backward(w, args.steps, args.warmup, args.key_len, args.key_density,
+                                        args.block_density)), flush=True)
         return
 
     if args.workspace_sweep:
