@@ -2,8 +2,8 @@
 GPU against the fp64 oracle: shapes (lengths near and between tile
 boundaries), causal or not, both key-mask forms (with entries that hide every
 key), packed strided views, fp32 I/O, negative and unusual scales, random
-block-sparse masks, and the backward (with and without valid key
-lengths).  Each
+block-sparse masks, and the backward (plain, after a key mask, after a
+block mask).  Each
 feature has its own tests; these check that they combine.  The cases are
 drawn once from a fixed seed, so every run sees the same list.  Inputs are
 standard normal and scales reach 1 (eight times the workloads'), so rows
@@ -219,3 +219,40 @@ def test_random_block_sparse(case):
                                  block_mask=(m, ea.SPARSE_BLOCK_Q, ea.SPARSE_BLOCK_K))
             assert_bf16_elementwise(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep], o_abs[keep],
                                     f"case {case['i']}")
+
+
+def _sparse_backward_cases(count=12, seed=6073):
+    rng = np.random.default_rng(seed)
+    return [dict(i=i, B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), N=_length(rng) // 2 + 1,
+                 causal=bool(rng.random() < 0.5), density=float(rng.uniform(0.05, 1.0)),
+                 scale=float(0.125 if rng.random() < 0.6 else rng.uniform(-0.4, 0.6)),
+                 seed=int(rng.integers(0, 2**31))) for i in range(count)]
+
+
+@pytest.mark.parametrize("case", _sparse_backward_cases(), ids=lambda c: "sb%02d_N%d%s_d%.2f" % (
+    c["i"], c["N"], "_causal" if c["causal"] else "", c["density"]))
+def test_random_block_sparse_backward(case):
+    """The backward after a block-sparse forward (attn_bwd_block_sparse):
+    random masks at random density, query blocks with no set block
+    included."""
+    from tests.parity import grad_magnitudes_blocks
+    B, H, N = case["B"], case["H"], case["N"]
+    print(f"[fuzz] {case}", flush=True)
+    w = Workload("fuzz_sbwd", B, H, N, 64, "bf16", 1.0, case["scale"], case["causal"], case["seed"], "")
+    q, k, v = make_inputs(w)
+    do = make_inputs(Workload("fuzz_sdo", B, H, N, 64, "bf16", 1.0, case["scale"], case["causal"],
+                              case["seed"] + 1, ""))[0]
+    rng = np.random.default_rng(case["seed"])
+    nbq, nbk = -(-N // ea.SPARSE_BLOCK_Q), -(-N // ea.SPARSE_BLOCK_K)
+    m = rng.random((nbq, nbk)) < case["density"]
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    md = torch.from_numpy(m).to(DEV)
+    o, lse = ea.forward(qd, kd, vd, scale=case["scale"], causal=case["causal"], block_mask=md)
+    grads = ea.backward(qd, kd, vd, o, lse, dod, scale=case["scale"], causal=case["causal"], block_mask=md)
+    torch.cuda.synchronize()
+    bm = (m, ea.SPARSE_BLOCK_Q, ea.SPARSE_BLOCK_K)
+    ref = attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), case["scale"], causal=case["causal"],
+                             block_mask=bm)
+    mags = grad_magnitudes_blocks(q, k, v, do, case["scale"], case["causal"], bm)
+    for name, g, r, mg in zip(("dQ", "dK", "dV"), grads, ref, mags):
+        assert_grad_within(f"{name} case {case['i']}", g, r, mg)
