@@ -272,8 +272,10 @@ struct TileDma {
 // end is exact whatever its accumulators hold).  A workgroup whose keys all
 // lie past the valid length only writes those zeros.  kKeysBlocks: the
 // workgroup visits only the query tiles whose block is set in one of its two
-// key columns of the block mask, every step on the general path, and a wave
-// drops (P = dS = 0) the halves its own column, or the causal mask, hides.
+// key columns of the block mask, pipelined like the others, and a wave drops
+// (P = dS = 0) the tiles its own column, or the causal mask, hides: on the
+// general path by a select, on the pipelined one by reading +inf for the
+// tile's L2 values.
 template <bool kCausal, int kWaves, int kKeys>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
@@ -320,9 +322,13 @@ bwd_dkdv_kernel(BwdArgs a) {
 
   // kKeysBlocks: the 64-query tiles whose query block has either of this
   // workgroup's two key columns set (causal: none before its first key),
-  // compacted into blk_list (wave 0 writes, every wave counts); from here on
-  // a tile index is a position in that list.
+  // compacted into blk_list (wave 0 writes, every wave counts), each entry
+  // the tile with bit 14 + c set when column c of the two is set; from here
+  // on a tile index is a position in that list.  inf_l2 holds +inf in place
+  // of a tile's L2 values: a pipelined step of a wave whose column the tile
+  // does not set reads its L2 there, so its probabilities are exactly 0.
   __shared__ uint16_t blk_list[kKeys == kKeysBlocks ? kMaxBlockTiles : 1];
+  __shared__ __attribute__((aligned(16))) float inf_l2[kKeys == kKeysBlocks ? 64 : 1];
   int n_listed = 0;
   if constexpr (kKeys == kKeysBlocks) {
     static_assert(kRows == 2 * kBlockK, "a workgroup spans two key columns of the block mask");
@@ -331,21 +337,24 @@ bwd_dkdv_kernel(BwdArgs a) {
     const bool c1_in = c0 + 1 < a.mask_cols;
     for (int base = kCausal ? (kb * kRows) / kBwdTile : 0; base < tq_end; base += 64) {
       const int t = base + lane;
-      bool act = false;
+      bool set0 = false, set1 = false;
       if (t < tq_end) {
         const uint8_t* mrow = a.block_mask + (size_t)(t * kBwdTile / kBlockQ) * a.mask_cols;
-        act = mrow[c0] != 0 || (c1_in && mrow[c0 + 1] != 0);
+        set0 = mrow[c0] != 0;
+        set1 = c1_in && mrow[c0 + 1] != 0;
       }
+      const bool act = set0 || set1;
       const uint64_t bal = __ballot(act);
       const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-      if (wave == 0 && act) blk_list[n_listed + below] = (uint16_t)t;
+      if (wave == 0 && act) blk_list[n_listed + below] = (uint16_t)(t | (set0 ? 1 << 14 : 0) | (set1 ? 1 << 15 : 0));
       n_listed += __popcll(bal);
     }
+    if (tid < 64) inf_l2[tid] = INFINITY;
     __syncthreads();
   }
   // the query tile at list position t (kKeysBlocks), else tile t itself
   auto tile_of = [&](int t) -> int {
-    if constexpr (kKeys == kKeysBlocks) return __builtin_amdgcn_readfirstlane((int)blk_list[t]);
+    if constexpr (kKeys == kKeysBlocks) return __builtin_amdgcn_readfirstlane((int)blk_list[t]) & 0x3fff;
     else return t;
   };
 
@@ -376,12 +385,12 @@ bwd_dkdv_kernel(BwdArgs a) {
   // jl) run pipelined, in whole turns of the ring and a last partial one;
   // the rest on the general path again.
   constexpr int kHead = kCausal ? (kWaves + 1) / 2 : 1;
-  const int t_fast_end = kKeys == kKeysBlocks ? 0 : jl >= 2 ? (jl - 2) / 2 + 1 : 0;
+  const int t_fast_end = jl >= 2 ? (jl - 2) / 2 + 1 : 0;
   const Dma dma(qg, dog, n, wave, lane, a.ws + (size_t)bh * 2 * a.n_pad, a.n_pad);
   auto dma_issue = [&](int t, char* sb) { dma.issue(tile_of(t), sb); };
 
   // a step is fast (pipelined, unmasked) when it has a step on each side
-  auto fast = [&](int j) { return kKeys != kKeysBlocks && j >= jf + 1 && j <= jl - 1; };
+  auto fast = [&](int j) { return j >= jf + 1 && j <= jl - 1; };
   // stage of half j (tile j/2; the half's rows start at 32*(j&1))
   auto half_stage = [&](int j) { return stage((j / 2 - t0) % kStages); };
   (void)half_stage;
@@ -395,9 +404,21 @@ bwd_dkdv_kernel(BwdArgs a) {
     const char* b = m + (32 * h + 16 * (i >> 1)) * kRow;
     return lds_read_vt(b + tr.off[0][i & 1], b + tr.off[1][i & 1]);
   };
-  // L2 of registers 4*g4 .. 4*g4+3 (queries 8*g4 + 4*hi + 0..3 of the half)
-  auto l2_group = [&](const char* sb, int h, int g4) -> f32x4 {
-    return *(const f32x4*)(sb + kStatOff + 16 * (8 * h + 2 * g4 + hi));
+  // L2 of registers 4*g4 .. 4*g4+3 (queries 8*g4 + 4*hi + 0..3 of the half);
+  // lb = the stage's L2 values (stage + kStatOff) or inf_l2
+  auto l2_group = [&](const char* lb, int h, int g4) -> f32x4 {
+    return *(const f32x4*)(lb + 16 * (8 * h + 2 * g4 + hi));
+  };
+  // where a pipelined step of this wave reads the L2 values of list position
+  // t held in stage sb: inf_l2 when its column of the block mask is clear
+  auto l2_base = [&](const char* sb, int t) -> const char* {
+    if constexpr (kKeys == kKeysBlocks) {
+      const int e = __builtin_amdgcn_readfirstlane((int)blk_list[min(t, kMaxBlockTiles - 1)]);
+      return (e >> (14 + wave_s / 2)) & 1 ? sb + kStatOff : reinterpret_cast<const char*>(inf_l2);
+    } else {
+      (void)t;
+      return sb + kStatOff;
+    }
   };
   auto nd_block = [&](const char* sb, int h) -> f32x16 {
     f32x16 r;
@@ -447,8 +468,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   // step j+1 is fast, its first four operands and L2 group.  Stages and half
   // indices as for step_fast.
   auto step_general = [&](int j, const char* nb, int hn, const char* cb, int hc, const char* pb, int hp,
-                          const char* nnb, f32x16& s_cur, f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt,
-                          const bf16x8 (&p_prv)[2], const bf16x8 (&ds_prv)[2], bf16x8 (&p_cur)[2],
+                          const char* nnb, const char* ln, f32x16& s_cur, f32x16& dp_cur, f32x16& s_nxt,
+                          f32x16& dp_nxt, const bf16x8 (&p_prv)[2], const bf16x8 (&ds_prv)[2], bf16x8 (&p_cur)[2],
                           bf16x8 (&ds_cur)[2]) __attribute__((always_inline)) {
     if (j + 1 >= jf && j + 1 <= jl) {
       dp_nxt = nd_block(nb, hn);
@@ -480,7 +501,7 @@ bwd_dkdv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 l4 = l2_group(cb, hc, g4);
+        const f32x4 l4 = l2_group(cb + kStatOff, hc, g4);
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
           const int r = 4 * g4 + e;
@@ -500,18 +521,20 @@ bwd_dkdv_kernel(BwdArgs a) {
     if (fast(j + 1)) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) ring[s] = slot_operand(s, nnb, hc, cb, hc);
-      l2n = l2_group(nb, hn, 0);
+      l2n = l2_group(ln, hn, 0);
     }
   };
 
   // Step j on the fast path.  nb/hn: half j+1; cb/hc: half j; pb/hp: half
-  // j-1; nnb: half j+2 (half index hc).  16 MFMA slots; in group g: S(j+1)
+  // j-1; nnb: half j+2 (half index hc); lc, ln: where half j's and half
+  // j+1's L2 values are read (l2_base).  16 MFMA slots; in group g: S(j+1)
   // step g, dV(j-1) step g, dK(j-1) step g, dP(j+1) step g (its accumulator
   // starts at -D).  Vector work on score pair k: FMA in slot 2k, exp2 in slot
   // 2k+1, products and packs in slot 2k+2.
   auto step_fast = [&](const char* nb, int hn, const char* cb, int hc, const char* pb, int hp, const char* nnb,
-                       f32x16& s_cur, f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt, const bf16x8 (&p_prv)[2],
-                       const bf16x8 (&ds_prv)[2], bf16x8 (&p_cur)[2], bf16x8 (&ds_cur)[2]) __attribute__((always_inline)) {
+                       const char* lc, const char* ln, f32x16& s_cur, f32x16& dp_cur, f32x16& s_nxt,
+                       f32x16& dp_nxt, const bf16x8 (&p_prv)[2], const bf16x8 (&ds_prv)[2], bf16x8 (&p_cur)[2],
+                       bf16x8 (&ds_cur)[2]) __attribute__((always_inline)) {
     f32x4 l2g[4];
     l2g[0] = l2n;
     dp_nxt = nd_block(nb, hn);
@@ -538,8 +561,8 @@ bwd_dkdv_kernel(BwdArgs a) {
       // operand of slot s+4 (of the next step, for the last four slots)
       if (s + 4 < 16) ring[s & 3] = slot_operand(s + 4, nb, hn, pb, hp);
       else ring[s & 3] = slot_operand(s - 12, nnb, hc, cb, hc);
-      if (s == 1 || s == 5 || s == 9) l2g[(s + 3) >> 2] = l2_group(cb, hc, (s + 3) >> 2);
-      if (s == 13) l2n = l2_group(nb, hn, 0);
+      if (s == 1 || s == 5 || s == 9) l2g[(s + 3) >> 2] = l2_group(lc, hc, (s + 3) >> 2);
+      if (s == 13) l2n = l2_group(ln, hn, 0);
       const int k = s >> 1;
       if ((s & 1) == 0) {
         t[2 * k] = __builtin_fmaf(s_cur[2 * k], c, -l2g[k >> 1][2 * (k & 1)]);
@@ -565,16 +588,18 @@ bwd_dkdv_kernel(BwdArgs a) {
   auto tile = [&](int t, auto st_tag, auto fast_tag) __attribute__((always_inline)) {
     constexpr int st = decltype(st_tag)::value;
     constexpr int sp = (st + kStages - 1) % kStages, sn = (st + 1) % kStages;
+    const char* lt = l2_base(stage(st), t);       // L2 of tile t
+    const char* lt1 = l2_base(stage(sn), t + 1);  // L2 of tile t+1
     if constexpr (decltype(fast_tag)::value) {
       // step 2t: j+1 = (t, 1), j = (t, 0), j-1 = (t-1, 1), j+2 = (t+1, 0)
-      step_fast(stage(st), 1, stage(st), 0, stage(sp), 1, stage(sn), sA, dpA, sB, dpB, pB, dsB, pA, dsA);
+      step_fast(stage(st), 1, stage(st), 0, stage(sp), 1, stage(sn), lt, lt, sA, dpA, sB, dpB, pB, dsB, pA, dsA);
       // step 2t+1: j+1 = (t+1, 0), j = (t, 1), j-1 = (t, 0), j+2 = (t+1, 1)
-      step_fast(stage(sn), 0, stage(st), 1, stage(st), 0, stage(sn), sB, dpB, sA, dpA, pA, dsA, pB, dsB);
+      step_fast(stage(sn), 0, stage(st), 1, stage(st), 0, stage(sn), lt, lt1, sB, dpB, sA, dpA, pA, dsA, pB, dsB);
     } else {
-      step_general(2 * t, stage(st), 1, stage(st), 0, stage(sp), 1, stage(sn), sA, dpA, sB, dpB, pB, dsB, pA,
-                   dsA);
-      step_general(2 * t + 1, stage(sn), 0, stage(st), 1, stage(st), 0, stage(sn), sB, dpB, sA, dpA, pA, dsA,
-                   pB, dsB);
+      step_general(2 * t, stage(st), 1, stage(st), 0, stage(sp), 1, stage(sn), lt, sA, dpA, sB, dpB, pB, dsB,
+                   pA, dsA);
+      step_general(2 * t + 1, stage(sn), 0, stage(st), 1, stage(st), 0, stage(sn), lt1, sB, dpB, sA, dpA, pA,
+                   dsA, pB, dsB);
     }
     vm_wait_barrier_tiles<Dma::kPerTile, kStages - 4>(
         max(0, min(min(t_end - 1, t + kStages - 2) - (t + 2), kStages - 4)));
@@ -589,8 +614,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   for (int i = 0; i < kStages - 1; ++i)
     if (t0 + i < t_end) dma_issue(t0 + i, stage(i));
   vm_wait_barrier_tiles<Dma::kPerTile, kStages - 3>(max(0, min(t_end - t0, kStages - 1) - 2));
-  step_general(2 * t0 - 1, stage(0), 0, stage(kStages - 1), 1, stage(kStages - 1), 0, stage(0), sB, dpB, sA, dpA,
-               pA, dsA, pB, dsB);
+  step_general(2 * t0 - 1, stage(0), 0, stage(kStages - 1), 1, stage(kStages - 1), 0, stage(0),
+               l2_base(stage(0), t0), sB, dpB, sA, dpA, pA, dsA, pB, dsB);
   // ---- head, body (whole turns of the ring), tail
   Unroll<0, kHead>::run([&](auto i) {
     if (t0 + decltype(i)::value < t_end) tile(t0 + decltype(i)::value, i, kGeneral());
@@ -663,8 +688,10 @@ bwd_dkdv_kernel(BwdArgs a) {
 // step runs on the general path, which also drops the keys whose bit is
 // clear (one mask word per 32-key half, a select per score).  kKeysBlocks:
 // the workgroup (one 128-query block) visits only the key tiles its row of
-// the block mask sets, every step on the general path; the ring is one
-// stage shorter so that two workgroups with their tile lists share a CU.
+// the block mask sets, pipelined like the others (no mask is needed away
+// from the causal diagonal and a ragged last tile, which are the last
+// listed); the ring is one stage shorter so that two workgroups with their
+// tile lists share a CU.
 template <bool kCausal, int kWaves, int kKeys>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a) {
@@ -766,9 +793,11 @@ bwd_dq_kernel(BwdArgs a) {
   // kKeysBlocks: the key tiles below kv_end that this query block's row of
   // the block mask sets, compacted into blk_list (wave 0 writes, every wave
   // counts); from here on a tile index is a position in that list, and each
-  // wave masks its halves by their real key offsets.
+  // wave masks its general-path halves by their real key offsets.  Causal:
+  // n_before counts the listed tiles that end before the workgroup's first
+  // query (a prefix of the list), which no wave needs to mask.
   __shared__ uint16_t blk_list[kKeys == kKeysBlocks ? kMaxBlockTiles : 1];
-  int n_listed = 0;
+  int n_listed = 0, n_before = 0;
   if constexpr (kKeys == kKeysBlocks) {
     static_assert(kRows == kBlockQ, "a workgroup is one query block of the block mask");
     const int kt_end = (kv_end + kBwdTile - 1) / kBwdTile;
@@ -780,7 +809,9 @@ bwd_dq_kernel(BwdArgs a) {
       const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
       if (wave == 0 && act) blk_list[n_listed + below] = (uint16_t)kt;
       n_listed += __popcll(bal);
+      n_before += __popcll(__ballot(act && (kt + 1) * kBwdTile <= qb * kRows));
     }
+    if constexpr (!kCausal) n_before = n_listed;
     __syncthreads();
   }
   auto tile_of = [&](int t) -> int {
@@ -790,15 +821,21 @@ bwd_dq_kernel(BwdArgs a) {
   const int t_end = kKeys == kKeysBlocks ? n_listed : (kv_end + kBwdTile - 1) / kBwdTile;
   const int jl = kCausal && kKeys != kKeysBlocks ? min(q0w / 32, 2 * t_end - 1) : 2 * t_end - 1;
   // Tile 0 runs on the general path; then tiles whose two steps are fast in
-  // every wave (2t+1 < the first wave's jl), in whole turns of the ring; the
-  // rest on the general path again.
+  // every wave (2t+1 < the first wave's jl; kKeysBlocks: listed tiles that
+  // need no mask, all but the last), in whole turns of the ring; the rest on
+  // the general path again.
   constexpr int kHead = 1;
   const int jl_min = kCausal ? min(qb * kWaves, 2 * t_end - 1) : 2 * t_end - 1;
-  const int t_fast_end = kKeys == kKeysBits || kKeys == kKeysBlocks ? 0 : jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
+  const int t_fast_end = kKeys == kKeysBits ? 0
+                         : kKeys == kKeysBlocks ? max(0, min(n_before, t_end - 1))
+                         : jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
   const Dma dma(kg, vg, n, wave, lane, nullptr, 0);
   auto dma_issue = [&](int t, char* sb) { dma.issue(tile_of(t), sb); };
 
-  auto fast = [&](int j) { return kKeys != kKeysBits && kKeys != kKeysBlocks && j >= 1 && j <= jl - 1; };
+  auto fast = [&](int j) {
+    if constexpr (kKeys == kKeysBlocks) return j >= 1 && j < 2 * t_fast_end;
+    else return kKeys != kKeysBits && j >= 1 && j <= jl - 1;
+  };
   auto half_stage = [&](int j) { return stage((j / 2) % kStages); };
   auto k_row = [&](const char* sb, int h, int ks) { return lds_read_b128(sb, h * 32 * kRow + row_off[ks]); };
   auto v_row = [&](const char* sb, int h, int ks) {

@@ -353,9 +353,12 @@ attn_status attn_bwd_masked(const void *q, const void *k, const void *v,
  *                as attn_fwd_block_sparse (one M for every batch entry and
  *                head; query block i / 128, key block j / 64).
  * Work follows M: the dQ kernel visits only the key tiles its query block's
- * row sets, the dK/dV kernel only the query tiles whose blocks set its key
- * columns; both run every step on their general path (no pipelined fast
- * path), so a dense M costs more than attn_bwd.  Other arguments and errors
+ * row sets, the dK/dV kernel (128 keys, two columns of M) the query tiles
+ * whose blocks set either of its columns; both pipeline the listed tiles as
+ * attn_bwd does, so an all-ones M costs about what attn_bwd does.  A key
+ * whose own block of a listed tile is 0 takes probability exactly 0 there
+ * (exp2 of -inf), so a NaN in that tile's Q rows still reaches its dK and
+ * dV (NaN - inf is NaN).  Other arguments and errors
  * as attn_bwd, plus ATTN_E_INVALID for a NULL block_mask or N > 262144.
  */
 attn_status attn_bwd_block_sparse(const void *q, const void *k, const void *v,

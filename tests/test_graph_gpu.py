@@ -22,17 +22,21 @@ def _inputs(N, seed, causal):
     return q, k, v, do
 
 
-@pytest.mark.parametrize("masked", ["none", "len", "bits"])
+@pytest.mark.parametrize("masked", ["none", "len", "bits", "blocks"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_and_backward_replay_in_a_graph(causal, masked):
     """masked: both passes with valid key lengths (one entry cut inside a
-    tile) or with a random key bit mask (attn_fwd_masked, attn_bwd_masked)."""
+    tile), a random key bit mask (attn_fwd_masked, attn_bwd_masked), or a
+    random block mask (attn_fwd_block_sparse, attn_bwd_block_sparse)."""
     q, k, v, do = _inputs(777, 9500 + causal, causal)
     masks = {}
     if masked == "len":
         masks["key_len"] = torch.tensor([777, 300], dtype=torch.int32, device=DEV)
     elif masked == "bits":
         masks["key_bits"] = ea.pack_key_mask(torch.rand(2, 777, device=DEV) < 0.6)
+    elif masked == "blocks":
+        masks["block_mask"] = torch.rand(-(-777 // ea.SPARSE_BLOCK_Q), -(-777 // ea.SPARSE_BLOCK_K),
+                                         device=DEV) < 0.5
     # eager results (also warms the library's per-device state up before capture)
     o_ref, lse_ref = ea.forward(q, k, v, scale=0.125, causal=causal, **masks)
     g_ref = ea.backward(q, k, v, o_ref, lse_ref, do, scale=0.125, causal=causal, **masks)
