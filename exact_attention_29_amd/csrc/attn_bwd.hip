@@ -161,6 +161,19 @@ __device__ __forceinline__ unsigned pack_bf16(float x, float y) {
   return __builtin_bit_cast(unsigned, p);
 }
 
+// x where bit kb (lanes 0-31) or bit kb + 4 (lanes 32-63) of the uniform
+// word w is set, else 0: the two bits as a lane mask in an SGPR pair (scalar
+// work; kb is a constant once unrolled, 0 <= kb <= 27) and one v_cndmask_b32
+// (the compiler would test the bit per lane).
+__device__ __forceinline__ float keep_bit(float x, uint32_t w, int kb) {
+  const uint32_t lo = (uint32_t)((int)(w << (31 - kb)) >> 31);
+  const uint32_t hi = (uint32_t)((int)(w << (27 - kb)) >> 31);
+  const uint64_t m = (uint64_t)lo | ((uint64_t)hi << 32);
+  float r;
+  asm("v_cndmask_b32 %0, 0, %1, %2" : "=v"(r) : "v"(x), "s"(m));
+  return r;
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -684,9 +697,10 @@ bwd_dkdv_kernel(BwdArgs a) {
 
 // kKeys: with kKeysLen / kKeysBits only the keys below the batch entry's
 // valid length are visited (the half holding the last one masked per
-// element), and an entry with no valid key gets dQ = 0; with kKeysBits every
-// step runs on the general path, which also drops the keys whose bit is
-// clear (one mask word per 32-key half, a select per score).  kKeysBlocks:
+// element), and an entry with no valid key gets dQ = 0; with kKeysBits the
+// keys whose bit is clear are dropped too (one mask word per 32-key half, a
+// select per probability: on the pipelined path with the lane mask formed by
+// scalar instructions from the word that came with the tile).  kKeysBlocks:
 // the workgroup (one 128-query block) visits only the key tiles its row of
 // the block mask sets, pipelined like the others (no mask is needed away
 // from the causal diagonal and a ragged last tile, which are the last
@@ -826,15 +840,32 @@ bwd_dq_kernel(BwdArgs a) {
   // the general path again.
   constexpr int kHead = 1;
   const int jl_min = kCausal ? min(qb * kWaves, 2 * t_end - 1) : 2 * t_end - 1;
-  const int t_fast_end = kKeys == kKeysBits ? 0
-                         : kKeys == kKeysBlocks ? max(0, min(n_before, t_end - 1))
+  const int t_fast_end = kKeys == kKeysBlocks ? max(0, min(n_before, t_end - 1))
                          : jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
   const Dma dma(kg, vg, n, wave, lane, nullptr, 0);
   auto dma_issue = [&](int t, char* sb) { dma.issue(tile_of(t), sb); };
+  // kKeysBits: the two mask words of the tile in each stage (keys 64t ..
+  // 64t+63), loaded beside its DMA by every wave in one 8-byte load (one
+  // more load per tile in the waits' count, which must match exactly; words
+  // past the entry's row read 0)
+  uint32_t kw0[kStages], kw1[kStages];
+  constexpr int kPerTile = Dma::kPerTile + (kKeys == kKeysBits ? 1 : 0);
+  auto words_issue = [&](int t, auto st_tag) {
+    if constexpr (kKeys == kKeysBits) {
+      constexpr int st = decltype(st_tag)::value;
+      const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.key_bits + (size_t)(bh / a.heads) * a.words), (short)0, a.words * 4, kBufferWord3);
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rw, 8 * t, 0, 0);
+      kw0[st] = w[0];
+      kw1[st] = w[1];
+    } else {
+      (void)t;
+    }
+  };
 
   auto fast = [&](int j) {
     if constexpr (kKeys == kKeysBlocks) return j >= 1 && j < 2 * t_fast_end;
-    else return kKeys != kKeysBits && j >= 1 && j <= jl - 1;
+    else return j >= 1 && j <= jl - 1;
   };
   auto half_stage = [&](int j) { return stage((j / 2) % kStages); };
   auto k_row = [&](const char* sb, int h, int ks) { return lds_read_b128(sb, h * 32 * kRow + row_off[ks]); };
@@ -928,13 +959,15 @@ bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  // Step j on the fast path (arguments as in the dK/dV kernel).  12 MFMA
-  // slots; in group g: S(j+1) step g, dQ(j-1) step g, dP(j+1) step g.
-  // Vector work on score pair k: FMA in slot a_k, exp2 in a_k + 1, product
-  // and pack in a_k + 2, with a_k = 0, 1, 3, 4, 6, 7, 9, 10.
+  // Step j on the fast path (arguments as in the dK/dV kernel; kw: half j's
+  // mask word, kKeysBits).  12 MFMA slots; in group g: S(j+1) step g, dQ(j-1)
+  // step g, dP(j+1) step g.  Vector work on score pair k: FMA in slot a_k,
+  // exp2 in a_k + 1, (mask,) product and pack in a_k + 2, with a_k = 0, 1,
+  // 3, 4, 6, 7, 9, 10.
   auto step_fast = [&](const char* nb, int hn, const char* cb, int hc, const char* pb, int hp, const char* nnb,
                        f32x16& s_cur, f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt, const bf16x8 (&ds_prv)[2],
-                       bf16x8 (&ds_cur)[2]) __attribute__((always_inline)) {
+                       bf16x8 (&ds_cur)[2], uint32_t kw) __attribute__((always_inline)) {
+    (void)kw;
     float t[16], e[16];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -953,6 +986,10 @@ bwd_dq_kernel(BwdArgs a) {
       for (int k = 0; k < 8; ++k) {
         const int r = 2 * k, a_k = k + (k >> 1);
         if (a_k + 2 == s) {
+          if constexpr (kKeys == kKeysBits) {  // keys k0 + 8*(r/4) + 4*hi + r%4 (+1)
+            e[r] = keep_bit(e[r], kw, 8 * (r >> 2) + (r & 3));
+            e[r + 1] = keep_bit(e[r + 1], kw, 8 * (r >> 2) + (r & 3) + 1);
+          }
           unsigned dw = pack_bf16(e[r] * dp_cur[r], e[r + 1] * dp_cur[r + 1]);
           pin(dw);
           set_word(ds_cur[r >> 3], (r & 7) >> 1, dw);
@@ -978,24 +1015,41 @@ bwd_dq_kernel(BwdArgs a) {
     constexpr int st = decltype(st_tag)::value;
     constexpr int sp = (st + kStages - 1) % kStages, sn = (st + 1) % kStages;
     if constexpr (decltype(fast_tag)::value) {
-      step_fast(stage(st), 1, stage(st), 0, stage(sp), 1, stage(sn), sA, dpA, sB, dpB, dsB, dsA);
-      step_fast(stage(sn), 0, stage(st), 1, stage(st), 0, stage(sn), sB, dpB, sA, dpA, dsA, dsB);
+      uint32_t w0 = 0, w1 = 0;  // the mask words of halves 2t, 2t+1
+      if constexpr (kKeys == kKeysBits) {
+        w0 = __builtin_amdgcn_readfirstlane(kw0[st]);
+        w1 = __builtin_amdgcn_readfirstlane(kw1[st]);
+      }
+      step_fast(stage(st), 1, stage(st), 0, stage(sp), 1, stage(sn), sA, dpA, sB, dpB, dsB, dsA, w0);
+      step_fast(stage(sn), 0, stage(st), 1, stage(st), 0, stage(sn), sB, dpB, sA, dpA, dsA, dsB, w1);
     } else {
       step_general(2 * t, stage(st), 1, stage(st), 0, stage(sp), 1, stage(sn), sA, dpA, sB, dpB, dsB, dsA);
       step_general(2 * t + 1, stage(sn), 0, stage(st), 1, stage(st), 0, stage(sn), sB, dpB, sA, dpA, dsA, dsB);
     }
-    vm_wait_barrier_tiles<Dma::kPerTile, kStages - 4>(
+    vm_wait_barrier_tiles<kPerTile, kStages - 4>(
         max(0, min(min(t_end - 1, t + kStages - 2) - (t + 2), kStages - 4)));
-    if (t + kStages - 1 < t_end) dma_issue(t + kStages - 1, stage(sp));
+    if (t + kStages - 1 < t_end) {
+      dma_issue(t + kStages - 1, stage(sp));
+      words_issue(t + kStages - 1, std::integral_constant<int, sp>());
+    }
   };
   using kGeneral = std::false_type;
   using kFast = std::true_type;
 
   // ---- prologue
+  if constexpr (kKeys == kKeysBits) {
+    Unroll<0, kStages - 1>::run([&](auto i) {
+      if (decltype(i)::value < t_end) {
+        dma_issue(decltype(i)::value, stage(decltype(i)::value));
+        words_issue(decltype(i)::value, i);
+      }
+    });
+  } else {
 #pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
-    if (i < t_end) dma_issue(i, stage(i));
-  vm_wait_barrier_tiles<Dma::kPerTile, kStages - 3>(max(0, min(t_end, kStages - 1) - 2));
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < t_end) dma_issue(i, stage(i));
+  }
+  vm_wait_barrier_tiles<kPerTile, kStages - 3>(max(0, min(t_end, kStages - 1) - 2));
   step_general(-1, stage(0), 0, stage(kStages - 1), 1, stage(kStages - 1), 0, stage(0), sB, dpB, sA, dpA, dsA,
                dsB);
   // ---- head, body (whole turns of the ring), tail

@@ -329,9 +329,10 @@ attn_status attn_bwd(const void *q, const void *k, const void *v,
  *   key_bits : const unsigned [B][ceil(N/32)] device array or NULL, as
  *              attn_fwd_masked (bit j%32 of word j/32 clear hides key j);
  *              both NULL is exactly attn_bwd.
- * O and LSE must come from the forward with the same masks.  With key_bits
- * the dQ kernel runs without its pipelined fast path (a select per score
- * on every step), so bit masks cost more than lengths.  Other arguments,
+ * O and LSE must come from the forward with the same masks.  Lengths skip
+ * the hidden keys' work; bits compute it and drop it (a select per
+ * probability), so a bit mask costs a little more than no mask at any
+ * density.  Other arguments,
  * layout, ownership, workspace and errors as attn_bwd (ATTN_E_ALIGN also
  * for a key_len or key_bits not 4-byte aligned).
  */
