@@ -108,11 +108,12 @@ def _delta_from_output(do, o):
     return (do * o).sum(axis=1)
 
 
-def _probability_columns(q, k_cols, lse, scale, causal, cols, cols_valid=None):
+def _probability_columns(q, k_cols, lse, scale, causal, cols, cols_valid=None, block_mask=None):
     """P [N, C] at key columns `cols` of one head: exp(S_ij - LSE_i) over
     every query i, with LSE_i the row's log-sum-exp of scaled, masked
     scores (so the column needs no other key).  cols_valid: bool [C] or
-    None, False for a column hidden by the key mask (all 0); a query that
+    None, False for a column hidden by the key mask (all 0); block_mask:
+    (M, bq, bk) or None, a pair whose block of M is 0 gives 0; a query that
     sees the column has a finite LSE."""
     s = fp64._scores(q, k_cols, scale)
     vis = np.ones(s.shape, dtype=bool)
@@ -120,11 +121,13 @@ def _probability_columns(q, k_cols, lse, scale, causal, cols, cols_valid=None):
         vis &= cols[None, :] <= np.arange(q.shape[0])[:, None]
     if cols_valid is not None:
         vis &= np.asarray(cols_valid, dtype=bool)[None, :]
+    if block_mask is not None:
+        vis &= fp64._block_visible(np.arange(q.shape[0]), k_cols.shape[0], block_mask, keys=cols)
     with np.errstate(over="ignore", invalid="ignore"):
         return np.where(vis, np.exp(np.where(vis, s, 0.0) - np.where(vis, lse[:, None], 0.0)), 0.0)
 
 
-def attention_backward_sampled(q, k, v, do, scale, causal, rows, keys, key_valid=None):
+def attention_backward_sampled(q, k, v, do, scale, causal, rows, keys, key_valid=None, block_mask=None):
     """dQ at query rows `rows` and dK, dV at key rows `keys` (float64,
     [B, H, len(rows), d] and [B, H, len(keys), d]): the gradients of
     ``attention_backward`` for a sample of their rows, at sizes where the
@@ -132,7 +135,8 @@ def attention_backward_sampled(q, k, v, do, scale, causal, rows, keys, key_valid
     P and dP (and D_i); row j of dK and dV needs column j of P and dP, and D
     for every query.  O and LSE of every query come from the forward oracle,
     so column j of P is exp(S_ij - LSE_i) and D_i = sum_f dO_if O_if.
-    key_valid: optional bool [B, N] key mask, as in ``attention_backward``."""
+    key_valid: optional bool [B, N] key mask and block_mask: optional (M,
+    bq, bk) block mask, as in ``attention_backward``."""
     q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
     kv = None if key_valid is None else np.asarray(key_valid, dtype=bool)
     rows = np.asarray(rows, dtype=np.int64)
@@ -145,13 +149,13 @@ def attention_backward_sampled(q, k, v, do, scale, causal, rows, keys, key_valid
             qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
             kvb = None if kv is None else kv[b]
             o, lse = fp64.attention(qh[None, None], kh[None, None], vh[None, None], scale, causal=causal,
-                                    key_valid=None if kvb is None else kvb[None])
+                                    key_valid=None if kvb is None else kvb[None], block_mask=block_mask)
             delta = _delta_from_output(doh, o[0, 0])
-            p_r = _probabilities(qh, kh, scale, causal, rows, kvb)
+            p_r = _probabilities(qh, kh, scale, causal, rows, kvb, block_mask)
             ds_r = _ds(p_r, _dp(doh[rows], vh), delta[rows])
             dq[b, h] = _dq(ds_r, kh, scale)
             p_c = _probability_columns(qh, kh[keys], lse[0, 0], scale, causal, keys,
-                                       None if kvb is None else kvb[keys])
+                                       None if kvb is None else kvb[keys], block_mask)
             ds_c = _ds(p_c, _dp(doh, vh[keys]), delta)
             dv[b, h] = _dv(p_c, doh)
             dk[b, h] = _dk(ds_c, qh, scale)

@@ -74,10 +74,12 @@ def _visible(rows, n_keys, causal, key_valid):
     return vis
 
 
-def _block_visible(rows, n_keys, block_mask):
-    """bool [R, N]: M[i // bq][j // bk] for query rows[r] and key j."""
+def _block_visible(rows, n_keys, block_mask, keys=None):
+    """bool [R, N]: M[i // bq][j // bk] for query rows[r] and key j (or,
+    given ``keys``, bool [R, len(keys)] for those keys only)."""
     m, bq, bk = block_mask
-    return np.asarray(m, dtype=bool)[rows[:, None] // bq, np.arange(n_keys)[None, :] // bk]
+    cols = np.arange(n_keys) if keys is None else np.asarray(keys)
+    return np.asarray(m, dtype=bool)[rows[:, None] // bq, cols[None, :] // bk]
 
 
 def _row_max(s):

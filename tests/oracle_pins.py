@@ -339,8 +339,9 @@ def pin_row_sampling():
 def pin_backward_row_sampling():
     """The sampled gradients (dQ at some query rows, dK and dV at some keys,
     from the forward oracle's O and LSE) are those rows of the full backward
-    oracle, for ragged, causal and single-key shapes, and under key-padding
-    masks (hidden sampled keys, an entry with no valid key)."""
+    oracle, for ragged, causal and single-key shapes, under key-padding
+    masks (hidden sampled keys, an entry with no valid key) and under block
+    masks (a query block and a key block with no set block)."""
     from oracle.backward import attention_backward, attention_backward_sampled
     rng = _rng(13)
     for n, causal, masked in ((70, False, False), (70, True, False), (37, True, False), (1, False, False),
@@ -359,6 +360,19 @@ def pin_backward_row_sampling():
         for got, ref, what in ((sq, dq[:, :, rows], "dQ"), (sk, dk[:, :, keys], "dK"),
                                (sv, dv[:, :, keys], "dV")):
             assert np.abs(got - ref).max() <= 1e-12, f"sampled {what} (n={n}, causal={causal}, masked={masked})"
+    for n, causal in ((70, False), (70, True), (45, True)):
+        q, k, v, do = rng.standard_normal((4, 2, 2, n, 8))
+        m = rng.random((-(-n // 16), -(-n // 8))) < 0.5
+        m[1, :] = False  # queries 16..31 see no key
+        m[:, 2] = False  # keys 16..23 are seen by no query
+        bm = (m, 16, 8)
+        rows = np.array(sorted({0, 20, n // 2, n - 1}))
+        keys = np.array(sorted({0, 18, n // 2, n - 1}))
+        dq, dk, dv = attention_backward(q, k, v, do, 0.4, causal=causal, block_mask=bm)
+        sq, sk, sv = attention_backward_sampled(q, k, v, do, 0.4, causal, rows, keys, block_mask=bm)
+        for got, ref, what in ((sq, dq[:, :, rows], "dQ"), (sk, dk[:, :, keys], "dK"),
+                               (sv, dv[:, :, keys], "dV")):
+            assert np.abs(got - ref).max() <= 1e-12, f"sampled {what} (n={n}, causal={causal}, block mask)"
 
 
 def _merge(o1, l1, o2, l2):

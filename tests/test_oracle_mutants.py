@@ -154,18 +154,23 @@ def test_independent_pins_catch_backward_mutant(name, monkeypatch):
 
 # mistakes in the steps only the sampled gradients use, caught by comparing
 # them with the full backward oracle (itself pinned above)
+from oracle.backward import _probability_columns as _ORIGINAL_COLUMNS  # noqa: E402
+
 SAMPLED_MUTANTS = {
     "delta_from_output_dropped": ("_delta_from_output", lambda do, o: np.zeros(do.shape[0])),
     "delta_from_output_values": ("_delta_from_output", lambda do, o: do.sum(axis=1)),
-    "columns_without_lse": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None: (
+    "columns_without_lse": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None, block_mask=None: (
         np.exp(scale * (q @ kc.T)))),
-    "columns_causal_reversed": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None: np.where(
+    "columns_causal_reversed": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None, block_mask=None: np.where(
         (cols[None, :] >= np.arange(q.shape[0])[:, None]) if causal else True,
         np.exp(scale * (q @ kc.T) - lse[:, None]), 0.0)),
-    "columns_ignore_key_mask": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None: (
+    "columns_ignore_key_mask": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None, block_mask=None: (
         np.where((cols[None, :] <= np.arange(q.shape[0])[:, None]) if causal else True,
                  np.exp(scale * (q @ kc.T) - lse[:, None]), 0.0))),
-    "columns_scale_dropped": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None: np.where(
+    "columns_ignore_block_mask": ("_probability_columns",
+                                  lambda q, kc, lse, scale, causal, cols, cols_valid=None, block_mask=None: (
+                                      _ORIGINAL_COLUMNS(q, kc, lse, scale, causal, cols, cols_valid))),
+    "columns_scale_dropped": ("_probability_columns", lambda q, kc, lse, scale, causal, cols, cols_valid=None, block_mask=None: np.where(
         (cols[None, :] <= np.arange(q.shape[0])[:, None]) if causal else True,
         np.exp(q @ kc.T - lse[:, None]), 0.0)),
 }
