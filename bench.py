@@ -382,12 +382,16 @@ def cpu_baseline(w, q, k, v, seconds, o_gpu=None, lse_gpu=None):
 
 def sparse_flops(w, m):
     """Algorithmic flops of a block-sparse call: 4*d per (query, key) pair of
-    every set (128-row, 64-key) block, clipped at N; non-causal only."""
+    every set (128-row, 64-key) block, clipped at N; when causal, only the
+    pairs with key <= query."""
     import numpy as np
     N = w.N
-    rows = np.minimum(128, N - 128 * np.arange(m.shape[0]))
-    keys = np.minimum(64, N - 64 * np.arange(m.shape[1]))
-    pairs = float((m * rows[:, None] * keys[None, :]).sum())
+    i = np.arange(N)
+    k0 = 64 * np.arange(m.shape[1])
+    k1 = np.minimum(k0 + 64, N)
+    lim = (i + 1)[:, None] if w.causal else N
+    seen = np.clip(np.minimum(lim, k1[None, :]) - k0[None, :], 0, None)  # [N, key blocks]
+    pairs = float((seen * np.asarray(m, dtype=bool)[i // 128]).sum())
     return 4.0 * w.B * w.H * pairs * w.d
 
 
@@ -564,8 +568,8 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_densi
     entry's keys (attn_bwd_masked, after the forward with the same masks);
     FLOPs then count the visible (query, key) pairs only: 10*d per pair.
     block_density: a random block mask as in the forward's block-sparse
-    lines (seed 1000; attn_bwd_block_sparse), FLOPs over the set blocks
-    (non-causal)."""
+    lines (seed 1000; attn_bwd_block_sparse), FLOPs over the visible pairs
+    of the set blocks."""
     import numpy as np
     import torch
     import exact_attention_29_amd as ea
@@ -608,7 +612,8 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_densi
     warm_run = WARMUP_RUN["launches"]
     if bmask is not None:
         flops = 2.5 * sparse_flops(w, bm_np)
-        counted = f"10*d per (query, key) pair of the set blocks ({int(bm_np.sum())} of {bm_np.size})"
+        counted = (f"10*d per visible (query, key) pair of the set blocks ({int(bm_np.sum())} of {bm_np.size})"
+                   + (", key <= query" if w.causal else ""))
     elif kl is None and kvalid is None:
         flops = 10.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
         counted = "10*B*H*N^2*d (x0.5 causal)"

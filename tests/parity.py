@@ -134,9 +134,10 @@ def assert_grad_within(name, got, ref, mag):
     assert mx <= GRAD["rel_max"], f"{name}: max error {mx:.3e} of max|ref| > {GRAD['rel_max']}"
 
 
-def grad_magnitudes_sampled(q, k, v, do, scale, causal, rows, keys, key_valid=None):
+def grad_magnitudes_sampled(q, k, v, do, scale, causal, rows, keys, key_valid=None, block_mask=None):
     """grad_magnitudes at query rows `rows` (dQ) and keys `keys` (dK, dV),
-    from rows and columns of P as in the oracle's sampled backward."""
+    from rows and columns of P as in the oracle's sampled backward (key
+    mask and block mask (M, bq, bk) as there)."""
     from oracle import attention
     from oracle import backward as ob
     from workloads import to_f64
@@ -150,13 +151,13 @@ def grad_magnitudes_sampled(q, k, v, do, scale, causal, rows, keys, key_valid=No
             qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
             kvb = None if key_valid is None else np.asarray(key_valid, dtype=bool)[b]
             o, lse = attention(qh[None, None], kh[None, None], vh[None, None], scale, causal=causal,
-                               key_valid=None if kvb is None else kvb[None])
+                               key_valid=None if kvb is None else kvb[None], block_mask=block_mask)
             delta = np.abs(ob._delta_from_output(doh, o[0, 0]))
-            p_r = ob._probabilities(qh, kh, scale, causal, rows, kvb)
+            p_r = ob._probabilities(qh, kh, scale, causal, rows, kvb, block_mask)
             mds_r = p_r * (np.abs(ob._dp(doh[rows], vh)) + delta[rows][:, None])
             mq[b, h] = abs(scale) * (mds_r @ np.abs(kh))
             p_c = ob._probability_columns(qh, kh[keys], lse[0, 0], scale, causal, keys,
-                                          None if kvb is None else kvb[keys])
+                                          None if kvb is None else kvb[keys], block_mask)
             mds_c = p_c * (np.abs(ob._dp(doh, vh[keys])) + delta[:, None])
             mk[b, h] = abs(scale) * (mds_c.T @ np.abs(qh))
             mv[b, h] = p_c.T @ np.abs(doh)

@@ -15,9 +15,9 @@ import pytest
 import torch
 
 import exact_attention_29_amd as ea
-from oracle import attention_backward
-from tests.parity import assert_grad_within, grad_magnitudes_blocks
-from workloads import Workload, make_inputs, to_f64
+from oracle import attention_backward, attention_backward_sampled
+from tests.parity import assert_grad_within, grad_magnitudes_blocks, grad_magnitudes_sampled
+from workloads import WORKLOADS, Workload, block_rows, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -111,3 +111,34 @@ def test_backward_block_sparse_deterministic():
     a = run(q, k, v, do, True, m)
     b = run(q, k, v, do, True, m)
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_block_sparse_patch_3mp_sampled(causal):
+    """The 3 MP patch shape (N = 11,616, one head) under a random block mask
+    at half density with an empty query block and an empty key block, the
+    launch configuration of the block-sparse bench lines: dQ at three random
+    128-row blocks, the empty one and the last; dK and dV at three random
+    128-key workgroups, the one holding the empty key block and the last,
+    against the oracle's gradients there; the empty blocks' gradients are
+    exactly 0."""
+    w = WORKLOADS["patch_3mp"]
+    q, k, v = (t[:, :1].contiguous() for t in make_inputs(w))
+    do = make_inputs(Workload("do", 1, 1, w.N, 64, "bf16", 1.0, w.scale, causal, w.seed + 61, ""))[0]
+    m = random_mask(w.N, 0.5, seed=6300)
+    m[40] = 0          # query rows 5,120 .. 5,247 see no key
+    m[:, 90] = 0       # keys 5,760 .. 5,823 are seen by no query
+    print(f"[case] 3 MP block-sparse causal={causal}", flush=True)
+    dq, dk, dv = run(q, k, v, do, causal, m)
+    rows = np.unique(np.concatenate([block_rows(w.N, 3, seed=85, rows_per_block=128), np.arange(5120, 5248)]))
+    keys = np.unique(np.concatenate([block_rows(w.N, 3, seed=86, rows_per_block=128), np.arange(5760, 5888)]))
+    bm = (m, 128, 64)
+    ref = attention_backward_sampled(to_f64(q), to_f64(k), to_f64(v), to_f64(do), w.scale, causal, rows, keys,
+                                     block_mask=bm)
+    mags = grad_magnitudes_sampled(q, k, v, do, w.scale, causal, rows, keys, block_mask=bm)
+    got = (dq[:, :, rows], dk[:, :, keys], dv[:, :, keys])
+    for name, g, r, mg in zip(("dQ", "dK", "dV"), got, ref, mags):
+        assert_grad_within(f"{name} 3 MP block-sparse causal={causal}", g, r, mg)
+    assert not dq[:, :, 5120:5248].float().any(), "a query block with no key block has dQ = 0"
+    assert not dk[:, :, 5760:5824].float().any() and not dv[:, :, 5760:5824].float().any(), \
+        "a key block no query sees has dK = dV = 0"

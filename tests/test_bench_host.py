@@ -102,3 +102,24 @@ def test_warm_up_lasts_the_minimum_time(monkeypatch):
     bench.warm_up(lambda: calls.append(time.sleep(0.001)), 3)
     assert time.perf_counter() - t0 >= 0.05
     assert bench.WARMUP_RUN["launches"] == len(calls) > 3
+
+
+def test_block_sparse_flop_count():
+    """FLOPs of a block-sparse call: an all-ones mask counts the dense pairs
+    (halved plus the diagonal when causal), an all-zeros mask none, and one
+    set block its own clipped pairs (key <= query when causal)."""
+    import dataclasses
+    import numpy as np
+    w = dataclasses.replace(WORKLOADS["patch_3mp"], B=1, H=1, N=300)
+    wc = dataclasses.replace(w, causal=True)
+    ones = np.ones((3, 5), dtype=bool)
+    assert bench.sparse_flops(w, ones) == 4.0 * 300 * 300 * 64
+    assert bench.sparse_flops(wc, ones) == 4.0 * (300 * 301 // 2) * 64
+    assert bench.sparse_flops(w, np.zeros_like(ones)) == 0.0
+    one = np.zeros_like(ones)
+    one[2, 4] = True  # queries 256..299, keys 256..299
+    assert bench.sparse_flops(w, one) == 4.0 * 44 * 44 * 64
+    assert bench.sparse_flops(wc, one) == 4.0 * (44 * 45 // 2) * 64
+    one = np.zeros_like(ones)
+    one[0, 3] = True  # queries 0..127, keys 192..255: all above the diagonal
+    assert bench.sparse_flops(wc, one) == 0.0
