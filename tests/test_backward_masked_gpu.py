@@ -108,8 +108,10 @@ def _bits(B, n, seed, density=0.7):
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_key_bits(n, causal):
     """A key bit mask (the forward's key_valid, packed): a random pattern,
-    an entry with no valid key, an entry with all keys valid; the dQ kernel
-    then runs every step on its general path."""
+    an entry with no valid key, an entry with all keys valid (n = 300 and
+    1,337 run pipelined dQ steps, which drop hidden keys through a lane
+    mask per register: keys 4 apart in one word go to the two lane
+    halves)."""
     q, k, v, do = inputs(3, 2, n, seed=5600 + n)
     compare_full(q, k, v, do, causal, None, f"bits n={n} causal={causal}", valid=_bits(3, n, 5650 + n))
 
@@ -174,3 +176,38 @@ def test_backward_key_len_patch_3mp_sampled(causal):
     for name, g, r, m in zip(("dQ", "dK", "dV"), got, ref, mags):
         assert_grad_within(f"{name} 3 MP key_len causal={causal}", g, r, m)
     check_exact_zeros(dq, dk, dv, kv, "3 MP")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_key_bits_patch_3mp_sampled(causal):
+    """The 3 MP patch shape (N = 11,616) with two entries of one head under
+    key bit masks: entry 0 with a random tenth of its keys hidden, entry 1
+    with every fourth 32-key word hidden whole and a random half of another
+    word's keys, plus a valid length of 9,000 on entry 1; dQ at three
+    random 128-row blocks plus the last, dK and dV at three random 128-key
+    blocks plus the last and the block around the length, against the
+    oracle's gradients there; hidden keys' dK and dV exactly 0."""
+    w = WORKLOADS["patch_3mp"]
+    q1, k1, v1 = (t[:, :1] for t in make_inputs(w))
+    q, k, v = (torch.cat([t, t.flip(2)], 0).contiguous() for t in (q1, k1, v1))
+    do = make_inputs(Workload("do", 2, 1, w.N, 64, "bf16", 1.0, w.scale, causal, w.seed + 62, ""))[0]
+    rng = np.random.default_rng(5800)
+    valid = np.ones((2, w.N), dtype=bool)
+    valid[0] = rng.random(w.N) >= 0.1
+    words = np.arange(w.N) // 32
+    valid[1] = (words % 4) != 3
+    half = (words % 4) == 1
+    valid[1, half] = rng.random(int(half.sum())) < 0.5
+    lengths = [w.N, 9000]
+    print(f"[case] 3 MP key bits + key_len={lengths} causal={causal}", flush=True)
+    dq, dk, dv = grads_gpu(q, k, v, do, w.scale, causal, lengths, valid)
+    rows = block_rows(w.N, 3, seed=87, rows_per_block=128)
+    keys = np.unique(np.concatenate([block_rows(w.N, 3, seed=88, rows_per_block=128), np.arange(8960, 9088)]))
+    kv = key_valid(lengths, w.N) & valid
+    ref = attention_backward_sampled(to_f64(q), to_f64(k), to_f64(v), to_f64(do), w.scale, causal, rows, keys,
+                                     key_valid=kv)
+    mags = grad_magnitudes_sampled(q, k, v, do, w.scale, causal, rows, keys, key_valid=kv)
+    got = (dq[:, :, rows], dk[:, :, keys], dv[:, :, keys])
+    for name, g, r, m in zip(("dQ", "dK", "dV"), got, ref, mags):
+        assert_grad_within(f"{name} 3 MP key bits causal={causal}", g, r, m)
+    check_exact_zeros(dq, dk, dv, kv, "3 MP bits")
