@@ -10,7 +10,7 @@ to stderr.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--n N]
   python bench.py --sweep FILE   # one JSON line per workload into FILE
   python bench.py --workspace-sweep   # device memory beyond O and LSE vs P, with fits
-  python bench.py --backward [--key-len L | --key-density D | --block-density D]   # dQ, dK, dV instead
+  python bench.py --backward [--key-len L | --key-density D | --block-density D] [--layout packed]   # dQ, dK, dV instead
 
 Besides the contract fields, the line carries per-launch kernel time (mean,
 median, min) from HIP events on the launch stream, a cold-cache variant
@@ -557,7 +557,7 @@ def bench_one(w, steps, warmup, with_cpu, cpu_seconds, cold_launches=0, clock=Fa
     return line
 
 
-def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_density=None):
+def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_density=None, layout="contiguous"):
     """attn_bwd (two kernels: dQ with the per-row terms, then dK/dV) on the workload, inputs and
     the forward's O, LSE resident.  FLOPs: the algorithmic 10*B*H*N^2*d of
     the recomputing backward pass (recompute S, then dV, dP, dQ, dK: five
@@ -569,7 +569,10 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_densi
     FLOPs then count the visible (query, key) pairs only: 10*d per pair.
     block_density: a random block mask as in the forward's block-sparse
     lines (seed 1000; attn_bwd_block_sparse), FLOPs over the visible pairs
-    of the set blocks."""
+    of the set blocks.  layout "packed": q, k, v head views of one packed
+    [B, N, 3*H*d] projection, dO and O token-major [B, N, H, d], and dq,
+    dk, dv written into head views of one packed gradient buffer
+    (attn_bwd_strided)."""
     import numpy as np
     import torch
     import exact_attention_29_amd as ea
@@ -579,6 +582,17 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_densi
     B, H, N, d = w.shape
     q, k, v = (t.to(dev) for t in make_inputs(w))
     do = make_inputs(Workload("do", B, H, N, d, "bf16", 1.0, w.scale, w.causal, w.seed + 50, ""))[0].to(dev)
+    if layout == "packed":
+        if block_density is not None:
+            raise SystemExit("--layout packed takes no --block-density")
+        x = torch.empty(B, N, 3 * H * d, dtype=q.dtype, device=dev)
+        views = [t.view(B, N, H, d).transpose(1, 2) for t in x.chunk(3, dim=-1)]
+        for dst, src in zip(views, (q, k, v)):
+            dst.copy_(src)
+        q, k, v = views
+        do_tok = torch.empty(B, N, H, d, dtype=q.dtype, device=dev)
+        do_tok.transpose(1, 2).copy_(do)
+        do = do_tok.transpose(1, 2)
     kl = None if key_len is None else torch.full((B,), key_len, dtype=torch.int32, device=dev)
     kvalid = None
     if key_density is not None:
@@ -590,8 +604,15 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_densi
     if block_density is not None:
         bm_np = np.random.default_rng(1000).random((-(-N // 128), -(-N // 64))) < block_density
         bmask = torch.from_numpy(bm_np).to(dev)
-    o, lse = ea.forward(q, k, v, scale=w.scale, causal=w.causal, key_len=kl, key_bits=kbits, block_mask=bmask)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    o_tok = torch.empty(B, N, H, d, dtype=q.dtype, device=dev) if layout == "packed" else None
+    o, lse = ea.forward(q, k, v, scale=w.scale, causal=w.causal, key_len=kl, key_bits=kbits, block_mask=bmask,
+                        out=None if o_tok is None else o_tok.transpose(1, 2))
+    if layout == "packed":
+        gx = torch.empty(B, N, 3 * H * d, dtype=q.dtype, device=dev)
+        dq, dk, dv = (t.view(B, N, H, d).transpose(1, 2) for t in gx.chunk(3, dim=-1))
+        layouts = [ea._layout(t) for t in (q, k, v, o, do, dq, dk, dv)]
+    else:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = torch.empty(ea.attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
@@ -602,6 +623,9 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_densi
         s = torch.cuda.current_stream(dev).cuda_stream
         if bmask is not None:
             ea.attn_bwd_block_sparse(*ptrs, B, H, N, d, w.scale, w.causal, bmask.data_ptr(), s)
+        elif layout == "packed":
+            ea.attn_bwd_strided(*ptrs, B, H, N, d, w.scale, w.causal, layouts, 0 if kl is None else kl.data_ptr(),
+                                0 if kbits is None else kbits.data_ptr(), s)
         elif kl is None and kbits is None:
             ea.attn_bwd(*ptrs, B, H, N, d, w.scale, w.causal, s)
         else:
@@ -635,7 +659,7 @@ def bench_backward(w, steps, warmup, key_len=None, key_density=None, block_densi
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.what}", "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "scale": w.scale, "key_len": key_len, "key_density": key_density,
-                   "block_density": block_density, "flops_counted": counted},
+                   "block_density": block_density, "layout": layout, "flops_counted": counted},
         "pct_of_bf16_peak": round(100.0 * flops / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
         "warmup_launches_run": warm_run,
         "timing": {"ms_mean": round(kern * 1e3, 4), "ms_median": round(median(per) * 1e3, 4),
@@ -767,7 +791,7 @@ def main():
             from dataclasses import replace
             w = replace(w, causal=args.causal == "yes")
         print(json.dumps(bench_backward(w, args.steps, args.warmup, args.key_len, args.key_density,
-                                        args.block_density)), flush=True)
+                                        args.block_density, args.layout)), flush=True)
         return
 
     if args.workspace_sweep:

@@ -3,7 +3,7 @@
 The functions ``attn_fwd``, ``attn_fwd_fp32``, ``attn_fwd_masked``,
 ``attn_fwd_fp32_masked``, ``attn_fwd_strided``, ``attn_fwd_split``,
 ``attn_fwd_split_workspace_size``, ``attn_fwd_block_sparse``,
-``attn_bwd``, ``attn_bwd_masked``, ``attn_bwd_block_sparse``, ``attn_bwd_noalloc``,
+``attn_bwd``, ``attn_bwd_masked``, ``attn_bwd_strided``, ``attn_bwd_block_sparse``, ``attn_bwd_noalloc``,
 ``attn_bwd_workspace_size``,
 ``attn_pack_key_mask`` and ``attn_strerror`` carry the names and
 arguments
@@ -21,8 +21,8 @@ import os
 import torch  # imported first: the library then binds to torch's HIP runtime
 
 __all__ = ["attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
-           "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_masked", "attn_bwd_block_sparse", "attn_bwd_noalloc", "attn_bwd_workspace_size",
-           "attn_pack_key_mask", "AttnLayout",
+           "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse", "attn_bwd", "attn_bwd_masked", "attn_bwd_strided", "attn_bwd_block_sparse",
+           "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_pack_key_mask", "AttnLayout",
            "backward", "attn_strerror", "forward", "pack_key_mask", "AttnError",
            "library_path", "load_library", "split_workspace"]
 
@@ -33,7 +33,7 @@ _lib = None
 ATTN_OK, ATTN_E_INVALID, ATTN_E_ALIGN, ATTN_E_DEVICE, ATTN_E_LAUNCH, ATTN_E_SCRATCH = range(6)
 # the static scratch of attn_bwd_noalloc (ATTN_BWD_NOALLOC_SCRATCH_BYTES in attn.h)
 BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
-EXPORTED = ("attn_bwd", "attn_bwd_masked", "attn_bwd_block_sparse", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
+EXPORTED = ("attn_bwd", "attn_bwd_masked", "attn_bwd_strided", "attn_bwd_block_sparse", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp32", "attn_fwd_masked", "attn_fwd_fp32_masked",
             "attn_fwd_strided", "attn_fwd_split", "attn_fwd_split_workspace_size", "attn_fwd_block_sparse",
             "attn_pack_key_mask", "attn_strerror")
 SPARSE_BLOCK_Q, SPARSE_BLOCK_K = 128, 64
@@ -90,6 +90,8 @@ def load_library():
     lib.attn_bwd.restype = i32
     lib.attn_bwd_masked.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr, ptr, ptr]
     lib.attn_bwd_masked.restype = i32
+    lib.attn_bwd_strided.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32] + [lay] * 8 + [ptr, ptr, ptr]
+    lib.attn_bwd_strided.restype = i32
     lib.attn_bwd_block_sparse.argtypes = [ptr] * 10 + [i32, i32, i32, i32, f32, i32, ptr, ptr]
     lib.attn_bwd_block_sparse.restype = i32
     lib.attn_bwd_noalloc.argtypes = [ptr] * 9 + [i32, i32, i32, i32, f32, i32, ptr]
@@ -182,6 +184,16 @@ def attn_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, sc
                                           int(bool(causal)), key_len, key_bits, stream))
 
 
+def attn_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, layouts, key_len,
+                     key_bits, stream):
+    """C entry point attn_bwd_strided: attn_bwd_masked plus the layouts of q,
+    k, v, o, dout, dq, dk, dv (a sequence of eight AttnLayout or None)."""
+    ref = lambda l: None if l is None else ctypes.byref(l)  # noqa: E731
+    _check(load_library().attn_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, float(scale),
+                                           int(bool(causal)), *[ref(l) for l in layouts], key_len, key_bits,
+                                           stream))
+
+
 def attn_bwd_block_sparse(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, block_mask,
                           stream):
     """C entry point attn_bwd_block_sparse: attn_bwd plus the device address
@@ -203,26 +215,33 @@ def attn_bwd_workspace_size(B, H, N):
 
 
 def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None, key_valid=None, key_bits=None,
-             block_mask=None):
+             block_mask=None, dq=None, dk=None, dv=None):
     """dQ, dK, dV (bf16 [B, H, N, d]) of attention for upstream gradient dout,
     from forward's o and lse (same q, k, v, scale, causal and masks).
     Key masks as in forward (int32 [B] key_len, bool [B, N] key_valid packed
     here, or int32 [B, ceil(N/32)] key_bits), through attn_bwd_masked:
     hidden keys get dK = dV = 0.  block_mask as in forward (bool or uint8
     [ceil(N/128), ceil(N/64)], no key mask), through attn_bwd_block_sparse.
-    Contiguous bf16 tensors on one GPU; the workspace
-    (attn_bwd_workspace_size bytes) is allocated here.  Launches on torch's
-    current stream."""
+    bf16 tensors on one GPU; q, k, v, o, dout may be strided views (features
+    contiguous, every stride a multiple of 8 elements), and dq, dk, dv may be
+    given as such views to write into (e.g. head views of a packed
+    projection's gradient); then attn_bwd_strided runs (no block mask).
+    The workspace (attn_bwd_workspace_size bytes) is allocated here.
+    Launches on torch's current stream."""
     ts = (q, k, v, o, dout)
-    if any(t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous() or t.device != q.device
-           for t in ts) or q.dim() != 4 or not q.is_cuda:
-        raise ValueError("q, k, v, o, dout must be contiguous bf16 [B, H, N, d] tensors on one GPU")
+    if any(t.dtype != torch.bfloat16 or t.shape != q.shape or t.device != q.device for t in ts) \
+            or q.dim() != 4 or not q.is_cuda:
+        raise ValueError("q, k, v, o, dout must be bf16 [B, H, N, d] tensors on one GPU")
     B, H, N, d = q.shape
     if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dq, dk, dv = (torch.empty_like(q, memory_format=torch.contiguous_format) if g is None else g
+                  for g in (dq, dk, dv))
+    if any(g.dtype != torch.bfloat16 or g.shape != q.shape or g.device != q.device for g in (dq, dk, dv)):
+        raise ValueError("dq, dk, dv must be bf16 [B, H, N, d] tensors like q")
+    strided = not all(t.is_contiguous() for t in (*ts, dq, dk, dv))
     if B * H * N == 0 and d == 64:
         return dq, dk, dv  # nothing to compute (the C entry points take B, H, N >= 1)
     if key_len is not None and (key_len.dtype != torch.int32 or key_len.shape != (B,)
@@ -242,14 +261,18 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, key_len=None, key_
         if block_mask.dtype not in (torch.bool, torch.uint8) or block_mask.shape != (nbq, nbk) \
                 or not block_mask.is_contiguous() or block_mask.device != q.device:
             raise ValueError(f"block_mask must be a contiguous bool or uint8 [{nbq}, {nbk}] tensor on q's device")
-        if key_len is not None or key_bits is not None:
-            raise ValueError("block_mask takes no key mask")
+        if key_len is not None or key_bits is not None or strided:
+            raise ValueError("block_mask takes contiguous tensors and no key mask")
     ws = torch.empty(attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
     with torch.cuda.device(q.device):
         if block_mask is not None:
             attn_bwd_block_sparse(*ptrs, B, H, N, d, scale, causal, block_mask.data_ptr(), _stream_handle(q.device))
+        elif strided:
+            attn_bwd_strided(*ptrs, B, H, N, d, scale, causal, [_layout(t) for t in (*ts, dq, dk, dv)],
+                             0 if key_len is None else key_len.data_ptr(),
+                             0 if key_bits is None else key_bits.data_ptr(), _stream_handle(q.device))
         elif key_len is None and key_bits is None:
             attn_bwd(*ptrs, B, H, N, d, scale, causal, _stream_handle(q.device))
         else:
@@ -319,7 +342,7 @@ def _layout(t):
     """AttnLayout of a [B, H, N, d] tensor view with contiguous features."""
     sb, sh, sn, sf = t.stride()
     if sf != 1:
-        raise ValueError("the d features of q, k, v and out must be contiguous (stride 1)")
+        raise ValueError("the d features of every tensor must be contiguous (stride 1)")
     return AttnLayout(sb, sh, sn)
 
 

@@ -82,7 +82,35 @@ struct BwdArgs {
   int words;                 // ceil(n / 32)
   const uint8_t* block_mask;  // block-sparse: [ceil(n/128)][mask_cols], 0 hides that block
   int mask_cols;              // ceil(n / 64)
+  // strided instances: element strides (batch, head, row) of q, k, v, o,
+  // dout, dq, dk, dv (index kTq .. kTdv); the others use [B][H][n][64]
+  long long sb[8];
+  long long sh[8];
+  int sn[8];
 };
+
+constexpr int kTq = 0, kTk = 1, kTv = 2, kTo = 3, kTdo = 4, kTdq = 5, kTdk = 6, kTdv = 7;
+
+// Element offset of head bh's [n][64] matrix in tensor t, and its row stride.
+template <bool kStrided>
+__device__ __forceinline__ size_t head_offset(const BwdArgs& a, int t, int bh) {
+  if constexpr (kStrided) {
+    const int b = bh / a.heads;
+    return (size_t)(b * a.sb[t] + (long long)(bh - b * a.heads) * a.sh[t]);
+  } else {
+    (void)t;
+    return (size_t)bh * a.n * kD;
+  }
+}
+template <bool kStrided>
+__device__ __forceinline__ int row_stride(const BwdArgs& a, int t) {
+  if constexpr (kStrided) return a.sn[t];
+  else {
+    (void)a;
+    (void)t;
+    return kD;
+  }
+}
 
 // Which (query, key) pairs take part, as a kernel template argument: all of
 // them, keys below each entry's valid length, (kKeysBits) keys whose bit is
@@ -114,16 +142,17 @@ __device__ __forceinline__ uint32_t key_word(const BwdArgs& a, int bh, int w) {
   return a.key_bits[(size_t)(bh / a.heads) * a.words + w];
 }
 
-// 16-byte chunk `ch` of row `row` of a [n][64] bf16 matrix, zero past row n.
-__device__ __forceinline__ u32x4 load_chunk(const uint16_t* base, int row, int ch, int n) {
+// 16-byte chunk `ch` of row `row` of a [n][64] bf16 matrix whose rows are
+// `rs` elements apart, zero past row n.
+__device__ __forceinline__ u32x4 load_chunk(const uint16_t* base, int row, int ch, int n, int rs = kD) {
   u32x4 w = {0u, 0u, 0u, 0u};
-  if (row < n) w = *(const u32x4*)(base + (size_t)row * kD + 8 * ch);
+  if (row < n) w = *(const u32x4*)(base + (size_t)row * rs + 8 * ch);
   return w;
 }
 
 // The 8 bf16 of features 16*ks + 8*hi .. +7 of one row, as an MFMA operand.
-__device__ __forceinline__ bf16x8 row_operand(const uint16_t* base, int row, int ks, int hi, int n) {
-  return __builtin_bit_cast(bf16x8, load_chunk(base, row, 2 * ks + hi, n));
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* base, int row, int ks, int hi, int n, int rs = kD) {
+  return __builtin_bit_cast(bf16x8, load_chunk(base, row, 2 * ks + hi, n, rs));
 }
 
 // Per-lane offsets of the transposed-operand reads (two ds_read_b64_tr_b16):
@@ -185,7 +214,7 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // fetches global chunk (l%8) ^ swz(row) of that row (swz depends on row bits
 // 1-3 only: the same chunk in every pass).  Rows past N of the ragged last
 // tile re-read row N-1: finite data whose probability is 0 or masked.
-template <int kWaves, bool kStats>
+template <int kWaves, bool kStats, bool kStr = false>
 struct TileDma {
   static constexpr int kPassRows = 8 * kWaves;
   static constexpr int kPasses = kBwdTile / kPassRows;
@@ -197,17 +226,33 @@ struct TileDma {
   const uint16_t* g0;
   const uint16_t* g1;
   int n, lane, row_in, chunk, lane_off, wave_s, stat_voff;
+  int e0, e1, lane_off1;  // kStr: row strides of the two matrices (elements), matrix 1's lane offset
 
-  // stats: this head's L2[n_pad], then -D[n_pad] (dK/dV only)
+  // stats: this head's L2[n_pad], then -D[n_pad] (dK/dV only).  kStr: the
+  // matrices' rows are rs0, rs1 elements apart (multiples of 8; the byte
+  // offsets up to row n-1 below 2^31, checked on the host), else 64.
   __device__ TileDma(const uint16_t* m0, const uint16_t* m1, int n_, int wave, int lane_, const float* stats,
-                     int n_pad)
+                     int n_pad, int rs0 = kD, int rs1 = kD)
       : g0(m0), g1(m1), n(n_), lane(lane_) {
     row_in = 8 * wave + (lane >> 3);
     chunk = (lane & 7) ^ swz(row_in);
-    lane_off = row_in * kRow + chunk * 16;
     wave_s = __builtin_amdgcn_readfirstlane(wave);
-    r0 = __builtin_amdgcn_make_buffer_rsrc((void*)m0, (short)0, n * kRow, kBufferWord3);
-    r1 = __builtin_amdgcn_make_buffer_rsrc((void*)m1, (short)0, n * kRow, kBufferWord3);
+    if constexpr (kStr) {
+      e0 = rs0;
+      e1 = rs1;
+      lane_off = row_in * 2 * e0 + chunk * 16;
+      lane_off1 = row_in * 2 * e1 + chunk * 16;
+      r0 = __builtin_amdgcn_make_buffer_rsrc((void*)m0, (short)0, (n - 1) * 2 * e0 + kRow, kBufferWord3);
+      r1 = __builtin_amdgcn_make_buffer_rsrc((void*)m1, (short)0, (n - 1) * 2 * e1 + kRow, kBufferWord3);
+    } else {
+      (void)rs0;
+      (void)rs1;
+      e0 = e1 = kD;
+      lane_off = row_in * kRow + chunk * 16;
+      lane_off1 = lane_off;
+      r0 = __builtin_amdgcn_make_buffer_rsrc((void*)m0, (short)0, n * kRow, kBufferWord3);
+      r1 = __builtin_amdgcn_make_buffer_rsrc((void*)m1, (short)0, n * kRow, kBufferWord3);
+    }
     stat_voff = 0;
     if constexpr (kStats) {
       // chunk ci of a tile's stats: L2 in chunks 0-15, -D in chunks 16-31
@@ -224,19 +269,21 @@ struct TileDma {
     if ((t + 1) * kBwdTile <= n) {
 #pragma unroll
       for (int ps = 0; ps < kPasses; ++ps) {
-        const int soff = (t * kBwdTile + ps * kPassRows) * kRow;
+        const int row0 = t * kBwdTile + ps * kPassRows;
+        const int soff = kStr ? row0 * 2 * e0 : row0 * kRow;
+        const int soff1 = kStr ? row0 * 2 * e1 : soff;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, (lds_void*)(d + ps * kPassRows * kRow), 16, lane_off, soff,
                                                  0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (lds_void*)(d + kTileBytes + ps * kPassRows * kRow), 16,
-                                                 lane_off, soff, 0, 0);
+                                                 lane_off1, soff1, 0, 0);
       }
     } else {
 #pragma unroll
       for (int ps = 0; ps < kPasses; ++ps) {
         const int row = min(t * kBwdTile + row_in + ps * kPassRows, n - 1);
-        __builtin_amdgcn_global_load_lds((global_void*)(g0 + (size_t)row * kD + chunk * 8),
+        __builtin_amdgcn_global_load_lds((global_void*)(g0 + (size_t)row * (kStr ? e0 : kD) + chunk * 8),
                                          (lds_void*)(d + ps * kPassRows * kRow), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((global_void*)(g1 + (size_t)row * kD + chunk * 8),
+        __builtin_amdgcn_global_load_lds((global_void*)(g1 + (size_t)row * (kStr ? e1 : kD) + chunk * 8),
                                          (lds_void*)(d + kTileBytes + ps * kPassRows * kRow), 16, 0, 0);
       }
     }
@@ -289,14 +336,14 @@ struct TileDma {
 // (P = dS = 0) the tiles its own column, or the causal mask, hides: on the
 // general path by a select, on the pipelined one by reading +inf for the
 // tile's L2 values.
-template <bool kCausal, int kWaves, int kKeys>
+template <bool kCausal, int kWaves, int kKeys, bool kStrided = false>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdArgs a) {
   constexpr int kStages = kWaves == 8 ? 5 : 4;
   constexpr int kRows = 32 * kWaves;        // keys per workgroup
   constexpr int kStatOff = 2 * kTileBytes;  // L2[64], then -D[64]
   constexpr int kStageBytes = kStatOff + 2 * kBwdTile * 4;
-  using Dma = TileDma<kWaves, true>;
+  using Dma = TileDma<kWaves, true, kStrided>;
   ATTN_BWD_RING(kStageBytes, kStages, stage);
 
   const int n = a.n;
@@ -308,11 +355,10 @@ bwd_dkdv_kernel(BwdArgs a) {
     bh = logical / a.blocks;
     kb = logical - bh * a.blocks;
   }
-  const size_t head = (size_t)bh * n * kD;
-  const uint16_t* qg = a.q + head;
-  const uint16_t* kg = a.k + head;
-  const uint16_t* vg = a.v + head;
-  const uint16_t* dog = a.dout + head;
+  const uint16_t* qg = a.q + head_offset<kStrided>(a, kTq, bh);
+  const uint16_t* kg = a.k + head_offset<kStrided>(a, kTk, bh);
+  const uint16_t* vg = a.v + head_offset<kStrided>(a, kTv, bh);
+  const uint16_t* dog = a.dout + head_offset<kStrided>(a, kTdo, bh);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -325,8 +371,8 @@ bwd_dkdv_kernel(BwdArgs a) {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int f = 32 * hi; f < 32 * hi + 32; f += 8) {
-          *(u32x4*)(a.dk + head + (size_t)key * kD + f) = z;
-          *(u32x4*)(a.dv + head + (size_t)key * kD + f) = z;
+          *(u32x4*)(a.dk + head_offset<kStrided>(a, kTdk, bh) + (size_t)key * row_stride<kStrided>(a, kTdk) + f) = z;
+          *(u32x4*)(a.dv + head_offset<kStrided>(a, kTdv, bh) + (size_t)key * row_stride<kStrided>(a, kTdv) + f) = z;
         }
       }
       return;
@@ -375,8 +421,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   bf16x8 kop[4], vop[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    kop[ks] = row_operand(kg, key, ks, hi, n);
-    vop[ks] = row_operand(vg, key, ks, hi, n);
+    kop[ks] = row_operand(kg, key, ks, hi, n, row_stride<kStrided>(a, kTk));
+    vop[ks] = row_operand(vg, key, ks, hi, n, row_stride<kStrided>(a, kTv));
   }
   const TrOffsets tr(lane);
   int row_off[4];  // row-operand read of step ks: row l32, chunk 2*ks + hi
@@ -399,7 +445,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   // the rest on the general path again.
   constexpr int kHead = kCausal ? (kWaves + 1) / 2 : 1;
   const int t_fast_end = jl >= 2 ? (jl - 2) / 2 + 1 : 0;
-  const Dma dma(qg, dog, n, wave, lane, a.ws + (size_t)bh * 2 * a.n_pad, a.n_pad);
+  const Dma dma(qg, dog, n, wave, lane, a.ws + (size_t)bh * 2 * a.n_pad, a.n_pad, row_stride<kStrided>(a, kTq),
+                row_stride<kStrided>(a, kTdo));
   auto dma_issue = [&](int t, char* sb) { dma.issue(tile_of(t), sb); };
 
   // a step is fast (pipelined, unmasked) when it has a step on each side
@@ -669,8 +716,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int key_e = key0 + (lane_e & 31);
   const int hi_e = lane_e >> 5;
   if (key_e < n) {
-    uint16_t* dkrow = a.dk + head + (size_t)key_e * kD;
-    uint16_t* dvrow = a.dv + head + (size_t)key_e * kD;
+    uint16_t* dkrow = a.dk + head_offset<kStrided>(a, kTdk, bh) + (size_t)key_e * row_stride<kStrided>(a, kTdk);
+    uint16_t* dvrow = a.dv + head_offset<kStrided>(a, kTdv, bh) + (size_t)key_e * row_stride<kStrided>(a, kTdv);
     const float scale = a.scale;
     bool hidden = false;  // a key past the valid length or with a clear bit
     if constexpr (kKeys == kKeysLen || kKeys == kKeysBits) hidden = key_e >= valid_keys<kKeys>(a, bh);
@@ -706,13 +753,13 @@ bwd_dkdv_kernel(BwdArgs a) {
 // from the causal diagonal and a ragged last tile, which are the last
 // listed); the ring is one stage shorter so that two workgroups with their
 // tile lists share a CU.
-template <bool kCausal, int kWaves, int kKeys>
+template <bool kCausal, int kWaves, int kKeys, bool kStrided = false>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(BwdArgs a) {
   constexpr int kStages = kKeys == kKeysBlocks ? 4 : kWaves == 8 ? 6 : 5;
   constexpr int kRows = 32 * kWaves;  // queries per workgroup
   constexpr int kStageBytes = 2 * kTileBytes;
-  using Dma = TileDma<kWaves, false>;
+  using Dma = TileDma<kWaves, false, kStrided>;
   ATTN_BWD_RING(kStageBytes, kStages, stage);
 
   const int n = a.n;
@@ -726,11 +773,10 @@ bwd_dq_kernel(BwdArgs a) {
     bh = logical / a.blocks;
     qb = logical - bh * a.blocks;
   }
-  const size_t head = (size_t)bh * n * kD;
-  const uint16_t* qg = a.q + head;
-  const uint16_t* kg = a.k + head;
-  const uint16_t* vg = a.v + head;
-  const uint16_t* dog = a.dout + head;
+  const uint16_t* qg = a.q + head_offset<kStrided>(a, kTq, bh);
+  const uint16_t* kg = a.k + head_offset<kStrided>(a, kTk, bh);
+  const uint16_t* vg = a.v + head_offset<kStrided>(a, kTv, bh);
+  const uint16_t* dog = a.dout + head_offset<kStrided>(a, kTdo, bh);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -745,7 +791,8 @@ bwd_dq_kernel(BwdArgs a) {
       if (qi < n) {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int f = 32 * hi; f < 32 * hi + 32; f += 8) *(u32x4*)(a.dq + head + (size_t)qi * kD + f) = z;
+        for (int f = 32 * hi; f < 32 * hi + 32; f += 8)
+          *(u32x4*)(a.dq + head_offset<kStrided>(a, kTdq, bh) + (size_t)qi * row_stride<kStrided>(a, kTdq) + f) = z;
       }
       return;
     }
@@ -755,8 +802,8 @@ bwd_dq_kernel(BwdArgs a) {
   bf16x8 qop[4], dop[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    qop[ks] = row_operand(qg, qi, ks, hi, n);
-    dop[ks] = row_operand(dog, qi, ks, hi, n);
+    qop[ks] = row_operand(qg, qi, ks, hi, n, row_stride<kStrided>(a, kTq));
+    dop[ks] = row_operand(dog, qi, ks, hi, n, row_stride<kStrided>(a, kTdo));
   }
   // L2 = LSE * log2(e) and -D = -sum_f dO_f O_f of this lane's query, formed
   // here from the 32 features of dO already in dop and the matching 32 of O
@@ -766,11 +813,11 @@ bwd_dq_kernel(BwdArgs a) {
   float* const hs = a.ws + (size_t)bh * 2 * a.n_pad;  // this head's L2, then -D
   float lse2 = INFINITY, ndl = 0.f;
   {
-    const uint16_t* og = a.o + head;
+    const uint16_t* og = a.o + head_offset<kStrided>(a, kTo, bh);
     float dsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 ow = load_chunk(og, qi, 2 * ks + hi, n);
+      const u32x4 ow = load_chunk(og, qi, 2 * ks + hi, n, row_stride<kStrided>(a, kTo));
       const u32x4 dw = __builtin_bit_cast(u32x4, dop[ks]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -842,7 +889,7 @@ bwd_dq_kernel(BwdArgs a) {
   const int jl_min = kCausal ? min(qb * kWaves, 2 * t_end - 1) : 2 * t_end - 1;
   const int t_fast_end = kKeys == kKeysBlocks ? max(0, min(n_before, t_end - 1))
                          : jl_min >= 2 ? (jl_min - 2) / 2 + 1 : 0;
-  const Dma dma(kg, vg, n, wave, lane, nullptr, 0);
+  const Dma dma(kg, vg, n, wave, lane, nullptr, 0, row_stride<kStrided>(a, kTk), row_stride<kStrided>(a, kTv));
   auto dma_issue = [&](int t, char* sb) { dma.issue(tile_of(t), sb); };
   // kKeysBits: the two mask words of the tile in each stage (keys 64t ..
   // 64t+63), loaded beside its DMA by every wave in one 8-byte load (one
@@ -1080,7 +1127,7 @@ bwd_dq_kernel(BwdArgs a) {
   }
 
   if (qi < n) {
-    uint16_t* row = a.dq + head + (size_t)qi * kD;
+    uint16_t* row = a.dq + head_offset<kStrided>(a, kTdq, bh) + (size_t)qi * row_stride<kStrided>(a, kTdq);
     const float scale = a.scale;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -1150,11 +1197,53 @@ attn_status bwd_validate(const void* q, const void* k, const void* v, const void
   return ATTN_OK;
 }
 
+// Element strides (batch, head, row) of the eight tensors q, k, v, o, dout,
+// dq, dk, dv (NULL layout: the contiguous [B][H][N][64] one), checked: every
+// stride a multiple of 8 elements (16 bytes: the kernels move 16-byte
+// chunks), none negative, a row stride of at most 2^24, the outputs' rows
+// at least 64 apart, and every byte offset the buffer loads of a tile form
+// (q and dout in the dK/dV kernel, k and v in the dQ kernel) below 2^31.
+// Sets *strided when some layout is given.
+attn_status bwd_layouts(const attn_layout* const lay[8], int H, int N, BwdArgs& a, bool* strided) {
+  *strided = false;
+  for (int t = 0; t < 8; ++t) {
+    if (!lay[t]) {
+      a.sn[t] = kD;
+      a.sh[t] = (long long)N * kD;
+      a.sb[t] = (long long)H * N * kD;
+      continue;
+    }
+    *strided = true;
+    const attn_layout& l = *lay[t];
+    if (l.batch < 0 || l.head < 0 || l.row < 0) return ATTN_E_INVALID;
+    if ((l.batch | l.head | l.row) & 7) return ATTN_E_ALIGN;
+    if (l.row > (1LL << 24)) return ATTN_E_INVALID;
+    a.sb[t] = l.batch;
+    a.sh[t] = l.head;
+    a.sn[t] = (int)l.row;
+  }
+  for (int t = kTdq; t <= kTdv; ++t)
+    if (a.sn[t] < kD) return ATTN_E_INVALID;  // an output's rows must not overlap
+  const int dma[4] = {kTq, kTdo, kTk, kTv};
+  for (int t : dma)
+    if ((long long)(N - 1) * 2 * a.sn[t] + kRow >= (1LL << 31)) return ATTN_E_INVALID;
+  return ATTN_OK;
+}
+
 attn_status bwd_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int N,
                        float scale, int causal, const int* key_len, const uint32_t* key_bits,
-                       const uint8_t* block_mask, void* stream) {
+                       const uint8_t* block_mask, void* stream, const BwdArgs* strides = nullptr) {
   BwdArgs a;
+  if (strides) {
+    for (int t = 0; t < 8; ++t) {
+      a.sb[t] = strides->sb[t];
+      a.sh[t] = strides->sh[t];
+      a.sn[t] = strides->sn[t];
+    }
+  } else {
+    for (int t = 0; t < 8; ++t) a.sb[t] = a.sh[t] = a.sn[t] = 0;
+  }
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -1193,6 +1282,32 @@ attn_status bwd_launch(const void* q, const void* k, const void* v, const void* 
     return launch_status(e);
   }
   const int keys = key_bits ? kKeysBits : key_len ? kKeysLen : kKeysAll;
+  if (strides) {  // strided tensors: 4-wave workgroups
+    const void* k_dq;
+    const void* k_dkdv;
+    if (causal) {
+      const void* const t_dq[3] = {reinterpret_cast<const void*>(&bwd_dq_kernel<true, 4, kKeysAll, true>),
+                                   reinterpret_cast<const void*>(&bwd_dq_kernel<true, 4, kKeysLen, true>),
+                                   reinterpret_cast<const void*>(&bwd_dq_kernel<true, 4, kKeysBits, true>)};
+      const void* const t_dkdv[3] = {reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, 4, kKeysAll, true>),
+                                     reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, 4, kKeysLen, true>),
+                                     reinterpret_cast<const void*>(&bwd_dkdv_kernel<true, 4, kKeysBits, true>)};
+      k_dq = t_dq[keys];
+      k_dkdv = t_dkdv[keys];
+    } else {
+      const void* const t_dq[3] = {reinterpret_cast<const void*>(&bwd_dq_kernel<false, 4, kKeysAll, true>),
+                                   reinterpret_cast<const void*>(&bwd_dq_kernel<false, 4, kKeysLen, true>),
+                                   reinterpret_cast<const void*>(&bwd_dq_kernel<false, 4, kKeysBits, true>)};
+      const void* const t_dkdv[3] = {reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, 4, kKeysAll, true>),
+                                     reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, 4, kKeysLen, true>),
+                                     reinterpret_cast<const void*>(&bwd_dkdv_kernel<false, 4, kKeysBits, true>)};
+      k_dq = t_dq[keys];
+      k_dkdv = t_dkdv[keys];
+    }
+    e = launch_main<4>(k_dq, a, B, H, N, s);
+    if (e == hipSuccess) e = launch_main<4>(k_dkdv, a, B, H, N, s);
+    return launch_status(e);
+  }
   if (causal) {
     const void* const k_dq[3] = {reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, kKeysAll>),
                                  reinterpret_cast<const void*>(&bwd_dq_kernel<true, kWavesCausal, kKeysLen>),
@@ -1271,6 +1386,30 @@ extern "C" attn_status attn_bwd_masked(const void* q, const void* k, const void*
   if (st != ATTN_OK) return st;
   return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
                     key_len, key_bits, nullptr, stream);
+}
+
+extern "C" attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                        const void* dout, void* dq, void* dk, void* dv, void* workspace, int B,
+                                        int H, int N, int d, float scale, int causal, const attn_layout* q_layout,
+                                        const attn_layout* k_layout, const attn_layout* v_layout,
+                                        const attn_layout* o_layout, const attn_layout* dout_layout,
+                                        const attn_layout* dq_layout, const attn_layout* dk_layout,
+                                        const attn_layout* dv_layout, const int* key_len, const unsigned* key_bits,
+                                        void* stream) {
+  if (!workspace) return ATTN_E_INVALID;
+  attn_status st = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  BwdArgs lay;
+  bool strided = false;
+  const attn_layout* const layouts[8] = {q_layout, k_layout, v_layout, o_layout,
+                                         dout_layout, dq_layout, dk_layout, dv_layout};
+  st = bwd_layouts(layouts, H, N, lay, &strided);
+  if (st != ATTN_OK) return st;
+  if (misaligned(workspace, 16) || misaligned(key_len, 4) || misaligned(key_bits, 4)) return ATTN_E_ALIGN;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  return bwd_launch(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, H, N, scale, causal,
+                    key_len, key_bits, nullptr, stream, strided ? &lay : nullptr);
 }
 
 extern "C" attn_status attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,

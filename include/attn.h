@@ -344,6 +344,43 @@ attn_status attn_bwd_masked(const void *q, const void *k, const void *v,
                             const unsigned *key_bits, void *stream);
 
 /*
+ * attn_bwd_strided: attn_bwd_masked on strided tensors, the backward of
+ * attn_fwd_strided: q, k, v, o, dout may be read where a packed projection
+ * (or the forward) left them, and dq, dk, dv written straight into the
+ * gradient of a packed projection (the layout the Qiita page's patch
+ * layer, section 4, gives its sdpa call: [B][N][3][H][d] split into heads).
+ *   *_layout : element strides of q, k, v, o, dout, dq, dk, dv, or NULL for
+ *              the contiguous [B][H][N][d] layout.  Every stride must be
+ *              >= 0 and a multiple of 8 elements (16 bytes); dq, dk and dv
+ *              need a row stride of at least d, and their rows must not
+ *              overlap across heads or batch entries (not checked beyond
+ *              the row stride); (N-1) * row * 2 + 128 must stay below 2^31
+ *              for q, dout, k and v (ATTN_E_ALIGN / ATTN_E_INVALID
+ *              otherwise).  Zero head or batch strides are allowed for the
+ *              inputs.
+ *   key_len, key_bits : as attn_bwd_masked (NULL for none).
+ * lse stays contiguous [B][H][N]; the workspace is attn_bwd's.  With every
+ * layout NULL this is exactly attn_bwd_masked; otherwise separate kernel
+ * instances that form each row's address from its strides run (4-wave
+ * workgroups), with the same arithmetic, so the gradients are bitwise those
+ * of the contiguous call on the same values.
+ */
+attn_status attn_bwd_strided(const void *q, const void *k, const void *v,
+                             const void *o, const float *lse,
+                             const void *dout, void *dq, void *dk, void *dv,
+                             void *workspace, int B, int H, int N, int d,
+                             float scale, int causal,
+                             const attn_layout *q_layout,
+                             const attn_layout *k_layout,
+                             const attn_layout *v_layout,
+                             const attn_layout *o_layout,
+                             const attn_layout *dout_layout,
+                             const attn_layout *dq_layout,
+                             const attn_layout *dk_layout,
+                             const attn_layout *dv_layout, const int *key_len,
+                             const unsigned *key_bits, void *stream);
+
+/*
  * attn_bwd_block_sparse: attn_bwd for a forward run by
  * attn_fwd_block_sparse with the same block_mask (FlashAttention reading
  * notes, section on block-sparse FlashAttention: the backward skips the

@@ -158,6 +158,34 @@ def test_backward_masked_validation():
         assert bwd(key_len=None, key_bits=None) == ea.ATTN_E_DEVICE
 
 
+def test_backward_strided_validation():
+    """attn_bwd_strided: attn_bwd_masked's checks plus the eight layouts
+    (strides non-negative multiples of 8 elements, outputs' rows at least 64
+    apart, the tile loads' byte offsets below 2^31), all before any device
+    call."""
+    lib = ea.load_library()
+    names = ("q", "k", "v", "o", "dout", "dq", "dk", "dv")
+
+    def bwd(N=100, key_len=None, **lays):
+        ptrs = [ALIGNED] * 10
+        lay = [None if lays.get(n) is None else ctypes.byref(ea.AttnLayout(*lays[n])) for n in names]
+        return lib.attn_bwd_strided(*ptrs, 1, 2, N, 64, 0.125, 0, *lay, key_len, None, None)
+    assert bwd(q=(0, 64, -64)) == ea.ATTN_E_INVALID          # negative stride
+    assert bwd(dout=(4096, 64, 196)) == ea.ATTN_E_ALIGN      # row not a 16-byte multiple
+    assert bwd(v=(4096, 12, 192)) == ea.ATTN_E_ALIGN         # head not a 16-byte multiple
+    assert bwd(dk=(4096, 8, 56)) == ea.ATTN_E_INVALID        # dK rows would overlap
+    assert bwd(dq=(4096, 8, 0)) == ea.ATTN_E_INVALID
+    assert bwd(k=(0, 0, 1 << 23), N=200) == ea.ATTN_E_INVALID     # K tile offsets >= 2^31
+    assert bwd(dout=(0, 0, 1 << 23), N=200) == ea.ATTN_E_INVALID  # dO tile offsets >= 2^31
+    assert bwd(o=(0, 0, 1 << 23), N=200) != ea.ATTN_E_INVALID     # O is read row by row
+    assert bwd(q=(0, 0, 1 << 25)) == ea.ATTN_E_INVALID       # row stride above 2^24
+    assert bwd(key_len=ALIGNED + 2) == ea.ATTN_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd() == ea.ATTN_E_DEVICE
+        assert bwd(q=(8192 * 3, 192, 3 * 128), k=(0, 0, 64), dk=(8192, 64, 128)) == ea.ATTN_E_DEVICE
+
+
 def test_backward_block_sparse_validation():
     """attn_bwd_block_sparse: attn_bwd's checks, a block mask, N <= 262,144,
     all before any device call."""

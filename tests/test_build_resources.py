@@ -39,8 +39,9 @@ def test_report_lists_every_kernel():
     assert len(fwd) == 10, fwd
     for kind in ("attn_fwd_f32_kernel", "attn_pack_key_mask_kernel"):
         assert sum(kind in n for n in names) == 1, kind
-    assert sum("bwd_dkdv_kernel" in n for n in names) == 8  # causal or not; all keys, lengths, bits, blocks
-    assert sum("bwd_dq_kernel" in n for n in names) == 8
+    # causal or not; all keys, lengths, bits, blocks contiguous; all keys, lengths, bits strided
+    assert sum("bwd_dkdv_kernel" in n for n in names) == 14
+    assert sum("bwd_dq_kernel" in n for n in names) == 14
 
 
 @pytest.mark.parametrize("name", sorted(report()) if os.path.exists(b.RESOURCES) else [])
