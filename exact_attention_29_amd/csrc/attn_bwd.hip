@@ -32,6 +32,9 @@
 // (exp2, dS, bf16 packing), and reads its MFMA operands from LDS four MFMAs
 // ahead.  -D enters dP as the initial value of its accumulator.  Causal
 // calls run each XCD's block of heads longest row block first (causal_order).
+// Instances for key masks (lengths, bits), block masks and strided tensors
+// (each tensor's rows addressed through its own batch, head and row
+// strides) share this structure.
 // No atomics: every output element is written by exactly one lane, so the
 // result is deterministic.  All products on v_mfma_f32_32x32x16_bf16 with
 // fp32 accumulation; P and dS are rounded to bf16 for the products, as in

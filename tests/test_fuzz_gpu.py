@@ -3,7 +3,7 @@ GPU against the fp64 oracle: shapes (lengths near and between tile
 boundaries), causal or not, both key-mask forms (with entries that hide every
 key), packed strided views, fp32 I/O, negative and unusual scales, random
 block-sparse masks, and the backward (plain, after a key mask, after a
-block mask).  Each
+block mask, on strided views).  Each
 feature has its own tests; these check that they combine.  The cases are
 drawn once from a fixed seed, so every run sees the same list.  Inputs are
 standard normal and scales reach 1 (eight times the workloads'), so rows
@@ -256,3 +256,48 @@ def test_random_block_sparse_backward(case):
     mags = grad_magnitudes_blocks(q, k, v, do, case["scale"], case["causal"], bm)
     for name, g, r, mg in zip(("dQ", "dK", "dV"), grads, ref, mags):
         assert_grad_within(f"{name} case {case['i']}", g, r, mg)
+
+
+def _strided_backward_cases(count=12, seed=6074):
+    rng = np.random.default_rng(seed)
+    return [dict(i=i, B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), N=_length(rng) // 2 + 1,
+                 causal=bool(rng.random() < 0.5), mask=str(rng.choice(["none", "len", "bits"])),
+                 out=str(rng.choice(["packed", "token", "contiguous"])),
+                 scale=float(0.125 if rng.random() < 0.6 else rng.uniform(-0.4, 0.6)),
+                 seed=int(rng.integers(0, 2**31))) for i in range(count)]
+
+
+@pytest.mark.parametrize("case", _strided_backward_cases(), ids=lambda c: "tb%02d_N%d%s_%s_%s" % (
+    c["i"], c["N"], "_causal" if c["causal"] else "", c["mask"], c["out"]))
+def test_random_strided_backward(case):
+    """The backward on packed projection views (attn_bwd_strided), dO
+    token-major, the gradients into a packed buffer, token-major views or
+    contiguous tensors: bitwise equal to the contiguous backward on copies
+    of the same values."""
+    B, H, N = case["B"], case["H"], case["N"]
+    print(f"[fuzz] {case}", flush=True)
+    g = torch.Generator().manual_seed(case["seed"] % (2**31))
+    x = torch.randn(B, N, 3 * H * 64, generator=g).to(torch.bfloat16).to(DEV)
+    q, k, v = (t.view(B, N, H, 64).transpose(1, 2) for t in x.chunk(3, dim=-1))
+    dout = torch.randn(B, N, H, 64, generator=g).to(torch.bfloat16).to(DEV).transpose(1, 2)
+    rng = np.random.default_rng(case["seed"])
+    masks = {}
+    if case["mask"] == "len":
+        masks["key_len"] = torch.tensor(rng.integers(0, N + 1, size=B), dtype=torch.int32, device=DEV)
+    elif case["mask"] == "bits":
+        masks["key_valid"] = torch.tensor(rng.random((B, N)) < 0.7, device=DEV)
+    o, lse = ea.forward(q, k, v, scale=case["scale"], causal=case["causal"], **masks)
+    if case["out"] == "packed":
+        gx = torch.empty(B, N, 3 * H * 64, dtype=torch.bfloat16, device=DEV)
+        outs = [t.view(B, N, H, 64).transpose(1, 2) for t in gx.chunk(3, dim=-1)]
+    elif case["out"] == "token":
+        outs = [torch.empty(B, N, H, 64, dtype=torch.bfloat16, device=DEV).transpose(1, 2) for _ in range(3)]
+    else:
+        outs = [torch.empty(B, H, N, 64, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    got = ea.backward(q, k, v, o, lse, dout, scale=case["scale"], causal=case["causal"], dq=outs[0], dk=outs[1],
+                      dv=outs[2], **masks)
+    ref = ea.backward(q.contiguous(), k.contiguous(), v.contiguous(), o.contiguous(), lse, dout.contiguous(),
+                      scale=case["scale"], causal=case["causal"], **masks)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        assert torch.equal(a, b), f"{name} case {case['i']} differs from the contiguous backward"
