@@ -474,9 +474,11 @@ bwd_dkdv_kernel(BwdArgs a) {
   };
   // where a pipelined step of this wave reads the L2 values of list position
   // t held in stage sb: inf_l2 when its column of the block mask is clear
+  // (t = n_listed, past the list, is asked for by the last tile and unused:
+  // it reads the last entry instead)
   auto l2_base = [&](const char* sb, int t) -> const char* {
     if constexpr (kKeys == kKeysBlocks) {
-      const int e = __builtin_amdgcn_readfirstlane((int)blk_list[min(t, kMaxBlockTiles - 1)]);
+      const int e = __builtin_amdgcn_readfirstlane((int)blk_list[max(0, min(t, n_listed - 1))]);
       return (e >> (14 + wave_s / 2)) & 1 ? sb + kStatOff : reinterpret_cast<const char*>(inf_l2);
     } else {
       (void)t;
