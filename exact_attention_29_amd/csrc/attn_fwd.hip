@@ -52,9 +52,10 @@
 //     over every CU; each workgroup runs its one or two pieces in a loop,
 //     hands each partial (unnormalised O^T, m, l) to a workspace slot, and
 //     the last piece of a tile to arrive merges them in piece order.
-// fp32 kernel: one thread per query row on the vector ALU (scores in fp64,
-// exp2 and sums in fp32), 8-key K/V tiles broadcast from LDS, hidden keys
-// skipped; same online softmax.  Used for fp32 I/O.
+// fp32 kernel: two lanes per query row on the vector ALU (each holds half of
+// the features; scores, row sums and O's accumulators in fp64, exp2 in fp32),
+// 8-key K/V tiles broadcast from LDS, hidden keys skipped; same online
+// softmax.  Used for fp32 I/O.
 
 #include <hip/hip_runtime.h>
 
@@ -1152,7 +1153,7 @@ struct F32Args {
   float* o;
   float* lse;
   int n;
-  int q_tiles;  // ceil(n / 64)
+  int q_tiles;  // ceil(n / kF32Rows)
   float scale;
   int causal;
   int heads;
@@ -1161,44 +1162,82 @@ struct F32Args {
 };
 
 constexpr int kF32Keys = 8;   // keys per LDS tile in the fp32 kernel
+constexpr int kF32Rows = 64;  // query rows per workgroup (two waves)
+constexpr int kF32Half = kD / 2;
 
-__global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
-  __shared__ float ks[kF32Keys][kD];
-  __shared__ float vs[kF32Keys][kD];
+// x[lane] + x[lane ^ 32] in both lanes of the pair, summed in the same order
+// (the lower half's value first), so the two lanes get the same bits.
+__device__ __forceinline__ double pair_sum_f64(double x) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = (unsigned)u, hi = (unsigned)(u >> 32);
+  const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  // after the swap each element holds one lane's word, the same lane's in both lanes of the pair
+  const double a = __builtin_bit_cast(double, ((unsigned long long)(unsigned)rh[0] << 32) | (unsigned)rl[0]);
+  const double b = __builtin_bit_cast(double, ((unsigned long long)(unsigned)rh[1] << 32) | (unsigned)rl[1]);
+  return a + b;
+}
+
+// Two lanes per query row: lane l of a wave owns row l % 32 of the wave's 32
+// and features [32 * (l / 32), +32) of its Q row and of its O accumulators,
+// so the partial dot products meet in one exchange with lane l ^ 32.
+__global__ void __launch_bounds__(2 * 64) attn_fwd_f32_kernel(F32Args a) {
+  __shared__ float4 ks[kF32Keys][kD / 4];
+  __shared__ float4 vs[kF32Keys][kD / 4];
   const int n = a.n;
   const int bh = blockIdx.x / a.q_tiles;
   const int qt = blockIdx.x - bh * a.q_tiles;
   const size_t head = (size_t)bh * n * kD;
-  const int qi = qt * 64 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;  // which 32 features this lane holds
+  const int qi = qt * kF32Rows + (threadIdx.x >> 6) * 32 + (lane & 31);
   const bool live = qi < n;
 
-  float qv[kD], acc[kD];
-#pragma unroll
-  for (int f = 0; f < kD; ++f) {
-    qv[f] = live ? a.q[head + (size_t)qi * kD + f] : 0.f;
-    acc[f] = 0.f;
-  }
   // Scores, the running max and t - m are kept in fp64: a 64-term fp32 dot
   // product and the rounding of s * c would each cost about 2^-24 * |s| in
   // the exponent, i.e. ~1e-5 in O and LSE once |s| reaches ~30 (a large
   // scale); in fp64 the products of fp32 values are exact and only the
-  // small difference t - m is rounded to fp32 for exp2.
+  // small difference t - m is rounded to fp32 for exp2.  O's accumulators
+  // and the row sum l are fp64 too: with up to N terms of mixed sign in
+  // fp32, their rounding reaches ~4e-6 of |O| on sharp rows (l alone
+  // ~3e-6), i.e. 1e-5 once |O| is a few units.
+  float qv[kF32Half];
+  double acc[kF32Half];
+  // loads past N read row N - 1 and are replaced by zeros (a select, so no
+  // load is predicated)
+  const float* const qrow = a.q + head + (size_t)min(qi, n - 1) * kD + half * kF32Half;
+#pragma unroll
+  for (int f = 0; f < kF32Half; f += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(qrow + f);
+    qv[f] = live ? x.x : 0.f;
+    qv[f + 1] = live ? x.y : 0.f;
+    qv[f + 2] = live ? x.z : 0.f;
+    qv[f + 3] = live ? x.w : 0.f;
+  }
+#pragma unroll
+  for (int f = 0; f < kF32Half; ++f) acc[f] = 0.0;
   const double c = (double)a.scale * 1.4426950408889634;  // log2(e)
   double m_run = -INFINITY;
-  float l_run = 0.f;
+  double l_run = 0.0;
   const int b_entry = bh / a.heads;
   const int n_k = a.key_len ? min(max(a.key_len[b_entry], 0), n) : n;
   const uint32_t* const mask_row = a.key_bits ? a.key_bits + (size_t)b_entry * ((n + 31) / 32) : nullptr;
-  const int kv_end = a.causal ? min(n_k, qt * 64 + 64) : n_k;
+  const int kv_end = a.causal ? min(n_k, qt * kF32Rows + kF32Rows) : n_k;
   const int row_last = a.causal ? min(qi, n_k - 1) : n_k - 1;
+  // the tile load: thread t moves 16 bytes of K and of V, row t / 16, chunk t % 16
+  static_assert(kF32Keys * kD / 4 == 2 * 64, "one 16-byte chunk of K and of V per thread");
+  const int ld_r = threadIdx.x >> 4, ld_c = threadIdx.x & 15;
 
   for (int k0 = 0; k0 < kv_end; k0 += kF32Keys) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < kF32Keys * kD; idx += 64) {
-      const int r = idx / kD, f = idx % kD;
-      const int key = k0 + r;
-      ks[r][f] = key < n ? a.k[head + (size_t)key * kD + f] : 0.f;
-      vs[r][f] = key < n ? a.v[head + (size_t)key * kD + f] : 0.f;
+    {
+      const int key = k0 + ld_r;
+      const size_t off = head + (size_t)min(key, n - 1) * kD + ld_c * 4;
+      const float4 kx = *reinterpret_cast<const float4*>(a.k + off);
+      const float4 vx = *reinterpret_cast<const float4*>(a.v + off);
+      const bool in = key < n;
+      ks[ld_r][ld_c] = make_float4(in ? kx.x : 0.f, in ? kx.y : 0.f, in ? kx.z : 0.f, in ? kx.w : 0.f);
+      vs[ld_r][ld_c] = make_float4(in ? vx.x : 0.f, in ? vx.y : 0.f, in ? vx.z : 0.f, in ? vx.w : 0.f);
     }
     __syncthreads();
     double t[kF32Keys];
@@ -1209,9 +1248,16 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     const uint32_t word = mask_row ? mask_row[k0 >> 5] >> (k0 & 31) : 0xffffffffu;
 #pragma unroll
     for (int r = 0; r < kF32Keys; ++r) {
-      double s = 0.0;
+      double part = 0.0;
 #pragma unroll
-      for (int f = 0; f < kD; ++f) s = __builtin_fma((double)qv[f], (double)ks[r][f], s);
+      for (int f4 = 0; f4 < kF32Half / 4; ++f4) {
+        const float4 kk = ks[r][half * (kF32Half / 4) + f4];
+        part = __builtin_fma((double)qv[4 * f4], (double)kk.x, part);
+        part = __builtin_fma((double)qv[4 * f4 + 1], (double)kk.y, part);
+        part = __builtin_fma((double)qv[4 * f4 + 2], (double)kk.z, part);
+        part = __builtin_fma((double)qv[4 * f4 + 3], (double)kk.w, part);
+      }
+      const double s = pair_sum_f64(part);
       const bool vis = k0 + r <= row_last && ((word >> r) & 1u);
       seen |= (vis ? 1u : 0u) << r;
       t[r] = vis ? s * c : -INFINITY;
@@ -1221,29 +1267,39 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Args a) {
     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((float)(m_run - m_new));
     const double msub = (m_new == -INFINITY) ? 0.0 : m_new;
     m_run = m_new;
-    l_run *= alpha;
+    l_run *= (double)alpha;
 #pragma unroll
-    for (int f = 0; f < kD; ++f) acc[f] *= alpha;
+    for (int f = 0; f < kF32Half; ++f) acc[f] *= (double)alpha;
     // a hidden key takes no part: its V row is skipped, not multiplied by
     // p = 0 (so a non-finite value there cannot reach this row)
 #pragma unroll
     for (int r = 0; r < kF32Keys; ++r) {
       if (!((seen >> r) & 1u)) continue;
-      const float p = __builtin_amdgcn_exp2f((float)(t[r] - msub));
+      const double p = __builtin_amdgcn_exp2f((float)(t[r] - msub));
       l_run += p;
 #pragma unroll
-      for (int f = 0; f < kD; ++f) acc[f] = __builtin_fmaf(p, vs[r][f], acc[f]);
+      for (int f4 = 0; f4 < kF32Half / 4; ++f4) {
+        const float4 vv = vs[r][half * (kF32Half / 4) + f4];
+        acc[4 * f4] = __builtin_fma(p, (double)vv.x, acc[4 * f4]);
+        acc[4 * f4 + 1] = __builtin_fma(p, (double)vv.y, acc[4 * f4 + 1]);
+        acc[4 * f4 + 2] = __builtin_fma(p, (double)vv.z, acc[4 * f4 + 2]);
+        acc[4 * f4 + 3] = __builtin_fma(p, (double)vv.w, acc[4 * f4 + 3]);
+      }
     }
   }
   if (live) {
     // a row that saw no key: O = 0, LSE = -inf (the empty sum); l is +0,
     // positive or NaN, and a NaN stays NaN (the test is on the bits)
-    const bool empty_row = __builtin_bit_cast(unsigned, l_run) == 0u;
-    const float inv = empty_row ? 0.f : 1.f / l_run;
+    const bool empty_row = __builtin_bit_cast(unsigned long long, l_run) == 0ull;
+    const double inv = empty_row ? 0.0 : 1.0 / l_run;
+    float* const orow = a.o + head + (size_t)qi * kD + half * kF32Half;
 #pragma unroll
-    for (int f = 0; f < kD; ++f) a.o[head + (size_t)qi * kD + f] = acc[f] * inv;
-    a.lse[(size_t)bh * n + qi] = empty_row ? -INFINITY
-                                           : (float)((m_run + (double)__log2f(l_run)) * 0.6931471805599453);
+    for (int f = 0; f < kF32Half; f += 4)
+      *reinterpret_cast<float4*>(orow + f) = make_float4((float)(acc[f] * inv), (float)(acc[f + 1] * inv),
+                                                         (float)(acc[f + 2] * inv), (float)(acc[f + 3] * inv));
+    if (half == 0)
+      a.lse[(size_t)bh * n + qi] = empty_row ? -INFINITY
+                                             : (float)((m_run + (double)__log2f((float)l_run)) * 0.6931471805599453);
   }
 }
 
@@ -1452,7 +1508,7 @@ attn_status launch_fp32(const float* q, const float* k, const float* v, float* o
   a.o = o;
   a.lse = lse;
   a.n = N;
-  a.q_tiles = (N + 63) / 64;
+  a.q_tiles = (N + kF32Rows - 1) / kF32Rows;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
   a.heads = H;
@@ -1460,7 +1516,7 @@ attn_status launch_fp32(const float* q, const float* k, const float* v, float* o
   a.key_bits = key_bits;
   void* args[] = {&a};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_f32_kernel),
-                                       dim3(B * H * a.q_tiles), dim3(64), args, 0,
+                                       dim3(B * H * a.q_tiles), dim3(2 * 64), args, 0,
                                        static_cast<hipStream_t>(stream));
   return launch_status(e);
 }

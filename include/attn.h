@@ -106,8 +106,9 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o,
  * attn_fwd_fp32: the same operation with fp32 input and output and no bf16
  * or reduced-precision products: scores, the running row max and their
  * difference are formed in fp64 (products of fp32 values are exact there),
- * exp2 and the sums of P and P V in fp32.  Same layout, ownership, stream
- * and error rules as attn_fwd; q, k, v, o are float.
+ * exp2 in fp32, the row sum of P and the sums P V in fp64, O rounded to fp32
+ * once at the end.  Same layout, ownership, stream and error rules as
+ * attn_fwd; q, k, v, o are float.
  */
 attn_status attn_fwd_fp32(const float *q, const float *k, const float *v,
                           float *o, float *lse, int B, int H, int N, int d,
