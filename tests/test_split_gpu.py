@@ -11,6 +11,8 @@ shapes that exercise each case of the decomposition:
   * tiles not a multiple of 8 (XCDs with different leftovers);
   * no whole round, long rows: every tile cut into several pieces;
   * a ragged last key tile (N not a multiple of 64) inside a piece;
+  * eight seeded random shapes the library splits, with random masks and
+    scales;
 plus key-padding masks (pieces that see no key at all), strided head views,
 NaN and infinite inputs, determinism, the arrival counters left at zero,
 and replays of captured graphs.  The decomposition is deterministic (pieces
@@ -23,7 +25,7 @@ import torch
 
 import exact_attention_29_amd as ea
 from oracle import attention as oracle_attention
-from tests.parity import BF16, assert_within, errors
+from tests.parity import BF16, assert_bf16_elementwise, assert_within, errors
 from workloads import Workload, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -49,9 +51,9 @@ def count_bytes():
     return (8 * (cus() // 8) * 4 + 255) // 256 * 256
 
 
-def splits(B, H, N):
-    """The library's rule for splitting a non-causal call (restated)."""
-    c = cus() // 8 if cus() >= 16 else 1
+def splits_at(B, H, N, n_cus):
+    """The library's rule for splitting a non-causal call on n_cus CUs (restated)."""
+    c = n_cus // 8 if n_cus >= 16 else 1
     tiles = B * H * -(-N // 256)
     n_kt = -(-N // 64)
     per, r8 = divmod(tiles, 8)
@@ -60,6 +62,10 @@ def splits(B, H, N):
     left = tiles - 8 * rounds * c
     return (0 < rem_max < c and n_kt >= c and 2 * left <= 8 * c and (rounds >= 1 or n_kt >= 160)
             and c * c * n_kt < 2 ** 31)
+
+
+def splits(B, H, N):
+    return splits_at(B, H, N, cus())
 
 
 def inputs(B, H, N, seed, sigma=1.0):
@@ -169,6 +175,58 @@ def test_split_with_random_key_mask_and_length():
     kl = torch.tensor([N, 2100], dtype=torch.int32, device=DEV)
     o, lse, _ = run_split(*(t.to(DEV) for t in (q, k, v)), key_len=kl, key_bits=bits)
     check(q, k, v, o, lse, "split with key mask", key_valid=valid)
+
+
+def _random_split_cases(count=8, seed=5150):
+    """Shapes drawn until the library splits them on 256 CUs (at most 200,000 rows, so
+    the oracle stays fast), each with no mask, valid lengths or a random
+    mask, at the workloads' scale or a sharper one."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        N, B, H = int(rng.integers(2048, 4200)), int(rng.integers(1, 3)), int(rng.integers(1, 80))
+        mask = str(rng.choice(["none", "len", "valid"]))
+        scale = float(0.125 if rng.random() < 0.6 else rng.uniform(-0.5, 1.0))
+        seed_i = int(rng.integers(0, 2**31))
+        if B * H * N <= 200_000 and splits_at(B, H, N, 256):  # drawn for a 256-CU MI355X
+            cases.append(dict(B=B, H=H, N=N, mask=mask, scale=scale, seed=seed_i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_split_cases(), ids=lambda c: "B%dH%dN%d_%s" % (c["B"], c["H"], c["N"], c["mask"]))
+def test_random_split_calls(case):
+    """forward() on random shapes, masks and scales; the cases the library
+    splits are compared with the oracle on every row (the others run the
+    plain kernel, covered elsewhere)."""
+    B, H, N, scale = case["B"], case["H"], case["N"], case["scale"]
+    if not splits(B, H, N):
+        pytest.skip("not split on this part")
+    print(f"[case] {case}", flush=True)
+    q, k, v = make_inputs(Workload("split_fuzz", B, H, N, 64, "bf16", 1.0, scale, False, case["seed"], ""))
+    rng = np.random.default_rng(case["seed"])
+    kwargs, valid = {}, None
+    if case["mask"] == "len":
+        lens = rng.integers(0, N + 1, size=B)
+        valid = np.arange(N)[None, :] < lens[:, None]
+        kwargs = dict(key_len=torch.tensor(lens, dtype=torch.int32, device=DEV))
+    elif case["mask"] == "valid":
+        valid = rng.random((B, N)) < rng.uniform(0.3, 1.0)
+        kwargs = dict(key_valid=torch.from_numpy(valid).to(DEV))
+    o, lse = ea.forward(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, **kwargs)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_attention(to_f64(q), to_f64(k), to_f64(v), scale, key_valid=valid)
+    o_h, lse_h = to_f64(o), to_f64(lse)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_h), empty), "rows that see no key differ"
+    assert np.all(o_h[empty] == 0.0)
+    keep = ~empty
+    if not keep.any():
+        return
+    if scale == 0.125:
+        assert_within(errors(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep]), BF16, str(case))
+    else:
+        o_abs, _ = oracle_attention(to_f64(q), to_f64(k), np.abs(to_f64(v)), scale, key_valid=valid)
+        assert_bf16_elementwise(o_h[keep], lse_h[keep], o_ref[keep], lse_ref[keep], o_abs[keep], str(case))
 
 
 def test_split_strided_views_match_contiguous_bitwise():
