@@ -16,7 +16,7 @@ import torch
 import exact_attention_29_amd as ea
 from oracle import attention as oracle_attention
 from tests.parity import BF16, assert_within, errors
-from workloads import WORKLOADS, Workload, make_inputs, sample_rows, to_f64
+from workloads import WORKLOADS, Workload, block_rows, make_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -94,11 +94,13 @@ def test_first_listed_tile_hidden_by_causality():
 
 
 def test_patch_3mp_sparse_sampled():
-    """The 3 MP patch shape with a quarter of the blocks set, sampled rows."""
+    """The 3 MP patch shape with a quarter of the blocks set: twelve random
+    128-row query blocks (every row offset of a block-sparse workgroup) and
+    the ragged last one, every row of them in every head."""
     w = WORKLOADS["patch_3mp"]
     B, H, N, d = w.shape
     rng = np.random.default_rng(930)
     m = rng.random(blocks(N)) < 0.25
     q, k, v = make_inputs(w)
     o, lse = run(q, k, v, m, w.scale, False)
-    check(q, k, v, o, lse, m, w.scale, False, "3 MP block-sparse", rows=sample_rows(N, 64, seed=31))
+    check(q, k, v, o, lse, m, w.scale, False, "3 MP block-sparse", rows=block_rows(N, 12, seed=31, rows_per_block=BQ))
