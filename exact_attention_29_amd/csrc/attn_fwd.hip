@@ -1224,22 +1224,27 @@ __global__ void __launch_bounds__(2 * 64) attn_fwd_f32_kernel(F32Args a) {
   const uint32_t* const mask_row = a.key_bits ? a.key_bits + (size_t)b_entry * ((n + 31) / 32) : nullptr;
   const int kv_end = a.causal ? min(n_k, qt * kF32Rows + kF32Rows) : n_k;
   const int row_last = a.causal ? min(qi, n_k - 1) : n_k - 1;
-  // the tile load: thread t moves 16 bytes of K and of V, row t / 16, chunk t % 16
+  // the tile load: thread t moves 16 bytes of K and of V, row t / 16, chunk
+  // t % 16; the next tile's chunks travel while this tile is computed
   static_assert(kF32Keys * kD / 4 == 2 * 64, "one 16-byte chunk of K and of V per thread");
   const int ld_r = threadIdx.x >> 4, ld_c = threadIdx.x & 15;
+  float4 kx, vx;
+  auto load_chunks = [&](int k0) __attribute__((always_inline)) {
+    const size_t off = head + (size_t)min(k0 + ld_r, n - 1) * kD + ld_c * 4;
+    kx = *reinterpret_cast<const float4*>(a.k + off);
+    vx = *reinterpret_cast<const float4*>(a.v + off);
+  };
+  if (kv_end > 0) load_chunks(0);
 
   for (int k0 = 0; k0 < kv_end; k0 += kF32Keys) {
     __syncthreads();
     {
-      const int key = k0 + ld_r;
-      const size_t off = head + (size_t)min(key, n - 1) * kD + ld_c * 4;
-      const float4 kx = *reinterpret_cast<const float4*>(a.k + off);
-      const float4 vx = *reinterpret_cast<const float4*>(a.v + off);
-      const bool in = key < n;
+      const bool in = k0 + ld_r < n;
       ks[ld_r][ld_c] = make_float4(in ? kx.x : 0.f, in ? kx.y : 0.f, in ? kx.z : 0.f, in ? kx.w : 0.f);
       vs[ld_r][ld_c] = make_float4(in ? vx.x : 0.f, in ? vx.y : 0.f, in ? vx.z : 0.f, in ? vx.w : 0.f);
     }
     __syncthreads();
+    if (k0 + kF32Keys < kv_end) load_chunks(k0 + kF32Keys);
     double t[kF32Keys];
     double mx = -INFINITY;
     uint32_t seen = 0;  // bit r: key k0 + r takes part in this row
