@@ -3,7 +3,8 @@ GPU against the fp64 oracle: shapes (lengths near and between tile
 boundaries), causal or not, both key-mask forms (with entries that hide every
 key), packed strided views, fp32 I/O, negative and unusual scales, random
 block-sparse masks, and the backward (plain, after a key mask, after a
-block mask, on strided views).  Each
+block mask, on strided views); a few cases at longer rows (N up to 9,000
+forward, 4,500 backward).  Each
 feature has its own tests; these check that they combine.  The cases are
 drawn once from a fixed seed, so every run sees the same list.  Inputs are
 standard normal and scales reach 1 (eight times the workloads'), so rows
@@ -119,6 +120,28 @@ def test_fp32_sharp_rows(case):
     test_random_forward(case)
 
 
+def _long_forward_cases(count=6, seed=8080):
+    """Longer rows (N 2,000-9,000, one or two heads per entry): many turns
+    of the LDS ring between the masked edges, with the same features."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        dtype = "fp32" if rng.random() < 0.3 else "bf16"
+        cases.append(dict(i=950 + i, B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)),
+                          N=int(rng.integers(2000, 9000)), causal=bool(rng.random() < 0.5),
+                          mask=str(rng.choice(["none", "len", "valid"])),
+                          packed=bool(dtype == "bf16" and rng.random() < 0.3), dtype=dtype,
+                          scale=float(0.125 if rng.random() < 0.5 else rng.uniform(-0.5, 1.0)),
+                          seed=int(rng.integers(0, 2**31))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _long_forward_cases(), ids=lambda c: "c%d_%s_N%d%s_%s" % (
+    c["i"], c["dtype"], c["N"], "_causal" if c["causal"] else "", c["mask"]))
+def test_random_forward_long_rows(case):
+    test_random_forward(case)
+
+
 def _backward_cases(count=12, seed=4048):
     rng = np.random.default_rng(seed)
     return [dict(i=i, B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), N=_length(rng) // 2 + 1,
@@ -195,6 +218,28 @@ def test_random_masked_backward(case):
         assert_grad_within(f"{name} case {case['i']}", g, r, m)
     hidden = torch.tensor(~valid, device=DEV)[:, None, :, None]
     assert not (grads[1].float() * hidden).any() and not (grads[2].float() * hidden).any(), "hidden keys"
+
+
+def _long_backward_cases(count=4, seed=8081):
+    """The backward at N 1,000-4,500: plain, and after key lengths or bits."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        B, H, N = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1000, 4500))
+        c = dict(i=960 + i, B=B, H=H, N=N, causal=bool(rng.random() < 0.5),
+                 scale=float(0.125 if rng.random() < 0.6 else rng.uniform(-0.4, 0.6)),
+                 lens=[int(x) for x in rng.integers(0, N + 1, size=B)], seed=int(rng.integers(0, 2**31)))
+        if i % 2:
+            c["bits"] = float(rng.uniform(0.2, 0.95))
+        cases.append(c)
+    return cases
+
+
+@pytest.mark.parametrize("case", _long_backward_cases(), ids=lambda c: "lb%d_N%d%s" % (
+    c["i"], c["N"], "_causal" if c["causal"] else ""))
+def test_random_backward_long_rows(case):
+    test_random_backward(case)
+    test_random_masked_backward(case)
 
 
 def _sparse_cases(count=12, seed=6072):
